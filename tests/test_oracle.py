@@ -1,0 +1,379 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test names what pins it: a library routine on a special case
+(torch scaled_dot_product_attention in float64), a closed form, brute force on
+tiny inputs, or an invariant stated by the pages (order independence of
+softmax over keys, exact log-sum-exp merging of split partials, reuse of one
+selection by every sparse layer). Together they are chosen so that a dropped
+scale, a wrong causal offset, an off-by-one window or candidate boundary, a
+reversed tie rule, a min-for-max score or a wrong GQA head map each fail at
+least one test.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+
+
+def bf16_exact(shape, rng, scale=1.0):
+    """float32 array of bf16-representable N(0, scale^2) values."""
+    x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * scale)
+    return x.to(torch.bfloat16).float().numpy()
+
+
+def sdpa_rows(q, K, V, positions, n_kv, band=None):
+    """torch SDPA (float64, enable_gqa) for query rows at `positions`.
+
+    band=None: causal mask j <= p. band=W: banded mask p-W < j <= p.
+    q: [rows][Hq][d]; K, V: [Hkv][n][d].
+    """
+    rows = q.shape[0]
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2))).double()[None]  # [1][Hq][rows][d]
+    kt = torch.from_numpy(np.ascontiguousarray(K[:, :n_kv])).double()[None]
+    vt = torch.from_numpy(np.ascontiguousarray(V[:, :n_kv])).double()[None]
+    j = torch.arange(n_kv)[None, :]
+    p = torch.as_tensor(np.asarray(positions))[:, None]
+    mask = j <= p
+    if band is not None:
+        mask &= j > p - band
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, enable_gqa=True)
+    return out[0].transpose(0, 1).numpy()
+
+
+# ---------------------------------------------------------------- full attention
+
+@pytest.mark.parametrize("Hq,Hkv,n_q,n_kv,d", [(4, 1, 40, 40, 128), (8, 2, 17, 53, 128), (6, 3, 9, 9, 16)])
+def test_full_attention_matches_sdpa(Hq, Hkv, n_q, n_kv, d):
+    """Library routine pin: causal GQA attention, including a chunk whose rows
+    sit at the end of a longer cache, against torch SDPA in float64."""
+    rng = np.random.default_rng(1 + n_q + Hq)
+    q = bf16_exact((n_q, Hq, d), rng)
+    K = bf16_exact((Hkv, n_kv, d), rng)
+    V = bf16_exact((Hkv, n_kv, d), rng)
+    pos = orc.query_positions(n_q, n_kv)
+    o, _ = orc.full_attention_rows(q, K, V, pos, orc.default_scale(d))
+    ref = sdpa_rows(q, K, V, pos, n_kv)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_query_positions_chunk_offset():
+    """A chunk of n_q new tokens occupies the last n_q cache slots."""
+    assert list(orc.query_positions(3, 10)) == [7, 8, 9]
+    assert list(orc.query_positions(4, 4)) == [0, 1, 2, 3]
+    with pytest.raises(ValueError):
+        orc.query_positions(5, 4)
+
+
+def test_softmax_rows_sum_to_one():
+    """Invariant: with V = one-hot rows the output is the attention weight
+    vector itself; it must be >= 0, zero beyond the causal limit, sum to 1."""
+    rng = np.random.default_rng(7)
+    d, n = 128, 100
+    q = bf16_exact((n, 4, d), rng, 2.0)
+    K = bf16_exact((1, n, d), rng)
+    V = np.eye(n, d, dtype=np.float32)[None]          # v_j = e_j
+    pos = orc.query_positions(n, n)
+    o, _ = orc.full_attention_rows(q, K, V, pos, orc.default_scale(d))
+    sums = o.sum(axis=2)
+    assert np.all(o >= 0)
+    np.testing.assert_allclose(sums, 1.0, atol=1e-5)
+    for t in range(n):
+        assert np.all(o[t, :, t + 1:] == 0)
+
+
+def test_lse_closed_form():
+    """Closed form: with q = a*e_0 and k_0 = c*e_0, k_j = 0 otherwise, the
+    logits are (scale*a*c, 0, ..., 0), so lse = log(exp(scale*a*c) + p) and
+    o = (exp(x) v_0 + sum_{j>=1} v_j) / (exp(x) + p)."""
+    d, n = 128, 11
+    a, c = 3.0, 2.0
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = a
+    K = np.zeros((1, n, d), np.float32)
+    K[0, 0, 0] = c
+    rng = np.random.default_rng(3)
+    V = bf16_exact((1, n, d), rng)
+    p = n - 1
+    o, lse = orc.full_attention_rows(q, K, V, [p], orc.default_scale(d))
+    x = a * c / math.sqrt(d)
+    assert abs(lse[0, 0] - math.log(math.exp(x) + p)) < 1e-12
+    V64 = V.astype(np.float64)
+    want = (math.exp(x) * V64[0, 0] + V64[0, 1:].sum(0)) / (math.exp(x) + p)
+    np.testing.assert_allclose(o[0, 0], want, atol=1e-12)
+
+
+def test_zero_query_is_mean_of_values():
+    """Closed form: q = 0 gives uniform weights, so o = mean of v over the set,
+    for full attention and for a sparse set."""
+    rng = np.random.default_rng(5)
+    d, n = 128, 30
+    q = np.zeros((1, 2, d), np.float32)
+    K = bf16_exact((1, n, d), rng)
+    V = bf16_exact((1, n, d), rng)
+    o, lse = orc.full_attention_rows(q, K, V, [n - 1], 0.1)
+    np.testing.assert_allclose(o[0, 0], V[0].astype(np.float64).mean(0), atol=1e-12)
+    assert abs(lse[0, 0] - math.log(n)) < 1e-12
+    idx = np.array([[[2, 5, -1, -1]]])
+    o2, _ = orc.sparse_attention_rows(q, K, V, idx, [n - 1], 3, 0.1)
+    want = V[0, [2, 5, 27, 28, 29]].astype(np.float64).mean(0)
+    np.testing.assert_allclose(o2[0, 1], want, atol=1e-12)
+
+
+# ------------------------------------------------------------------ selection
+
+def _beats(sa, a, sb, b):
+    return sa > sb or (sa == sb and a < b)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_defining_property_and_brute_force(seed):
+    """Brute force: on tiny inputs, enumerate every k-subset; exactly one has
+    every member beating every non-member under (score desc, index asc), and
+    topk_select must return it. Scores are drawn from a small grid so that
+    exact ties occur."""
+    rng = np.random.default_rng(seed)
+    n = 9
+    sig = rng.integers(-3, 4, size=n).astype(np.float64) / 4
+    for k in range(0, n + 2):
+        idx, _ = orc.topk_select(sig, k)
+        got = set(int(i) for i in idx if i >= 0)
+        if k >= n:
+            assert got == set(range(n))
+            continue
+        winners = []
+        for sub in itertools.combinations(range(n), k):
+            s = set(sub)
+            if all(_beats(sig[i], i, sig[o], o) for i in s for o in range(n) if o not in s):
+                winners.append(s)
+        assert len(winners) == 1
+        assert got == winners[0]
+        assert list(idx) == sorted(idx)
+
+
+def test_topk_negative_zero_ties_by_index():
+    """-0.0 and +0.0 are the same score, so the lower index wins the tie."""
+    sig = np.array([-1.0, -0.0, 0.0, -0.0, 0.0, -2.0])
+    idx, _ = orc.topk_select(sig, 2)
+    assert list(idx) == [1, 2]
+    idx, _ = orc.topk_select(sig, 3)
+    assert list(idx) == [1, 2, 3]
+
+
+def test_topk_padding_and_count():
+    """Fewer candidates than k: every candidate is taken, the rest is -1."""
+    idx, tau = orc.topk_select(np.array([0.5, 0.1, 0.9]), 5)
+    assert list(idx) == [0, 1, 2, -1, -1] and tau == -math.inf
+    idx, _ = orc.topk_select(np.zeros(0), 4)
+    assert list(idx) == [-1] * 4
+
+
+def test_selection_is_group_max_not_mean():
+    """Constructed case where the max over the group's heads and the mean
+    disagree: head A scores (x=5, y=4), head B (x=-5, y=3). The group max
+    ranks x first (5 > 4); a mean would rank y first (3.5 > 0)."""
+    d = 128
+    scale = 1.0
+    K = np.zeros((1, 10, d), np.float32)
+    K[0, 0, 0] = 1.0     # key x at position 0
+    K[0, 1, 1] = 1.0     # key y at position 1
+    q = np.zeros((2, d), np.float32)
+    q[0, 0], q[0, 1] = 5.0, 4.0
+    q[1, 0], q[1, 1] = -5.0, 3.0
+    sig = orc.selection_scores(q, K[0], p=9, window=2, scale=scale)
+    assert sig.shape == (8,)
+    assert sig[0] == 5.0 and sig[1] == 4.0
+    idx, _ = orc.topk_select(sig, 1)
+    assert list(idx) == [0]
+
+
+def test_candidates_exclude_window():
+    """Reading R3: candidates are j <= p-W, i.e. exactly p-W+1 of them."""
+    rng = np.random.default_rng(11)
+    d = 128
+    K = bf16_exact((1, 50, d), rng)
+    q = bf16_exact((4, d), rng)
+    for p, W in [(49, 8), (7, 8), (8, 8), (20, 1)]:
+        s = orc.selection_scores(q, K[0], p, W, 0.1)
+        assert s.shape[0] == max(0, p - W + 1) == orc.candidate_count(p, W)
+
+
+def test_head_permutation_invariance():
+    """Permuting heads inside a group leaves sigma (a max) unchanged."""
+    rng = np.random.default_rng(12)
+    d = 128
+    K = bf16_exact((1, 40, d), rng)
+    q = bf16_exact((8, d), rng)
+    s1 = orc.selection_scores(q, K[0], 39, 4, 0.1)
+    s2 = orc.selection_scores(q[rng.permutation(8)], K[0], 39, 4, 0.1)
+    assert np.array_equal(s1, s2)
+
+
+def test_nested_selection():
+    """Superset property of growing budgets: I_k is contained in I_{k+1}."""
+    rng = np.random.default_rng(13)
+    d = 128
+    K = bf16_exact((1, 64, d), rng)
+    q = bf16_exact((4, d), rng)
+    s = orc.selection_scores(q, K[0], 63, 4, orc.default_scale(d))
+    prev = set()
+    for k in range(0, 62):
+        cur = set(int(i) for i in orc.topk_select(s, k)[0] if i >= 0)
+        assert prev <= cur and len(cur) == min(k, s.shape[0])
+        prev = cur
+
+
+def test_duplicate_keys_pick_lower_index():
+    """Exact ties from identical key rows resolve to the lower index."""
+    rng = np.random.default_rng(14)
+    d = 128
+    K = bf16_exact((1, 40, d), rng)
+    q = bf16_exact((4, d), rng)
+    hot = (q.sum(0) / np.linalg.norm(q.sum(0)) * 16).astype(np.float32)
+    hot = torch.from_numpy(hot).to(torch.bfloat16).float().numpy()
+    K[0, 9] = hot
+    K[0, 3] = hot
+    K[0, 20] = hot
+    s = orc.selection_scores(q, K[0], 39, 4, orc.default_scale(d))
+    assert s[3] == s[9] == s[20] == s.max()
+    assert list(orc.topk_select(s, 1)[0]) == [3]
+    assert list(orc.topk_select(s, 2)[0]) == [3, 9]
+
+
+# --------------------------------------------------------------- sparse layers
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (8, 2)])
+def test_sparse_equals_full_when_budget_covers_context(Hq, Hkv):
+    """Pin: with k + W >= p + 1 every earlier token is kept, so the sparse
+    layer equals causal full attention (itself pinned to SDPA). The budget is
+    chosen so that k + W = n exactly, which makes an off-by-one in the
+    candidate or window boundary drop a token on the last row."""
+    rng = np.random.default_rng(21)
+    d, n, W = 128, 48, 5
+    k = n - W
+    q0 = bf16_exact((n, Hq, d), rng)
+    q1 = bf16_exact((n, Hq, d), rng)
+    K = bf16_exact((Hkv, n, d), rng)
+    V = bf16_exact((Hkv, n, d), rng)
+    pos = orc.query_positions(n, n)
+    sel = orc.full_attn_select_rows(q0, K, V, pos, k, W, orc.default_scale(d))
+    o, _ = orc.sparse_attention_rows(q1, K, V, sel["idx"], pos, W, orc.default_scale(d))
+    ref = sdpa_rows(q1, K, V, pos, n)
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [1, 4, 16])
+def test_k0_equals_sliding_window(W):
+    """Pin: with k = 0 the sparse layer is sliding-window attention, i.e.
+    SDPA with the band mask p-W < j <= p."""
+    rng = np.random.default_rng(22 + W)
+    d, n, Hq, Hkv = 128, 40, 4, 2
+    q = bf16_exact((n, Hq, d), rng)
+    K = bf16_exact((Hkv, n, d), rng)
+    V = bf16_exact((Hkv, n, d), rng)
+    pos = orc.query_positions(n, n)
+    idx = np.full((n, Hkv, 0), -1)
+    o, _ = orc.sparse_attention_rows(q, K, V, idx, pos, W, orc.default_scale(d))
+    ref = sdpa_rows(q, K, V, pos, n, band=W)
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+def test_sparse_is_key_order_independent():
+    """Order independence of softmax over keys: permuting an index row (and
+    its padding) leaves the sparse output unchanged."""
+    rng = np.random.default_rng(23)
+    d, n = 128, 60
+    q0 = bf16_exact((n, 4, d), rng)
+    q1 = bf16_exact((n, 4, d), rng)
+    K = bf16_exact((1, n, d), rng)
+    V = bf16_exact((1, n, d), rng)
+    pos = orc.query_positions(n, n)
+    sel = orc.full_attn_select_rows(q0, K, V, pos, 7, 6, orc.default_scale(d))
+    idx = sel["idx"].copy()
+    for t in range(n):
+        idx[t, 0] = idx[t, 0][rng.permutation(7)]
+    o1, _ = orc.sparse_attention_rows(q1, K, V, sel["idx"], pos, 6, orc.default_scale(d))
+    o2, _ = orc.sparse_attention_rows(q1, K, V, idx, pos, 6, orc.default_scale(d))
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+
+
+def test_selected_count_rule():
+    """Count of valid indices per row is min(k, max(0, p-W+1))."""
+    rng = np.random.default_rng(24)
+    d, n, k, W = 128, 70, 9, 13
+    q = bf16_exact((n, 4, d), rng)
+    K = bf16_exact((1, n, d), rng)
+    V = bf16_exact((1, n, d), rng)
+    pos = orc.query_positions(n, n)
+    sel = orc.full_attn_select_rows(q, K, V, pos, k, W, orc.default_scale(d))
+    for t in range(n):
+        row = sel["idx"][t, 0]
+        cnt = int((row >= 0).sum())
+        assert cnt == min(k, max(0, t - W + 1))
+        assert np.all(row[:cnt] <= t - W)
+        assert np.all(np.diff(row[:cnt]) > 0)
+        assert np.all(row[cnt:] == -1)
+
+
+# ---------------------------------------------------------- chunk and decode
+
+def test_chunk_rows_equal_full_prefill_rows():
+    """Consistency: the rows of a chunk at the end of a cache equal the same
+    rows of a prefill over the whole sequence (outputs and selections)."""
+    rng = np.random.default_rng(31)
+    d, n, nq, k, W = 128, 64, 16, 6, 5
+    q = bf16_exact((n, 8, d), rng)
+    K = bf16_exact((2, n, d), rng)
+    V = bf16_exact((2, n, d), rng)
+    s = orc.default_scale(d)
+    full = orc.full_attn_select_rows(q, K, V, orc.query_positions(n, n), k, W, s)
+    chunk = orc.full_attn_select_rows(q[n - nq:], K, V, orc.query_positions(nq, n), k, W, s)
+    np.testing.assert_allclose(chunk["o"], full["o"][n - nq:], atol=0)
+    assert np.array_equal(chunk["idx"], full["idx"][n - nq:])
+
+
+def test_decode_step_equals_prefill_row():
+    """Consistency: a decode step at position p (after writing kv_new into slot
+    p) equals prefill row p, for the full layer and for each sparse layer,
+    and every sparse layer uses the one selection of the full layer."""
+    rng = np.random.default_rng(32)
+    d, n, k, W, Hq, Hkv = 128, 40, 5, 4, 8, 2
+    s = orc.default_scale(d)
+    q = bf16_exact((n, Hq, d), rng)
+    qs = [bf16_exact((n, Hq, d), rng) for _ in range(3)]
+    K = bf16_exact((Hkv, n, d), rng)
+    V = bf16_exact((Hkv, n, d), rng)
+    pos = orc.query_positions(n, n)
+    full = orc.full_attn_select_rows(q, K, V, pos, k, W, s)
+    sparse = [orc.sparse_attention_rows(x, K, V, full["idx"], pos, W, s)[0] for x in qs]
+    Kc = np.zeros((Hkv, n + 3, d), np.float32)
+    Vc = np.zeros((Hkv, n + 3, d), np.float32)
+    Kc[:, :n - 1] = K[:, :n - 1]
+    Vc[:, :n - 1] = V[:, :n - 1]
+    kv_new = np.stack([K[:, n - 1], V[:, n - 1]], axis=1)
+    dec = orc.decode_step(q[n - 1], [x[n - 1] for x in qs], kv_new, Kc, Vc, n, k, W, s)
+    np.testing.assert_allclose(dec["o_full"], full["o"][n - 1], atol=0)
+    assert np.array_equal(dec["idx"], full["idx"][n - 1])
+    for a, b in zip(dec["o_sparse"], sparse):
+        np.testing.assert_allclose(a, b[n - 1], atol=0)
+    assert np.array_equal(Kc[:, n - 1], K[:, n - 1])
+
+
+def test_lse_combine_of_split_partials():
+    """Split partials over disjoint key subsets merged with the log-sum-exp
+    correction equal attention over the union (split-K decode)."""
+    rng = np.random.default_rng(33)
+    d, n = 128, 90
+    q = bf16_exact((4, d), rng, 2.0)
+    K = bf16_exact((n, d), rng)
+    V = bf16_exact((n, d), rng)
+    keys = np.arange(n)
+    whole = orc.attention_over_set(q, K, V, keys, 0.2)
+    parts = [orc.attention_over_set(q, K, V, keys[a:b], 0.2) for a, b in [(0, 13), (13, 60), (60, 90)]]
+    o, lse = orc.lse_combine(parts)
+    np.testing.assert_allclose(o, whole[0], atol=1e-13)
+    np.testing.assert_allclose(lse, whole[1], atol=1e-13)
