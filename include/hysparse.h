@@ -1,0 +1,188 @@
+/*
+ * hysparse.h - C ABI of libhysparse: token-level hybrid sparse attention with
+ * KV Reuse on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these web pages (cited by title and section):
+ *
+ *  [HS2-cs]  "HySparse2 od Xiaomi zkracuje zpracovani dlouheho kontextu",
+ *            section "Proc neni nutne znovu zpracovat cely dlouhy vstup"
+ *            (KV Reuse paragraph): the sparse layers of a hybrid block take
+ *            over the KV cache and the token selection of the full-attention
+ *            layer before them; selection is per token; recent tokens are
+ *            always included and share the cache with the selected ones.
+ *  [DAIR]    "DAIR.AI weekly: HySparse2 ..." bullets "Two levels of KV
+ *            sharing" and "Prefill exits early": same facts; a forced window
+ *            of recent tokens replaces the sliding-window branch.
+ *  [HS2-en]  "HySparse2 Cuts the Prefill Path for Tool-Using Agents", section
+ *            "Tool Responses Turn Prefill Into the Bottleneck": prefill writes
+ *            the KV cache that decoding reuses.
+ *  [SSA-3.6] "Simplified Sparse Attention via Gist Tokens", section 3.6
+ *            "Kernel Design": sparse kernels compute exact attention over the
+ *            kept keys; split partials merge by the log-sum-exp correction.
+ *
+ * Definitions used by every call (d = head_dim = 128, G = q_heads/kv_heads,
+ * query head h reads KV head g = h / G):
+ *   p          absolute position of a query row. Prefill/chunk: row t of n_q
+ *              new rows sits at p = n_kv - n_q + t. Decode: p = seq_lens[b]-1.
+ *   s_h(j)     scale * <q_h, k_g(j)>, scale = 1/sqrt(d) unless given.
+ *   Win(p)     [max(0, p-W+1), p]: forced recent window, the query included.
+ *   C(p)       {j : 0 <= j <= p-W}: top-k candidates (tokens older than the
+ *              window).
+ *   sigma(j)   max over the G heads of group g of s_h(j): selection score.
+ *   I(p, g)    top_k members of C(p) by (sigma desc, j asc); all of C(p) when
+ *              |C(p)| <= top_k.
+ * The pages do not print the score, the window extent or the candidate set;
+ * the definitions above are the readings this library implements.
+ *
+ * Conventions (all calls):
+ *  - Element types: q, o, kv, kv_new are bf16 (raw uint16 storage);
+ *    lse is fp32; idx and seq_lens are int32. All are device pointers.
+ *  - Layouts (row-major, innermost last):
+ *      q, o (prefill)   [batch][n_q][q_heads][d]
+ *      q, o (decode)    [batch][q_heads][d]            (n_q == 1)
+ *      lse              [batch][q_heads][n_q]           (may be NULL)
+ *      idx              [batch][n_q][kv_heads][top_k]   ascending, -1 padded
+ *      kv_new           [batch][kv_heads][2][d]         (K row, then V row)
+ *      kv (cache)       element (b, g, t, K|V, e) at
+ *                         b*kv_stride_b + g*kv_stride_h + t*kv_stride_t
+ *                         + (V ? kv_v_offset : 0) + e
+ *                       Strides of 0 select the default interleaved layout
+ *                       [batch][kv_heads][kv_capacity][2][d]. Every K and V
+ *                       row must start on a 16-byte boundary.
+ *  - Ownership: the caller owns every buffer, including the workspace sized
+ *    by hs_workspace_size. The library allocates no device memory and keeps
+ *    no pointer after a call returns.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *    stream). All work is enqueued asynchronously on it; buffers must stay
+ *    valid until the stream reaches them. No call synchronises the host.
+ *  - Errors: arguments are validated on the host before anything is
+ *    enqueued, so a non-OK status means no work was queued (except
+ *    HS_ERR_HIP, reported when a launch fails). A detail message for the
+ *    calling thread's last failure is returned by hs_last_error(). No C++
+ *    exception crosses this boundary. Faults inside kernels surface at the
+ *    caller's next synchronisation, as for any HIP kernel.
+ *  - Device: the current HIP device must be gfx950, else HS_ERR_UNSUPPORTED.
+ *  - Inputs must be finite; NaN or Inf inputs give unspecified results.
+ *  - Calls are reentrant; concurrent calls need separate workspaces.
+ */
+#ifndef HYSPARSE_H
+#define HYSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HS_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+typedef enum {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment or size         */
+  HS_ERR_UNSUPPORTED = 2, /* device is not gfx950, or an unsupported shape  */
+  HS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  HS_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed    */
+  HS_ERR_INTERNAL = 5
+} hs_status;
+
+typedef enum {
+  HS_OP_FULL_ATTN_SELECT = 0,
+  HS_OP_SPARSE_ATTN_REUSE = 1,
+  HS_OP_DECODE_STEP = 2
+} hs_op;
+
+/* hs_shape.flags */
+#define HS_FLAG_EXACT_RESCAN 1u /* every selection row takes the exact
+                                   rescan path instead of the sampled
+                                   threshold filter (testing hook; same
+                                   results, slower) */
+
+typedef struct {
+  int32_t batch;       /* B >= 1                                            */
+  int32_t n_q;         /* query rows per sequence; 1 for decode calls       */
+  int32_t n_kv;        /* prefill: keys visible to the last query row       */
+  int32_t kv_capacity; /* token slots per (b, kv head) in the cache         */
+  int32_t q_heads;     /* Hq; Hq % Hkv == 0 and Hq / Hkv in {1,2,4,8}       */
+  int32_t kv_heads;    /* Hkv >= 1                                          */
+  int32_t head_dim;    /* must be 128                                       */
+  int32_t top_k;       /* k >= 0                                            */
+  int32_t window;      /* W >= 1 (the window contains the query itself)     */
+  float scale;         /* 0 selects 1/sqrt(head_dim)                        */
+  int64_t kv_stride_b; /* elements; 0 with the three below = default layout */
+  int64_t kv_stride_h;
+  int64_t kv_stride_t;
+  int64_t kv_v_offset;
+  uint32_t flags;      /* HS_FLAG_*                                         */
+  uint32_t reserved;   /* must be 0                                         */
+} hs_shape;
+
+/* Workspace bytes that `op` needs for shape `s`. For HS_OP_DECODE_STEP and
+ * for decode calls of HS_OP_SPARSE_ATTN_REUSE, max_seq_len bounds every
+ * seq_lens[b] of the calls the workspace will serve; it is ignored for
+ * prefill. Writes the size to *bytes (0 is a valid answer). */
+hs_status hs_workspace_size(hs_op op, const hs_shape* s, int32_t max_seq_len,
+                            size_t* bytes);
+
+/* Full-attention layer of a hybrid block, prefill or chunked prefill
+ * ([HS2-cs], [DAIR], [HS2-en]). For every batch b, query row t and query
+ * head h: o = softmax_j(s_h(j)) v_g(j) over 0 <= j <= p (causal GQA
+ * attention) and lse = log sum_j exp(s_h(j)). For every (b, t, g): idx row =
+ * I(p, g) in ascending order, -1 padded to top_k.
+ *   q    bf16 [B][n_q][Hq][d]; kv: the cache, rows [0, n_kv) valid (the
+ *        chunk's own K/V rows already written at [n_kv-n_q, n_kv)).
+ *   o    bf16 [B][n_q][Hq][d]; lse fp32 [B][Hq][n_q] or NULL;
+ *   idx  int32 [B][n_q][Hkv][top_k] (may be NULL only when top_k == 0).
+ * Requires 1 <= n_q <= n_kv <= kv_capacity. */
+hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv,
+                              void* o, float* lse, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* One sparse layer of a hybrid block ([HS2-cs], [DAIR]): reuses the full
+ * layer's KV cache and selection. For every row and head h (group g):
+ * o = softmax over j in S of s_h(j), weighted sum of v_g(j), where
+ * S = {valid entries of the idx row} U Win(p). Writes nothing to the cache.
+ *   Prefill: seq_lens == NULL; q, o [B][n_q][Hq][d]; idx [B][n_q][Hkv][k];
+ *            p = n_kv - n_q + t.
+ *   Decode:  seq_lens != NULL (device int32 [B], context length including
+ *            the newest token), n_q == 1; q, o [B][Hq][d]; idx [B][Hkv][k];
+ *            p = seq_lens[b] - 1.
+ * Every valid idx entry must lie in C(p) and rows must hold no duplicates
+ * (as produced by hs_full_attn_select / hs_decode_step); entries < 0 are
+ * padding. */
+hs_status hs_sparse_attn_reuse(const hs_shape* s, const void* q,
+                               const void* kv, const int32_t* idx,
+                               const int32_t* seq_lens, void* o, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Full-attention layer for one decode step over a batch ([HS2-en],
+ * [HS2-cs]): writes kv_new[b] into cache slot seq_lens[b]-1, attends over
+ * [0, seq_lens[b]) for each query head, and selects once: idx[b][g] =
+ * I(seq_lens[b]-1, g), which the following sparse layers pass unchanged to
+ * hs_sparse_attn_reuse (decode form).
+ *   q       bf16 [B][Hq][d];  kv_new bf16 [B][Hkv][2][d];  kv: the cache.
+ *   seq_lens device int32 [B], 1 <= seq_lens[b] <= max_seq_len
+ *           <= kv_capacity (host-side bound used for launch sizing).
+ *   o       bf16 [B][Hq][d]; lse fp32 [B][Hq] or NULL;
+ *   idx     int32 [B][Hkv][top_k]. */
+hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new,
+                         void* kv, const int32_t* seq_lens,
+                         int32_t max_seq_len, void* o, float* lse,
+                         int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Static English name of a status code. */
+const char* hs_status_string(hs_status st);
+
+/* Detail message of the calling thread's most recent failed call ("" if
+ * none). Valid until the thread's next library call. */
+const char* hs_last_error(void);
+
+/* HS_VERSION of the built library. */
+int32_t hs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYSPARSE_H */

@@ -1,0 +1,121 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import token_level_sparse_hs_amd as hs
+from token_level_sparse_hs_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hysparse.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from token_level_sparse_hs_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    ver = int(re.search(r"#define HS_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.hs_version() == ver
+    for st in range(6):
+        assert lib.hs_status_string(st)
+    assert lib.hs_status_string(99) == b"unknown status"
+
+
+def test_shape_struct_matches_header():
+    # 9 int32 + float + 4 int64 + 2 uint32 with natural alignment
+    assert ctypes.sizeof(_lib.HsShape) == 80
+
+
+def base_shape(**kw):
+    d = dict(batch=1, n_q=64, n_kv=64, kv_capacity=64, q_heads=8, kv_heads=2, top_k=16, window=8)
+    d.update(kw)
+    return hs.make_shape(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), _lib.HS_ERR_INVALID_ARG),
+    (dict(head_dim=64), _lib.HS_ERR_UNSUPPORTED),
+    (dict(q_heads=6, kv_heads=4), _lib.HS_ERR_INVALID_ARG),
+    (dict(q_heads=48, kv_heads=3), _lib.HS_ERR_UNSUPPORTED),
+    (dict(top_k=-1), _lib.HS_ERR_INVALID_ARG),
+    (dict(top_k=9000), _lib.HS_ERR_INVALID_ARG),
+    (dict(window=0), _lib.HS_ERR_INVALID_ARG),
+    (dict(n_q=65), _lib.HS_ERR_INVALID_ARG),
+    (dict(n_kv=65), _lib.HS_ERR_INVALID_ARG),
+    (dict(flags=8), _lib.HS_ERR_INVALID_ARG),
+    (dict(kv_strides=(0, 0, 12, 0)), _lib.HS_ERR_INVALID_ARG),
+])
+def test_invalid_shapes_rejected_before_launch(lib, kw, status):
+    s = base_shape(**kw)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    st = lib.hs_full_attn_select(ctypes.byref(s), fake, fake, fake, None, fake, fake, 1 << 30, None)
+    assert st == status, lib.hs_last_error()
+    assert lib.hs_last_error()
+
+
+def test_null_pointers_and_workspace(lib):
+    s = base_shape()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.hs_full_attn_select(ctypes.byref(s), None, fake, fake, None, fake, fake, 1 << 30, None) == _lib.HS_ERR_INVALID_ARG
+    assert lib.hs_full_attn_select(ctypes.byref(s), fake, fake, fake, None, None, fake, 1 << 30, None) == _lib.HS_ERR_INVALID_ARG
+    need = _lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, s)
+    assert need > 0
+    st = lib.hs_full_attn_select(ctypes.byref(s), fake, fake, fake, None, fake, fake, need - 1, None)
+    assert st == _lib.HS_ERR_WORKSPACE
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.hs_full_attn_select(ctypes.byref(s), mis, fake, fake, None, fake, fake, need, None) == _lib.HS_ERR_INVALID_ARG
+    sd = base_shape(n_q=1)
+    assert lib.hs_decode_step(ctypes.byref(sd), fake, fake, fake, None, 64, fake, None, fake, fake, 1 << 30, None) == _lib.HS_ERR_INVALID_ARG
+    assert lib.hs_decode_step(ctypes.byref(sd), fake, fake, fake, fake, 65, fake, None, fake, fake, 1 << 30, None) == _lib.HS_ERR_INVALID_ARG
+    sp = base_shape(n_q=2)
+    assert lib.hs_sparse_attn_reuse(ctypes.byref(sp), fake, fake, fake, fake, fake, fake, 1 << 30, None) == _lib.HS_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(lib):
+    s = base_shape(top_k=0)
+    assert _lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, s) == 0
+    s = base_shape(n_q=1)
+    assert _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s, 0) == 0
+    assert _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s, 64) > 0
+    assert _lib.workspace_size(_lib.HS_OP_DECODE_STEP, s, 64) > 0
+    with pytest.raises(_lib.HsError):
+        _lib.workspace_size(_lib.HS_OP_DECODE_STEP, s, 0)
+    # large workload sizes stay within the memory of one GPU
+    big = hs.make_shape(batch=1, n_q=16384, n_kv=1064960, kv_capacity=1064976, q_heads=32, kv_heads=4,
+                        top_k=4096, window=1024)
+    assert _lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, big) < 16 << 30
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libhysparse.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

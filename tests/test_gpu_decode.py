@@ -1,0 +1,79 @@
+"""GPU parity of the decode path: append + full attention + select once, then
+sparse layers that reuse the one selection, over several steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import token_level_sparse_hs_amd as hs
+from token_level_sparse_hs_amd import synth
+from parity import OutStats, check_idx_row, f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_decode(lengths, steps, Hq, Hkv, k, W, seed, n_sparse=2):
+    print(f"[case] decode lengths={lengths} steps={steps} Hq={Hq} Hkv={Hkv} k={k} W={W} seed={seed}", flush=True)
+    B = len(lengths)
+    cap = max(lengths) + steps
+    kv = torch.zeros((B, Hkv, cap, 2, 128), dtype=torch.bfloat16, device=DEV)
+    for b, L in enumerate(lengths):
+        kv[b, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), seed + 17 * b, DEV)
+    Ks = [kv[b, :, :, 0].float().cpu().numpy() for b in range(B)]
+    Vs = [kv[b, :, :, 1].float().cpu().numpy() for b in range(B)]
+    scale = orc.default_scale(128)
+    full, sparse = OutStats(), OutStats()
+    swaps = 0
+    for s in range(steps):
+        cur = [L + s + 1 for L in lengths]
+        seq_lens = torch.tensor(cur, dtype=torch.int32, device=DEV)
+        q = synth.randn_bf16((B, Hq, 128), seed + 1000 + s, DEV)
+        kv_new = synth.randn_bf16((B, Hkv, 2, 128), seed + 2000 + s, DEV)
+        qs = [synth.randn_bf16((B, Hq, 128), seed + 3000 + 10 * s + i, DEV) for i in range(n_sparse)]
+        o, lse, idx = hs.decode_step(q, kv_new, kv, seq_lens, max(cur), top_k=k, window=W)
+        osp = [hs.sparse_attn_reuse(x, kv, idx, top_k=k, window=W, seq_lens=seq_lens) for x in qs]
+        torch.cuda.synchronize()
+        o_np, lse_np, idx_np = f32(o), lse.cpu().numpy(), idx.cpu().numpy()
+        for b in range(B):
+            ref = orc.decode_step(f32(q[b]), [f32(x[b]) for x in qs], f32(kv_new[b]), Ks[b], Vs[b], cur[b], k, W, scale)
+            full.add(o_np[b], ref["o_full"])
+            assert np.abs(lse_np[b] - ref["lse_full"]).max() <= 1e-3
+            for g in range(Hkv):
+                swaps += check_idx_row(idx_np[b, g], ref["idx"][g], ref["sigma"][g], ref["tau"][g], cur[b] - 1, W, k,
+                                       where=f"step{s} b{b} g{g}")
+            pos = np.array([cur[b] - 1])
+            for x, osx in zip(qs, osp):
+                r, _ = orc.sparse_attention_rows(f32(x[b])[None], Ks[b], Vs[b], idx_np[b][None], pos, W, scale)
+                sparse.add(f32(osx[b]), r[0])
+        # the cache row written by the library equals kv_new
+        for b in range(B):
+            assert torch.equal(kv[b, :, cur[b] - 1], kv_new[b])
+    full.check("decode full o")
+    sparse.check("decode sparse o")
+    return swaps
+
+
+def test_decode_small_batch():
+    run_decode([300, 1200, 5000], 3, 8, 2, 64, 32, seed=11)
+
+
+def test_decode_gqa4_short_rows():
+    # rows with fewer candidates than k, and a row inside the window
+    run_decode([5, 40, 100, 700], 2, 4, 1, 64, 32, seed=12)
+
+
+def test_decode_exact_ties():
+    B, Hq, Hkv, k, W = 1, 8, 1, 4, 4
+    L = 64
+    kv = torch.zeros((B, Hkv, L + 1, 2, 128), dtype=torch.bfloat16, device=DEV)
+    kv[0, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 77, DEV)
+    q = synth.randn_bf16((B, Hq, 128), 78, DEV)
+    hot = (q[0].float().sum(0) / q[0].float().sum(0).norm() * 20).to(torch.bfloat16)
+    for j in (3, 9, 10, 30, 31, 50):
+        kv[0, 0, j, 0] = hot
+    kv_new = synth.randn_bf16((B, Hkv, 2, 128), 79, DEV)
+    seq_lens = torch.tensor([L + 1], dtype=torch.int32, device=DEV)
+    o, lse, idx = hs.decode_step(q, kv_new, kv, seq_lens, L + 1, top_k=k, window=W)
+    torch.cuda.synchronize()
+    assert idx[0, 0].tolist() == [3, 9, 10, 30]

@@ -1,0 +1,422 @@
+// C ABI of libhysparse: argument validation, workspace planning and launch
+// orchestration. Every argument is checked on the host before anything is
+// enqueued; the library allocates no device memory and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/hysparse.h"
+#include "hs_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hs_status fail(hs_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hs_status fail(hs_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hs_status ok() {
+  g_last_error.clear();
+  return HS_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// ------------------------------------------------------------ device check
+
+std::mutex g_arch_mu;
+std::vector<int> g_arch_state;  // per device: 0 unknown, 1 ok, 2 unsupported
+
+hs_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(HS_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if ((int)g_arch_state.size() <= dev) g_arch_state.resize(dev + 1, 0);
+  if (g_arch_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(HS_ERR_HIP, "hipGetDeviceProperties failed");
+    g_arch_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (g_arch_state[dev] == 2) return fail(HS_ERR_UNSUPPORTED, "device %d is %s, libhysparse needs gfx950", dev, prop.gcnArchName);
+  }
+  if (g_arch_state[dev] == 2) return fail(HS_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return HS_OK;
+}
+
+// ------------------------------------------------------------ shape checks
+
+struct Layout {
+  int64_t sb, sh, st, voff;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hs_status validate_common(const hs_shape* s, Layout* lay) {
+  if (!s) return fail(HS_ERR_INVALID_ARG, "shape is NULL");
+  if (s->reserved != 0) return fail(HS_ERR_INVALID_ARG, "reserved must be 0");
+  if (s->batch < 1) return fail(HS_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
+  if (s->head_dim != 128) return fail(HS_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
+  if (s->kv_heads < 1 || s->q_heads < 1 || s->q_heads % s->kv_heads != 0)
+    return fail(HS_ERR_INVALID_ARG, "q_heads (%d) must be a positive multiple of kv_heads (%d)", s->q_heads, s->kv_heads);
+  const int G = s->q_heads / s->kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(HS_ERR_UNSUPPORTED, "q_heads/kv_heads must be 1, 2, 4 or 8 (got %d)", G);
+  if (s->top_k < 0 || s->top_k > hs::kMaxTopK)
+    return fail(HS_ERR_INVALID_ARG, "top_k must be in [0, %d] (got %d)", hs::kMaxTopK, s->top_k);
+  if (s->window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", s->window);
+  if (s->kv_capacity < 1) return fail(HS_ERR_INVALID_ARG, "kv_capacity must be >= 1");
+  if (!(s->scale >= 0.f) || std::isinf(s->scale)) return fail(HS_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if ((s->flags & ~HS_FLAG_EXACT_RESCAN) != 0) return fail(HS_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  Layout l;
+  if (s->kv_stride_b == 0 && s->kv_stride_h == 0 && s->kv_stride_t == 0 && s->kv_v_offset == 0) {
+    l.st = 2 * 128;
+    l.voff = 128;
+    l.sh = (int64_t)s->kv_capacity * l.st;
+    l.sb = (int64_t)s->kv_heads * l.sh;
+  } else {
+    l.sb = s->kv_stride_b;
+    l.sh = s->kv_stride_h;
+    l.st = s->kv_stride_t;
+    l.voff = s->kv_v_offset;
+    if (l.sb < 0 || l.sh < 0 || l.st <= 0 || l.voff < 0)
+      return fail(HS_ERR_INVALID_ARG, "cache strides must be non-negative (t-stride positive)");
+    if (l.sb % 8 || l.sh % 8 || l.st % 8 || l.voff % 8)
+      return fail(HS_ERR_INVALID_ARG, "cache strides and V offset must be multiples of 8 elements (16-byte rows)");
+  }
+  *lay = l;
+  return HS_OK;
+}
+
+float eff_scale(const hs_shape* s) { return s->scale == 0.f ? 1.0f / std::sqrt((float)s->head_dim) : s->scale; }
+
+hs::KvView kv_view(const void* kv, const Layout& l) {
+  return hs::KvView{static_cast<const uint16_t*>(kv), l.sb, l.sh, l.st, l.voff};
+}
+
+// ------------------------------------------------------------ plans
+
+struct PrefillPlan {
+  int64_t rows = 0;
+  int cap = 0;
+  int stride = 1;
+  int max_samples = 0;
+  bool sample = false;
+  size_t off_theta = 0, off_counts = 0, off_bs = 0, off_bj = 0, off_samples = 0, off_stat = 0, total = 0;
+};
+
+PrefillPlan plan_prefill(const hs_shape* s) {
+  PrefillPlan p;
+  p.rows = (int64_t)s->batch * s->n_q * s->kv_heads;
+  if (s->top_k == 0) return p;
+  const int64_t max_cand = std::max<int64_t>(0, (int64_t)s->n_kv - s->window + 1);
+  p.cap = (int)std::min<int64_t>(round_up(3 * (int64_t)s->top_k + 256, 64), std::max<int64_t>(max_cand, 1));
+  p.sample = max_cand > p.cap;
+  p.stride = std::max(1, s->top_k / 64);
+  p.max_samples = p.sample ? (int)round_up((max_cand + p.stride - 1) / p.stride, 64) : 0;
+  size_t o = 0;
+  p.off_theta = o;
+  o = align_up(o + (size_t)p.rows * 4);
+  p.off_counts = o;
+  o = align_up(o + (size_t)p.rows * 4);
+  p.off_bs = o;
+  o = align_up(o + (size_t)p.rows * p.cap * 4);
+  p.off_bj = o;
+  o = align_up(o + (size_t)p.rows * p.cap * 4);
+  p.off_samples = o;
+  o = align_up(o + (size_t)p.rows * p.max_samples * 4);
+  p.off_stat = o;
+  o = align_up(o + 4);
+  p.total = o;
+  return p;
+}
+
+struct DecodePlan {
+  int splits = 1, split_len = 32;
+  int64_t sigma_stride = 0;
+  size_t off_sigma = 0, off_part = 0, total = 0;
+};
+
+// Splits a per-(b, g) key stream of up to `nkeys` keys so that the grid holds
+// roughly 8192 waves (32 per CU), in multiples of 32 keys.
+void plan_splits(int64_t bg, int64_t nkeys, int* splits, int* split_len) {
+  const int64_t target = std::max<int64_t>(1, (8192 + bg - 1) / bg);
+  int64_t len = round_up(std::max<int64_t>(1, (nkeys + target - 1) / target), 32);
+  len = std::max<int64_t>(len, 32);
+  *split_len = (int)len;
+  *splits = (int)std::max<int64_t>(1, (nkeys + len - 1) / len);
+}
+
+DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
+  DecodePlan p;
+  const int G = s->q_heads / s->kv_heads;
+  const int64_t bg = (int64_t)s->batch * s->kv_heads;
+  plan_splits(bg, max_seq_len, &p.splits, &p.split_len);
+  p.sigma_stride = round_up(max_seq_len, 64);
+  size_t o = 0;
+  p.off_sigma = o;
+  o = align_up(o + (s->top_k > 0 ? (size_t)bg * p.sigma_stride * 4 : 0));
+  p.off_part = o;
+  o = align_up(o + (size_t)bg * p.splits * G * (128 + 2) * 4);
+  p.total = o;
+  return p;
+}
+
+DecodePlan plan_decode_sparse(const hs_shape* s) {
+  DecodePlan p;
+  const int G = s->q_heads / s->kv_heads;
+  const int64_t bg = (int64_t)s->batch * s->kv_heads;
+  plan_splits(bg, (int64_t)s->top_k + s->window, &p.splits, &p.split_len);
+  p.off_part = 0;
+  p.total = align_up((size_t)bg * p.splits * G * (128 + 2) * 4);
+  return p;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess) return fail(HS_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* hs_status_string(hs_status st) {
+  switch (st) {
+    case HS_OK: return "ok";
+    case HS_ERR_INVALID_ARG: return "invalid argument";
+    case HS_ERR_UNSUPPORTED: return "unsupported";
+    case HS_ERR_WORKSPACE: return "workspace too small";
+    case HS_ERR_HIP: return "HIP error";
+    case HS_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+const char* hs_last_error(void) { return g_last_error.c_str(); }
+
+int32_t hs_version(void) { return HS_VERSION; }
+
+hs_status hs_workspace_size(hs_op op, const hs_shape* s, int32_t max_seq_len, size_t* bytes) {
+  Layout lay;
+  if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  switch (op) {
+    case HS_OP_FULL_ATTN_SELECT:
+      if (s->n_q < 1 || s->n_kv < s->n_q) return fail(HS_ERR_INVALID_ARG, "need 1 <= n_q <= n_kv");
+      *bytes = plan_prefill(s).total;
+      return ok();
+    case HS_OP_SPARSE_ATTN_REUSE:
+      *bytes = max_seq_len > 0 ? plan_decode_sparse(s).total : 0;
+      return ok();
+    case HS_OP_DECODE_STEP:
+      if (max_seq_len < 1) return fail(HS_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+      *bytes = plan_decode_full(s, max_seq_len).total;
+      return ok();
+  }
+  return fail(HS_ERR_INVALID_ARG, "unknown op %d", (int)op);
+}
+
+hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, void* o, float* lse, int32_t* idx,
+                              void* ws, size_t ws_bytes, void* stream) {
+  Layout lay;
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  if (s->n_q < 1 || s->n_kv < s->n_q || s->n_kv > s->kv_capacity)
+    return fail(HS_ERR_INVALID_ARG, "need 1 <= n_q (%d) <= n_kv (%d) <= kv_capacity (%d)", s->n_q, s->n_kv, s->kv_capacity);
+  if (!q || !kv || !o) return fail(HS_ERR_INVALID_ARG, "q, kv and o must be non-NULL");
+  if (s->top_k > 0 && !idx) return fail(HS_ERR_INVALID_ARG, "idx must be non-NULL when top_k > 0");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o)) return fail(HS_ERR_INVALID_ARG, "q, kv and o must be 16-byte aligned");
+  if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3)) || (idx && (reinterpret_cast<uintptr_t>(idx) & 3)))
+    return fail(HS_ERR_INVALID_ARG, "lse and idx must be 4-byte aligned");
+  const PrefillPlan plan = plan_prefill(s);
+  if (plan.total > 0 && (!ws || ws_bytes < plan.total))
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, ws_bytes);
+  if (plan.total > 0 && (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)))
+    return fail(HS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  st = check_device();
+  if (st != HS_OK) return st;
+
+  hipStream_t hst = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const float scale = eff_scale(s);
+  const hs::KvView kvv = kv_view(kv, lay);
+  const bool select = s->top_k > 0;
+  float* theta = select ? reinterpret_cast<float*>(w + plan.off_theta) : nullptr;
+
+  if (select) {
+    if (plan.sample) {
+      hs::SampleParams sp{};
+      sp.q = static_cast<const uint16_t*>(q);
+      sp.kv = kvv;
+      sp.B = s->batch; sp.n_q = s->n_q; sp.n_kv = s->n_kv; sp.Hq = s->q_heads; sp.Hkv = s->kv_heads;
+      sp.window = s->window; sp.scale = scale; sp.stride = plan.stride; sp.max_samples = plan.max_samples;
+      sp.samples = reinterpret_cast<float*>(w + plan.off_samples);
+      HIP_TRY(hs::launch_sample_scores(sp, hst));
+    }
+    hs::ThresholdParams tp{};
+    tp.B = s->batch; tp.n_q = s->n_q; tp.n_kv = s->n_kv; tp.Hkv = s->kv_heads; tp.top_k = s->top_k;
+    tp.window = s->window; tp.cap = plan.cap; tp.stride = plan.stride; tp.max_samples = plan.max_samples;
+    tp.samples = reinterpret_cast<const float*>(w + plan.off_samples);
+    tp.theta = theta;
+    HIP_TRY(hs::launch_threshold(tp, plan.rows, hst));
+  }
+
+  hs::PrefillParams pp{};
+  pp.q = static_cast<const uint16_t*>(q);
+  pp.kv = kvv;
+  pp.o = static_cast<uint16_t*>(o);
+  pp.lse = lse;
+  pp.B = s->batch; pp.n_q = s->n_q; pp.n_kv = s->n_kv; pp.Hq = s->q_heads; pp.Hkv = s->kv_heads; pp.window = s->window;
+  pp.scale = scale;
+  pp.select = select ? 1 : 0;
+  pp.theta = theta;
+  pp.buf_sigma = select ? reinterpret_cast<float*>(w + plan.off_bs) : nullptr;
+  pp.buf_j = select ? reinterpret_cast<int32_t*>(w + plan.off_bj) : nullptr;
+  pp.counts = select ? reinterpret_cast<int32_t*>(w + plan.off_counts) : nullptr;
+  pp.cap = plan.cap;
+  HIP_TRY(hs::launch_prefill_attn(pp, hst));
+
+  if (select) {
+    hs::SelectParams sp{};
+    sp.q = static_cast<const uint16_t*>(q);
+    sp.kv = kvv;
+    sp.B = s->batch; sp.n_q = s->n_q; sp.n_kv = s->n_kv; sp.Hq = s->q_heads; sp.Hkv = s->kv_heads;
+    sp.top_k = s->top_k; sp.window = s->window; sp.scale = scale;
+    sp.buf_sigma = pp.buf_sigma; sp.buf_j = pp.buf_j; sp.counts = pp.counts; sp.cap = plan.cap;
+    sp.force_rescan = (s->flags & HS_FLAG_EXACT_RESCAN) ? 1 : 0;
+    sp.idx = idx;
+    sp.rescan_count = nullptr;
+    HIP_TRY(hs::launch_select_prefill(sp, plan.rows, hst));
+  }
+  return ok();
+}
+
+hs_status hs_sparse_attn_reuse(const hs_shape* s, const void* q, const void* kv, const int32_t* idx,
+                               const int32_t* seq_lens, void* o, void* ws, size_t ws_bytes, void* stream) {
+  Layout lay;
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  const bool decode = seq_lens != nullptr;
+  if (decode) {
+    if (s->n_q != 1) return fail(HS_ERR_INVALID_ARG, "decode calls need n_q == 1 (got %d)", s->n_q);
+  } else if (s->n_q < 1 || s->n_kv < s->n_q || s->n_kv > s->kv_capacity) {
+    return fail(HS_ERR_INVALID_ARG, "need 1 <= n_q (%d) <= n_kv (%d) <= kv_capacity (%d)", s->n_q, s->n_kv, s->kv_capacity);
+  }
+  if (!q || !kv || !o) return fail(HS_ERR_INVALID_ARG, "q, kv and o must be non-NULL");
+  if (s->top_k > 0 && !idx) return fail(HS_ERR_INVALID_ARG, "idx must be non-NULL when top_k > 0");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o)) return fail(HS_ERR_INVALID_ARG, "q, kv and o must be 16-byte aligned");
+  DecodePlan plan;
+  if (decode) {
+    plan = plan_decode_sparse(s);
+    if (!ws || ws_bytes < plan.total)
+      return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, ws_bytes);
+    if (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) return fail(HS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  st = check_device();
+  if (st != HS_OK) return st;
+  hipStream_t hst = static_cast<hipStream_t>(stream);
+
+  hs::DecodeParams dp{};
+  dp.q = static_cast<const uint16_t*>(q);
+  dp.kv = kv_view(kv, lay);
+  dp.B = s->batch; dp.n_q = decode ? 1 : s->n_q; dp.n_kv = decode ? s->kv_capacity : s->n_kv; dp.Hq = s->q_heads; dp.Hkv = s->kv_heads;
+  dp.top_k = s->top_k; dp.window = s->window; dp.scale = eff_scale(s);
+  dp.seq_lens = seq_lens;
+  dp.idx = idx;
+  dp.o = static_cast<uint16_t*>(o);
+  dp.lse = nullptr;
+  if (decode) {
+    dp.splits = plan.splits;
+    dp.split_len = plan.split_len;
+    dp.part = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_part);
+    if (plan.splits == 1) dp.part = nullptr;
+  } else {
+    dp.splits = 1;
+    dp.split_len = s->top_k + s->window + 32;
+  }
+  HIP_TRY(hs::launch_sparse(dp, hst));
+  if (decode && plan.splits > 1) {
+    hs::CombineParams cp{};
+    cp.part = dp.part; cp.o = dp.o; cp.lse = nullptr; cp.seq_lens = seq_lens;
+    cp.B = s->batch; cp.Hq = s->q_heads; cp.Hkv = s->kv_heads; cp.splits = plan.splits; cp.split_len = plan.split_len;
+    cp.sparse_k = s->top_k; cp.window = s->window; cp.max_len = s->kv_capacity;
+    HIP_TRY(hs::launch_combine(cp, hst));
+  }
+  return ok();
+}
+
+hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, void* kv, const int32_t* seq_lens,
+                         int32_t max_seq_len, void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+  Layout lay;
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  if (s->n_q != 1) return fail(HS_ERR_INVALID_ARG, "decode calls need n_q == 1 (got %d)", s->n_q);
+  if (max_seq_len < 1 || max_seq_len > s->kv_capacity)
+    return fail(HS_ERR_INVALID_ARG, "need 1 <= max_seq_len (%d) <= kv_capacity (%d)", max_seq_len, s->kv_capacity);
+  if (!q || !kv_new || !kv || !seq_lens || !o) return fail(HS_ERR_INVALID_ARG, "q, kv_new, kv, seq_lens and o must be non-NULL");
+  if (s->top_k > 0 && !idx) return fail(HS_ERR_INVALID_ARG, "idx must be non-NULL when top_k > 0");
+  if (!aligned16(q) || !aligned16(kv_new) || !aligned16(kv) || !aligned16(o))
+    return fail(HS_ERR_INVALID_ARG, "q, kv_new, kv and o must be 16-byte aligned");
+  const DecodePlan plan = plan_decode_full(s, max_seq_len);
+  if (!ws || ws_bytes < plan.total) return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) return fail(HS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  st = check_device();
+  if (st != HS_OK) return st;
+  hipStream_t hst = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+
+  hs::AppendParams ap{};
+  ap.kv_new = static_cast<const uint16_t*>(kv_new);
+  ap.kv = static_cast<uint16_t*>(kv);
+  ap.sb = lay.sb; ap.sh = lay.sh; ap.st = lay.st; ap.voff = lay.voff;
+  ap.seq_lens = seq_lens; ap.B = s->batch; ap.Hkv = s->kv_heads; ap.cap = max_seq_len;
+  HIP_TRY(hs::launch_append(ap, hst));
+
+  hs::DecodeParams dp{};
+  dp.q = static_cast<const uint16_t*>(q);
+  dp.kv = kv_view(kv, lay);
+  dp.B = s->batch; dp.n_q = 1; dp.n_kv = max_seq_len; dp.Hq = s->q_heads; dp.Hkv = s->kv_heads;
+  dp.top_k = s->top_k; dp.window = s->window; dp.scale = eff_scale(s);
+  dp.seq_lens = seq_lens;
+  dp.splits = plan.splits; dp.split_len = plan.split_len;
+  dp.o = static_cast<uint16_t*>(o);
+  dp.lse = lse;
+  dp.part = reinterpret_cast<float*>(w + plan.off_part);
+  dp.sigma = s->top_k > 0 ? reinterpret_cast<float*>(w + plan.off_sigma) : nullptr;
+  dp.sigma_stride = plan.sigma_stride;
+  HIP_TRY(hs::launch_decode_full(dp, hst));
+  if (plan.splits > 1) {
+    hs::CombineParams cp{};
+    cp.part = dp.part; cp.o = dp.o; cp.lse = lse; cp.seq_lens = seq_lens;
+    cp.B = s->batch; cp.Hq = s->q_heads; cp.Hkv = s->kv_heads; cp.splits = plan.splits; cp.split_len = plan.split_len;
+    cp.sparse_k = -1; cp.window = s->window; cp.max_len = max_seq_len;
+    HIP_TRY(hs::launch_combine(cp, hst));
+  }
+  if (s->top_k > 0) {
+    hs::SelectDecodeParams sp{};
+    sp.B = s->batch; sp.Hkv = s->kv_heads; sp.top_k = s->top_k; sp.window = s->window;
+    sp.seq_lens = seq_lens; sp.sigma = dp.sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = idx;
+    HIP_TRY(hs::launch_select_decode(sp, s->batch * s->kv_heads, hst));
+  }
+  return ok();
+}
+
+}  // extern "C"

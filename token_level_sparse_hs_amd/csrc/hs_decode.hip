@@ -1,0 +1,346 @@
+// Gather-based attention for the sparse-reuse layers and for decode (gfx950).
+//
+// Sparse-reuse layers ("HySparse2 od Xiaomi zkracuje zpracovani dlouheho
+// kontextu", section "Proc neni nutne znovu zpracovat cely dlouhy vstup";
+// DAIR.AI weekly, bullet "Two levels of KV sharing"): every sparse layer reuses
+// the full layer's KV cache and selection, attending from its own queries to
+// S = (selected tokens) U (forced recent window). Decode full attention
+// ("HySparse2 Cuts the Prefill Path for Tool-Using Agents", section "Tool
+// Responses Turn Prefill Into the Bottleneck": decoding reuses the cache that
+// prefill wrote) streams a sequence's whole cache once and also emits the
+// group score row that the decode selection ranks. Split partials (m, l, acc)
+// are merged by the log-sum-exp correction ("Simplified Sparse Attention via
+// Gist Tokens", section 3.6, three-kernel split-K decode).
+//
+// Design (MI355X): one wave per work item (row or split), so thousands of
+// independent waves keep enough 16-byte gathers in flight to cover HBM
+// latency; no block-level synchronisation.
+//  * A work item walks a virtual key list in chunks of 32 keys. FULL: keys
+//    [k0, k1) of a decode row. SPARSE: the idx row (entries < 0 are padding)
+//    followed by the window Win(p).
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K rows gathered straight
+//    from the cache into A operands (16 B per lane); the G query heads of the
+//    group occupy MFMA columns 0..G-1, so one K/V row read serves all heads.
+//  * V rows are gathered 4 keys x 8 dims per lane, transposed with byte
+//    permutes into a per-wave LDS tile, and read back as the A operand of
+//    O^T = V^T P^T; P^T is already in B-operand layout in registers.
+//  * Softmax state is per lane (query column = lane%16) with two cross-lane
+//    exchanges (lane^16, lane^32) per chunk; accumulation is fp32.
+#include "hs_common.hpp"
+#include "hs_kernels.hpp"
+
+namespace hs {
+
+namespace {
+
+constexpr int kVtS = 36;  // per-wave V^T tile row stride in bf16 (72 B)
+
+__device__ __forceinline__ void lds_wait() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+template <bool SPARSE>
+struct KeyList {
+  // SPARSE: virtual v < k -> idx[v] (if >= 0), else window token w0 + (v-k).
+  // FULL: v -> v.
+  // Selected entries outside [0, lim] (padding, or a malformed row) are
+  // skipped, so no gather leaves the sequence's valid rows.
+  const int32_t* sel;
+  int k;
+  int w0;
+  int lim;
+  int end;  // virtual end (exclusive)
+  __device__ __forceinline__ int key(int v) const {
+    if (v >= end) return -1;
+    if constexpr (!SPARSE) return v;
+    if (v >= k) return w0 + (v - k);
+    const int j = sel[v];
+    return (j >= 0 && j <= lim) ? j : -1;
+  }
+};
+
+template <int G, bool SPARSE>
+__global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t Vt_all[4][128 * kVtS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, gq = lane >> 4;
+  uint16_t* Vt = Vt_all[wave];
+
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  const bool decode = P.seq_lens != nullptr;
+  int b, t, g, split, p;
+  int64_t total;
+  if (decode) {
+    total = (int64_t)P.B * P.Hkv * P.splits;
+    if (item >= total) return;
+    split = (int)(item % P.splits);
+    const int64_t bg = item / P.splits;
+    g = (int)(bg % P.Hkv);
+    b = (int)(bg / P.Hkv);
+    t = 0;
+    p = imin(P.seq_lens[b], P.n_kv) - 1;  // n_kv carries the host bound max_seq_len
+    if (p < 0) return;
+  } else {
+    total = (int64_t)P.B * P.n_q * P.Hkv;
+    if (item >= total) return;
+    split = 0;
+    g = (int)(item % P.Hkv);
+    const int64_t bt = item / P.Hkv;
+    t = (int)(bt % P.n_q);
+    b = (int)(bt / P.n_q);
+    p = P.n_kv - P.n_q + t;
+  }
+  const int64_t qrow = (int64_t)b * P.n_q + t;  // decode: n_q == 1
+
+  KeyList<SPARSE> kl;
+  int vbeg, vend;
+  if (SPARSE) {
+    kl.sel = P.idx + (qrow * P.Hkv + g) * (int64_t)P.top_k;
+    kl.k = P.top_k;
+    kl.w0 = imax(0, p - P.window + 1);
+    kl.lim = p - P.window;
+    const int nv = P.top_k + (p - kl.w0 + 1);
+    vbeg = split * P.split_len;
+    vend = imin(nv, vbeg + P.split_len);
+  } else {
+    kl.sel = nullptr;
+    kl.k = 0;
+    kl.w0 = 0;
+    kl.lim = p;
+    vbeg = split * P.split_len;
+    vend = imin(p + 1, vbeg + P.split_len);
+  }
+  kl.end = vend;
+  if (vbeg >= vend) return;  // split beyond this row: the combine skips it
+
+  // Query operand: column n = head g*G + n (n < G), dims 32s + 8*gq .. +8.
+  bf16x8 qb[4];
+  {
+    const uint16_t* qp = P.q + (qrow * P.Hq + (int64_t)g * G + (n < G ? n : 0)) * kHeadDim + 8 * gq;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qb[s] = as_bf16x8(n < G ? ld16(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u});
+  }
+
+  f32x4 oacc[8] = {};
+  float m_run = kNegInf, l_part = 0.f;
+  const float cexp = P.scale * kLog2e;
+  const int cand_end = p - P.window;  // last candidate position (FULL score row)
+  float* sig_row = nullptr;
+  if (!SPARSE && P.sigma) sig_row = P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride;
+
+  for (int v0 = vbeg; v0 < vend; v0 += 32) {
+    // --- gather K rows (A operands): tile c row r = n + 16c
+    bf16x8 ka[2][4];
+    bool rv[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int j = kl.key(v0 + n + 16 * c);
+      rv[c] = j >= 0;
+      const uint16_t* kr = P.kv.k_row(b, g, j >= 0 ? j : 0) + 8 * gq;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[c][s] = as_bf16x8(rv[c] ? ld16(kr + 32 * s) : u32x4{0u, 0u, 0u, 0u});
+    }
+    // --- gather V rows: key groups kg = gq and gq+4 (4 keys each), dims 8n..8n+7
+    u32x4 vw[2][4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = kl.key(v0 + 4 * (gq + 4 * hh) + r);
+        vw[hh][r] = j >= 0 ? ld16(P.kv.v_row(b, g, j) + 8 * n) : u32x4{0u, 0u, 0u, 0u};
+      }
+    const uint64_t m0 = ballot(rv[0]), m1 = ballot(rv[1]);
+    const uint32_t vmask = (uint32_t)(m0 & 0xffffu) | ((uint32_t)(m1 & 0xffffu) << 16);
+
+    // --- S^T tiles
+    f32x4 acc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f32x4 a = {};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a = mfma16x16x32(ka[c][s], qb[s], a);
+      acc[c] = a;
+    }
+    // lane holds query column n, chunk keys 16c + 4*gq + i
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!((vmask >> (16 * c + 4 * gq + i)) & 1u)) acc[c][i] = kNegInf;
+
+    if (!SPARSE && sig_row && v0 <= cand_end) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float mxh = group_max<G>(acc[c][i]);
+          const int j = v0 + 16 * c + 4 * gq + i;
+          if (n == 0 && j <= cand_end) sig_row[j] = mxh * P.scale;
+        }
+      }
+    }
+
+    // --- V^T into LDS
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int kg = gq + 4 * hh;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int w = c >> 1;
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        u32x2 tv;
+        tv[0] = __builtin_amdgcn_perm(vw[hh][1][w], vw[hh][0][w], sel);
+        tv[1] = __builtin_amdgcn_perm(vw[hh][3][w], vw[hh][2][w], sel);
+        *reinterpret_cast<u32x2*>(&Vt[(8 * n + c) * kVtS + 4 * kg]) = tv;
+      }
+    }
+
+    // --- online softmax
+    float mx = kNegInf;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[c][i]);
+    mx = xor32_max(xor16_max(mx));
+    const float m_new = fmaxf(m_run, mx * cexp);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(acc[c][i], cexp, -m_use));
+        acc[c][i] = pv;
+        psum += pv;
+      }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int bk = 0; bk < 8; ++bk) oacc[bk] *= alpha;
+    u32x4 pw;
+    pw[0] = pack_bf16x2(acc[0][0], acc[0][1]);
+    pw[1] = pack_bf16x2(acc[0][2], acc[0][3]);
+    pw[2] = pack_bf16x2(acc[1][0], acc[1][1]);
+    pw[3] = pack_bf16x2(acc[1][2], acc[1][3]);
+    const bf16x8 pb = as_bf16x8(pw);
+
+    lds_wait();
+#pragma unroll
+    for (int bk = 0; bk < 8; ++bk) {
+      const uint16_t* vr = &Vt[(16 * bk + n) * kVtS];
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 4 * gq);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 + 4 * gq);
+      const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+      oacc[bk] = mfma16x16x32(as_bf16x8(w), pb, oacc[bk]);
+    }
+    lds_wait();
+  }
+
+  const float l_tot = xor32_sum(xor16_sum(l_part));
+  if (n >= G) return;
+  const int head = g * G + n;
+  if (P.splits == 1) {
+    const float inv = 1.f / l_tot;
+    uint16_t* op = P.o + (qrow * P.Hq + head) * kHeadDim;
+#pragma unroll
+    for (int bk = 0; bk < 8; ++bk) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[bk][0] * inv, oacc[bk][1] * inv);
+      w[1] = pack_bf16x2(oacc[bk][2] * inv, oacc[bk][3] * inv);
+      *reinterpret_cast<u32x2*>(op + 16 * bk + 4 * gq) = w;
+    }
+    if (P.lse && gq == 0) P.lse[((int64_t)b * P.Hq + head) * P.n_q + t] = m_run * kLn2 + __logf(l_tot);
+  } else {
+    float* pp = P.part + ((((int64_t)b * P.Hkv + g) * P.splits + split) * G + n) * (kHeadDim + 2);
+#pragma unroll
+    for (int bk = 0; bk < 8; ++bk)
+      *reinterpret_cast<f32x4*>(pp + 16 * bk + 4 * gq) = oacc[bk];
+    if (gq == 0) {
+      pp[kHeadDim] = m_run;
+      pp[kHeadDim + 1] = l_tot;
+    }
+  }
+}
+
+// Decode: write kv_new[b] into cache slot seq_lens[b]-1.
+__global__ void append_kernel(AppendParams P) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 16-byte piece
+  const int64_t total = (int64_t)P.B * P.Hkv * 2 * 16;
+  if (i >= total) return;
+  const int c = (int)(i & 15);
+  const int kvsel = (int)((i >> 4) & 1);
+  const int64_t bg = i >> 5;
+  const int g = (int)(bg % P.Hkv);
+  const int b = (int)(bg / P.Hkv);
+  const int slot = P.seq_lens[b] - 1;
+  if (slot < 0 || slot >= P.cap) return;  // out-of-range length: nothing written
+  const u32x4 w = ld16(P.kv_new + ((bg * 2 + kvsel) * kHeadDim) + 8 * c);
+  uint16_t* dst = P.kv + (int64_t)b * P.sb + (int64_t)g * P.sh + (int64_t)slot * P.st + (kvsel ? P.voff : 0) + 8 * c;
+  st16(dst, w);
+}
+
+// Log-sum-exp merge of split partials; one 128-thread block per (b, head).
+__global__ __launch_bounds__(128) void combine_kernel(CombineParams P) {
+  const int bh = blockIdx.x;
+  const int head = bh % P.Hq, b = bh / P.Hq;
+  const int G = P.Hq / P.Hkv;
+  const int g = head / G, n = head % G;
+  const int L = imin(P.seq_lens[b], P.max_len);
+  if (L < 1) return;
+  const int nv = P.sparse_k >= 0 ? P.sparse_k + (L < P.window ? L : P.window) : L;
+  const int ns = imin(P.splits, (nv + P.split_len - 1) / P.split_len);
+  const float* base = P.part + (((int64_t)b * P.Hkv + g) * P.splits * G + n) * (kHeadDim + 2);
+  const int64_t sstride = (int64_t)G * (kHeadDim + 2);
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * sstride + kHeadDim]);
+  const float Mu = M == kNegInf ? 0.f : M;
+  float acc = 0.f, l = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* pp = base + s * sstride;
+    const float w = __builtin_amdgcn_exp2f(pp[kHeadDim] - Mu);
+    acc += w * pp[threadIdx.x];
+    l += w * pp[kHeadDim + 1];
+  }
+  const float o = acc / l;
+  P.o[((int64_t)b * P.Hq + head) * kHeadDim + threadIdx.x] = (uint16_t)f32_to_bf16_bits(o);
+  if (P.lse && threadIdx.x == 0) P.lse[(int64_t)b * P.Hq + head] = M * kLn2 + __logf(l);
+}
+
+template <int G, bool SPARSE>
+hipError_t launch_gather_g(const DecodeParams& p, hipStream_t s) {
+  const int64_t items = p.seq_lens ? (int64_t)p.B * p.Hkv * p.splits : (int64_t)p.B * p.n_q * p.Hkv;
+  const int64_t blocks = (items + 3) / 4;
+  flash_gather_kernel<G, SPARSE><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <bool SPARSE>
+hipError_t launch_gather(const DecodeParams& p, hipStream_t s) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_gather_g<1, SPARSE>(p, s);
+    case 2: return launch_gather_g<2, SPARSE>(p, s);
+    case 4: return launch_gather_g<4, SPARSE>(p, s);
+    case 8: return launch_gather_g<8, SPARSE>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_full(const DecodeParams& p, hipStream_t s) { return launch_gather<false>(p, s); }
+hipError_t launch_sparse(const DecodeParams& p, hipStream_t s) { return launch_gather<true>(p, s); }
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.Hkv * 32;
+  append_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
+  combine_kernel<<<dim3((unsigned)(p.B * p.Hq)), dim3(128), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -1,0 +1,122 @@
+// Kernel parameter blocks and launchers of libhysparse (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hs_common.hpp"
+
+namespace hs {
+
+constexpr int kMaxTopK = 8192;   // largest supported top_k
+constexpr int kPrefillKeyTile = 64;
+
+// ----------------------------------------------------------- prefill attention
+struct PrefillParams {
+  const uint16_t* q;  // [B][n_q][Hq][128]
+  KvView kv;
+  uint16_t* o;        // [B][n_q][Hq][128]
+  float* lse;         // [B][Hq][n_q] or null
+  int B, n_q, n_kv, Hq, Hkv, window;
+  float scale;
+  // selection (select == 0: no selection, buffers unused)
+  int select;
+  const float* theta;  // [rows] scaled-score threshold per (b,t,g) row
+  float* buf_sigma;    // [rows][cap]
+  int32_t* buf_j;      // [rows][cap]
+  int32_t* counts;     // [rows]
+  int cap;
+};
+
+// Sampled scores for the per-row filter thresholds.
+struct SampleParams {
+  const uint16_t* q;
+  KvView kv;
+  int B, n_q, n_kv, Hq, Hkv, window;
+  float scale;
+  int stride;       // sampled keys j = s * stride
+  int max_samples;  // row stride of `samples`
+  float* samples;   // [rows][max_samples]
+};
+
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
+hipError_t launch_sample_scores(const SampleParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ selection
+struct SelectParams {
+  const uint16_t* q;
+  KvView kv;
+  int B, n_q, n_kv, Hq, Hkv, top_k, window;
+  float scale;
+  const float* buf_sigma;
+  const int32_t* buf_j;
+  const int32_t* counts;
+  int cap;
+  int force_rescan;
+  int32_t* idx;            // [rows][top_k]
+  uint32_t* rescan_count;  // optional counter of rows that took the rescan
+};
+
+struct ThresholdParams {
+  int B, n_q, n_kv, Hkv, top_k, window, cap, stride, max_samples;
+  const float* samples;
+  float* theta;
+};
+
+struct SelectDecodeParams {
+  int B, Hkv, top_k, window;
+  const int32_t* seq_lens;
+  const float* sigma;  // [B*Hkv][sigma_stride]
+  int64_t sigma_stride;
+  int32_t* idx;        // [B][Hkv][top_k]
+};
+
+hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s);
+hipError_t launch_threshold(const ThresholdParams& p, int64_t rows, hipStream_t s);
+hipError_t launch_select_decode(const SelectDecodeParams& p, int rows, hipStream_t s);
+
+// --------------------------------------------------------- flash-decode family
+// One wave per work item. FULL: contiguous keys [k0, k1) of a decode row,
+// writes the group score row. SPARSE: keys = idx row U forced window.
+struct DecodeParams {
+  const uint16_t* q;  // prefill: [B][n_q][Hq][128]; decode: [B][Hq][128]
+  KvView kv;
+  int B, n_q, n_kv, Hq, Hkv, top_k, window;
+  float scale;
+  const int32_t* seq_lens;  // decode: [B]; prefill: null
+  const int32_t* idx;       // SPARSE: [B][n_q][Hkv][top_k]
+  int splits;               // key splits per (b, g) (decode only)
+  int split_len;            // keys per split (FULL) / virtual keys per split (SPARSE)
+  // outputs
+  uint16_t* o;              // used when splits == 1
+  float* lse;               // [B][Hq][n_q] or null (splits == 1)
+  float* part;              // splits > 1: [B][Hkv][splits][G][128 + 2]
+  float* sigma;             // FULL: [B*Hkv][sigma_stride]
+  int64_t sigma_stride;
+};
+
+struct AppendParams {
+  const uint16_t* kv_new;  // [B][Hkv][2][128]
+  uint16_t* kv;
+  int64_t sb, sh, st, voff;
+  const int32_t* seq_lens;
+  int B, Hkv, cap;
+};
+
+struct CombineParams {
+  const float* part;
+  uint16_t* o;   // [B][Hq][128]
+  float* lse;    // [B][Hq] or null
+  const int32_t* seq_lens;
+  int B, Hq, Hkv, splits, split_len;
+  int sparse_k;  // SPARSE: top_k (virtual keys = top_k + |Win|); FULL: -1
+  int window;
+  int max_len;   // host bound on seq_lens
+};
+
+hipError_t launch_decode_full(const DecodeParams& p, hipStream_t s);
+hipError_t launch_sparse(const DecodeParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+}  // namespace hs

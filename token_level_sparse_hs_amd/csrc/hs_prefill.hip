@@ -1,0 +1,403 @@
+// Prefill full-attention layer with fused token selection (gfx950).
+//
+// Computes, for a chunk of n_q query rows at the end of an n_kv-token cache,
+// causal GQA attention (o, lse) and the per-(row, KV group) candidate set for
+// token-level top-k selection: the full-attention layer of a hybrid block
+// whose selection the following sparse layers reuse ("HySparse2 od Xiaomi
+// zkracuje zpracovani dlouheho kontextu", section "Proc neni nutne znovu
+// zpracovat cely dlouhy vstup"; DAIR.AI weekly, bullets "Two levels of KV
+// sharing" and "Prefill exits early").
+//
+// Design (MI355X):
+//  * One 256-thread block = 4 waves = one KV group g and 4*(32/G) query
+//    tokens. Each wave owns 32 MFMA rows = 32/G tokens x the G query heads of
+//    group g, so the group's heads share every K/V tile staged in LDS and the
+//    group maximum over heads (the selection score) is a reduction over G
+//    adjacent lanes.
+//  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: with the key
+//    axis on MFMA rows and the query rows on lanes, every per-row softmax
+//    quantity (running max, sum, rescale) is lane-local apart from one
+//    lane^32 exchange, and the S^T accumulator is already laid out as the B
+//    operand of the PV product. K tiles live row-major in LDS, V tiles
+//    transposed (written transposed once per tile, read as 2x8-byte pieces).
+//  * Online softmax in fp32 on exp2 with the scale folded into one FMA.
+//  * Selection: the per-lane scaled logits are maxed over the G head lanes
+//    (DPP), staged per wave in LDS, and every candidate (j <= p - W) whose
+//    score reaches the row's threshold is appended, in ascending key order,
+//    to the row's candidate buffer with a wave ballot + mbcnt compaction.
+//    Thresholds come from sampled scores (below); rows whose candidates all
+//    fit the buffer use -inf, i.e. the buffer is then the full score row.
+//  * Blocks run late (long) query tiles first; the group index varies
+//    fastest over blockIdx so that, with blocks dealt round-robin to the 8
+//    XCDs, each XCD's L2 serves one KV head.
+#include "hs_common.hpp"
+#include "hs_kernels.hpp"
+
+namespace hs {
+
+namespace {
+
+constexpr int kKS = 136;  // K tile row stride in bf16 (272 B: conflict-free 16-B reads)
+constexpr int kVS = 68;   // V^T tile row stride in bf16 (136 B)
+
+__device__ __forceinline__ void lds_wait() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// Cooperative load of 64 key rows [key0, key0+64) of (b, g): K row-major into
+// Ks, V transposed into Vt. Rows at or beyond `valid_end` are zero-filled.
+// 256 threads; thread (kq = tid/16, dq = tid%16) moves rows 4kq..4kq+3,
+// dims 8dq..8dq+7.
+__device__ __forceinline__ void load_kv_tile(const KvView& kv, int b, int g, int key0, int valid_end,
+                                             uint16_t* Ks, uint16_t* Vt, bool with_v) {
+  const int tid = threadIdx.x;
+  const int dq = tid & 15, kq = tid >> 4;
+  u32x4 kw[4], vw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = key0 + 4 * kq + r;
+    if (j < valid_end) {
+      kw[r] = ld16(kv.k_row(b, g, j) + 8 * dq);
+      if (with_v) vw[r] = ld16(kv.v_row(b, g, j) + 8 * dq);
+    } else {
+      kw[r] = u32x4{0u, 0u, 0u, 0u};
+      vw[r] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) st16(&Ks[(4 * kq + r) * kKS + 8 * dq], kw[r]);
+  if (with_v) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int w = c >> 1;
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 t;
+      t[0] = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
+      t[1] = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
+      *reinterpret_cast<u32x2*>(&Vt[(8 * dq + c) * kVS + 4 * kq]) = t;
+    }
+  }
+}
+
+// S^T tile (64 keys x 32 query rows) of this wave: acc[c][i] holds the raw
+// dot product of key 32c + 8(i/4) + 4h + i%4 with query row l%32.
+__device__ __forceinline__ void qk_tile(const uint16_t* Ks, const bf16x8* qb, f32x16* acc) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, n = lane & 31;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    f32x16 a = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 kop = as_bf16x8(ld16(&Ks[(32 * c + n) * kKS + 16 * s + 8 * h]));
+      a = mfma32x32x16(kop, qb[s], a);
+    }
+    acc[c] = a;
+  }
+}
+
+// Loads this lane's query operand: row n = l%32 of the wave (token n/G, head
+// g*G + n%G), dims 16s + 8h .. +8 for s = 0..7.
+template <int G>
+__device__ __forceinline__ void load_q(const uint16_t* q, int b, int n_q, int Hq, int g, int tok, bf16x8* qb) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, n = lane & 31;
+  const bool ok = tok < n_q;
+  const int head = g * G + (n % G);
+  const uint16_t* qp = q + (((int64_t)b * n_q + (ok ? tok : 0)) * Hq + head) * kHeadDim + 8 * h;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(ok ? ld16(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u});
+}
+
+// Writes the group-max scores of the wave's tile into sig[TPW][64] (raw,
+// unscaled). Lanes with n%G == 0 hold each token's maxima.
+template <int G>
+__device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, n = lane & 31;
+  float mx[2][16];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx[c][i] = group_max<G>(acc[c][i]);
+  if (n % G == 0) {
+    float* row = sig + (n / G) * 64;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v = {mx[c][4 * q4], mx[c][4 * q4 + 1], mx[c][4 * q4 + 2], mx[c][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(row + 32 * c + 8 * q4 + 4 * h) = v;
+      }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
+  constexpr int TPW = 32 / G;
+  constexpr int TPB = 4 * TPW;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[128 * kVS];
+  __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, n = lane & 31;
+  const int ntq = (P.n_q + TPB - 1) / TPB;
+  int L = blockIdx.x;
+  const int g = L % P.Hkv;
+  L /= P.Hkv;
+  const int b = L % P.B;
+  L /= P.B;
+  const int t0 = (ntq - 1 - L) * TPB;
+  const int off = P.n_kv - P.n_q;
+
+  const int wt0 = t0 + wave * TPW;
+  const int tok = wt0 + n / G;
+  const bool tok_ok = tok < P.n_q;
+  const int head = g * G + (n % G);
+  const int p_lane = tok_ok ? off + tok : -1;
+  const int p_wlo = off + wt0;
+  const int p_whi = off + imin(wt0 + TPW, P.n_q) - 1;
+  const bool wave_live = wt0 < P.n_q;
+
+  bf16x8 qb[8];
+  load_q<G>(P.q, b, P.n_q, P.Hq, g, tok, qb);
+
+  float theta[TPW];
+  int cnt[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tk = wt0 + u;
+    theta[u] = (P.select && tk < P.n_q) ? P.theta[((int64_t)b * P.n_q + tk) * P.Hkv + g] : kNegInf;
+    cnt[u] = 0;
+  }
+
+  f32x16 oacc[4] = {};
+  float m_run = kNegInf, l_run = 0.f;
+  const float cexp = P.scale * kLog2e;
+
+  const int p_bhi = off + imin(t0 + TPB, P.n_q) - 1;
+  const int ntiles = p_bhi / 64 + 1;
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int key0 = kt * 64;
+    load_kv_tile(P.kv, b, g, key0, P.n_kv, Ks, Vt, true);
+    __syncthreads();
+    if (wave_live && key0 <= p_whi) {
+      f32x16 acc[2];
+      qk_tile(Ks, qb, acc);
+      if (key0 + 63 > p_wlo) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = key0 + 32 * c + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (j > p_lane) acc[c][i] = kNegInf;
+          }
+      }
+      if (P.select && key0 <= p_whi - P.window) {
+        float* ws = sig[wave];
+        stage_group_max<G>(acc, ws);
+        lds_wait();
+        const int j = key0 + lane;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int tk = wt0 + u;
+          const float v = ws[u * 64 + lane] * P.scale;
+          const bool pass = tk < P.n_q && j <= off + tk - P.window && v >= theta[u];
+          const uint64_t m = ballot(pass);
+          if (m) {
+            const int pos = cnt[u] + (int)lane_prefix(m);
+            if (pass && pos < P.cap) {
+              const int64_t row = ((int64_t)b * P.n_q + tk) * P.Hkv + g;
+              P.buf_sigma[row * P.cap + pos] = v;
+              P.buf_j[row * P.cap + pos] = j;
+            }
+            cnt[u] += __popcll(m);
+          }
+        }
+      }
+      // online softmax (exp2 domain)
+      float mx = kNegInf;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[c][i]);
+      mx = xor32_max(mx);
+      const float m_new = fmaxf(m_run, mx * cexp);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(acc[c][i], cexp, -m_use));
+          acc[c][i] = pv;
+          psum += pv;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[bk][i] *= alpha;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = s >> 1, base = 8 * (s & 1);
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[c][base + 2 * e], acc[c][base + 2 * e + 1]);
+        pb[s] = as_bf16x8(w);
+      }
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk) {
+        const uint16_t* vrow = &Vt[(32 * bk + n) * kVS];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int kb = 32 * (s >> 1) + 16 * (s & 1) + 4 * h;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
+          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s], oacc[bk]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  const float l_tot = xor32_sum(l_run);
+  if (tok_ok) {
+    const float inv = 1.f / l_tot;
+    uint16_t* op = P.o + (((int64_t)b * P.n_q + tok) * P.Hq + head) * kHeadDim;
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[bk][4 * q4] * inv, oacc[bk][4 * q4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[bk][4 * q4 + 2] * inv, oacc[bk][4 * q4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + 32 * bk + 8 * q4 + 4 * h) = w;
+      }
+    if (P.lse && h == 0) P.lse[((int64_t)b * P.Hq + head) * P.n_q + tok] = m_run * kLn2 + __logf(l_tot);
+  }
+  if (P.select && lane == 0) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tk = wt0 + u;
+      if (tk < P.n_q) P.counts[((int64_t)b * P.n_q + tk) * P.Hkv + g] = cnt[u];
+    }
+  }
+}
+
+// Scores of sampled keys j = s*stride (s = 0..nsamp(p)-1, nsamp(p) =
+// ceil(|C(p)|/stride)) for every (b, t, g) row, computed with the same MFMA
+// sequence as the attention kernel, into samples[row][s].
+template <int G>
+__global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
+  constexpr int TPW = 32 / G;
+  constexpr int TPB = 4 * TPW;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKS];
+  __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31;
+  const int ntq = (P.n_q + TPB - 1) / TPB;
+  int L = blockIdx.x;
+  const int g = L % P.Hkv;
+  L /= P.Hkv;
+  const int b = L % P.B;
+  L /= P.B;
+  const int t0 = (ntq - 1 - L) * TPB;
+  const int off = P.n_kv - P.n_q;
+  const int wt0 = t0 + wave * TPW;
+  const int tok = wt0 + n / G;
+
+  bf16x8 qb[8];
+  load_q<G>(P.q, b, P.n_q, P.Hq, g, tok, qb);
+
+  const int p_bhi = off + imin(t0 + TPB, P.n_q) - 1;
+  const int ncand_hi = imax(0, p_bhi - P.window + 1);
+  const int ns_hi = (ncand_hi + P.stride - 1) / P.stride;
+  const int ntiles = (ns_hi + 63) / 64;
+  const int wlast = imin(wt0 + TPW, P.n_q) - 1;
+  const int ns_whi = wt0 < P.n_q ? (imax(0, off + wlast - P.window + 1) + P.stride - 1) / P.stride : 0;
+
+  const int dq = tid & 15, kq = tid >> 4;
+  for (int st = 0; st < ntiles; ++st) {
+    const int s0 = st * 64;
+    {
+      u32x4 kw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = s0 + 4 * kq + r;
+        kw[r] = s < ns_hi ? ld16(P.kv.k_row(b, g, s * P.stride) + 8 * dq) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st16(&Ks[(4 * kq + r) * kKS + 8 * dq], kw[r]);
+    }
+    __syncthreads();
+    if (s0 < ns_whi) {
+      f32x16 acc[2];
+      qk_tile(Ks, qb, acc);
+      float* ws = sig[wave];
+      stage_group_max<G>(acc, ws);
+      lds_wait();
+      const int s = s0 + lane;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int tk = wt0 + u;
+        if (tk >= P.n_q) continue;
+        const int ncand = imax(0, off + tk - P.window + 1);
+        const int ns = (ncand + P.stride - 1) / P.stride;
+        if (s < ns) {
+          const int64_t row = ((int64_t)b * P.n_q + tk) * P.Hkv + g;
+          P.samples[row * P.max_samples + s] = ws[u * 64 + lane] * P.scale;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int G>
+hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t s) {
+  constexpr int TPB = 4 * (32 / G);
+  const int64_t blocks = (int64_t)((p.n_q + TPB - 1) / TPB) * p.B * p.Hkv;
+  prefill_attn_kernel<G><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_sample_g(const SampleParams& p, hipStream_t s) {
+  constexpr int TPB = 4 * (32 / G);
+  const int64_t blocks = (int64_t)((p.n_q + TPB - 1) / TPB) * p.B * p.Hkv;
+  sample_scores_kernel<G><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_prefill_g<1>(p, s);
+    case 2: return launch_prefill_g<2>(p, s);
+    case 4: return launch_prefill_g<4>(p, s);
+    case 8: return launch_prefill_g<8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_sample_scores(const SampleParams& p, hipStream_t s) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_sample_g<1>(p, s);
+    case 2: return launch_sample_g<2>(p, s);
+    case 4: return launch_sample_g<4>(p, s);
+    case 8: return launch_sample_g<8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hs
