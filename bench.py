@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid sparse attention hot path on one MI355X.
+
+One step = one pass of the prefill hot path over the prefill32k workload
+(B=1, 32768 tokens, 32 query / 4 KV heads, d=128, top-k 2048, window 512,
+64 needles): the full-attention layer with token selection, then three
+sparse layers that reuse its KV cache and indices. Inputs are resident in HBM
+before timing starts. `value` is prefill tokens/s of that block.
+
+Beside it: the batched decode workload (64 sequences, contexts drawn from
+[65536, 262144], 32 steps of append + full attention + select once + three
+sparse layers), reported as microseconds per step, and the CPU oracle timed
+on a bounded sample of prefill rows.
+
+Per-kernel durations come from the library's HIP-event timing on the stream
+the kernels run on; the roofline object describes the kernel that takes the
+most time in the step. Prints ONE JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_counts(w):
+    """Algorithmic work of one prefill block (formulas in the design notes)."""
+    d, G = 128, w.Hq // w.Hkv
+    off = w.n_kv - w.n_q
+    pairs = 0
+    s_sum = 0          # sum over rows of |S| = min(k, |C(p)|) + |Win(p)|
+    for t in range(w.n_q):
+        p = off + t
+        pairs += p + 1
+        c = max(0, p - w.window + 1)
+        s_sum += min(w.top_k, c) + min(w.window, p + 1)
+    full_flops = 4.0 * d * w.Hq * pairs * w.B
+    sparse_flops = 4.0 * d * w.Hq * s_sum * w.B
+    gather_bytes = 512.0 * w.Hkv * s_sum * w.B
+    qo_bytes = 2 * w.B * w.n_q * w.Hq * d * 2.0
+    idx_bytes = 4.0 * w.B * w.n_q * w.Hkv * w.top_k
+    return {"full_flops": full_flops, "sparse_flops_per_layer": sparse_flops,
+            "sparse_bytes_per_layer": gather_bytes + qo_bytes + idx_bytes}
+
+
+def run_prefill(args, hs, synth, _lib, torch):
+    w = synth.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    log(f"[bench] generating {w.name} inputs")
+    case = synth.make_prefill_case(w, dev)
+    q, kv, qs = case["q_full"], case["kv"], case["q_sparse"]
+    shape = hs.make_shape(batch=w.B, n_q=w.n_q, n_kv=w.n_kv, kv_capacity=kv.shape[2], q_heads=w.Hq,
+                          kv_heads=w.Hkv, top_k=w.top_k, window=w.window)
+    ws = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), dev)
+
+    def step():
+        o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, workspace=ws)
+        outs = [hs.sparse_attn_reuse(x, kv, idx, top_k=w.top_k, window=w.window, n_kv=w.n_kv) for x in qs]
+        return o, idx, outs
+
+    for i in range(args.warmup):
+        step()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    _lib.timing_read()
+    _lib.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.timing_enable(False)
+    kt = _lib.timing_read()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step")
+    for k, (n, tot) in sorted(kt.items(), key=lambda x: -x[1][1]):
+        log(f"[bench]   {k:16s} launches={n:5d} avg={tot / n * 1e3:10.1f} us  share/step={tot / args.steps:8.3f} ms")
+    return w, ms_per_step, kt, case
+
+
+def run_decode(args, hs, synth, _lib, torch):
+    w = synth.WORKLOADS["decode64"]
+    dev = "cuda:0"
+    lengths = synth.decode_lengths(w)
+    steps = args.decode_steps
+    log(f"[bench] generating decode64 cache (sum of lengths {sum(lengths)})")
+    case = synth.make_decode_case(w, dev, lengths, steps)
+    kv = case["kv"]
+    cap = case["cap"]
+    shape = hs.make_shape(batch=w.B, n_q=1, n_kv=0, kv_capacity=cap, q_heads=w.Hq, kv_heads=w.Hkv,
+                          top_k=w.top_k, window=w.window)
+    ws_full = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
+    ws_sp = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, shape, 1), dev)
+    seqs = [torch.tensor([L + s + 1 for L in lengths], dtype=torch.int32, device=dev) for s in range(steps)]
+    torch.cuda.synchronize()
+    _lib.timing_read()
+    _lib.timing_enable(True)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        st = case["steps"][s]
+        o, lse, idx = hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[s], max(lengths) + s + 1,
+                                     top_k=w.top_k, window=w.window, workspace=ws_full)
+        for x in st["q_sparse"]:
+            hs.sparse_attn_reuse(x, kv, idx, top_k=w.top_k, window=w.window, seq_lens=seqs[s], workspace=ws_sp)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.timing_enable(False)
+    kt = _lib.timing_read()
+    us_step = (t1 - t0) * 1e6 / steps
+    log(f"[bench] decode64: {us_step:.1f} us/step")
+    for k, (n, tot) in sorted(kt.items(), key=lambda x: -x[1][1]):
+        log(f"[bench]   {k:16s} launches={n:5d} avg={tot / n * 1e3:10.1f} us")
+    # algorithmic bytes
+    full_bytes = sum(512.0 * w.Hkv * (L + s + 1) for L in lengths for s in range(steps)) / steps
+    sp_rows = sum(min(w.top_k, max(0, L + s + 1 - w.window)) + min(w.window, L + s + 1)
+                  for L in lengths for s in range(steps)) / steps
+    sp_bytes = 512.0 * w.Hkv * sp_rows + 4.0 * w.B * w.Hkv * w.top_k + 2 * 2.0 * w.B * w.Hq * 128
+    n_sp, t_sp = kt.get("sparse_decode", (0, 0.0))
+    n_cb, t_cb = kt.get("lse_combine", (0, 0.0))
+    n_df, t_df = kt.get("decode_full", (0, 0.0))
+    sp_us = t_sp / max(1, n_sp) * 1e3
+    df_us = t_df / max(1, n_df) * 1e3
+    dec = {
+        "workload": "decode64", "batch": w.B, "context": [w.ctx_lo, w.ctx_hi], "steps": steps,
+        "us_per_step": round(us_step, 2),
+        "sparse_layer_kernel_us": round(sp_us, 2),
+        "sparse_decode_roofline": {"bound": "hbm", "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(sp_bytes / (sp_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "bytes_per_launch": sp_bytes},
+        "decode_full_roofline": {"bound": "hbm", "achieved": round(full_bytes / (df_us * 1e-6) / 1e9, 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(full_bytes / (df_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                 "bytes_per_launch": full_bytes},
+    }
+    del case, kv
+    torch.cuda.empty_cache()
+    return dec
+
+
+def cpu_baseline(args, w, case, torch):
+    """The oracle on a bounded sample of prefill rows of the same workload
+    (the very inputs the GPU step used, copied to the host)."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    K = case["kv"][0, :, :w.n_kv, 0].float().numpy()
+    V = case["kv"][0, :, :w.n_kv, 1].float().numpy()
+    qf = case["q_full"][0].float().numpy()
+    qs = [x[0].float().numpy() for x in case["q_sparse"]]
+    scale = orc.default_scale(128)
+    pos_all = orc.query_positions(w.n_q, w.n_kv)
+
+    def rows_time(rows):
+        t0 = time.perf_counter()
+        pos = pos_all[rows]
+        res = orc.full_attn_select_rows(qf[rows], K, V, pos, w.top_k, w.window, scale)
+        for x in qs:
+            orc.sparse_attention_rows(x[rows], K, V, res["idx"], pos, w.window, scale)
+        return time.perf_counter() - t0
+
+    # rows spread evenly over the chunk so the mean context matches the workload
+    probe = [w.n_q // 2]
+    t_one = rows_time(probe)
+    R = int(max(4, min(256, args.cpu_seconds / max(t_one, 1e-3))))
+    rows = sorted(set(int(x) for x in np.linspace(0, w.n_q - 1, R)))
+    t = rows_time(rows)
+    return {"value": round(len(rows) / t, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} query rows evenly spaced over the {w.n_q}-row {w.name} chunk "
+                      f"(full layer + selection + {len(qs)} sparse layers), {t:.1f} s of CPU time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill32k")
+    ap.add_argument("--decode-steps", type=int, default=32)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the hot path is single-GPU by design); --gpus {args.gpus} "
+              f"is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import token_level_sparse_hs_amd as hs
+    from token_level_sparse_hs_amd import _lib, synth
+    _lib.load()
+
+    w, ms_step, kt, case = run_prefill(args, hs, synth, _lib, torch)
+    counts = prefill_counts(w)
+    tokens = w.B * w.n_q
+    value = tokens / (ms_step * 1e-3)
+
+    dom = max(kt.items(), key=lambda x: x[1][1])[0]
+    n_pa, t_pa = kt["prefill_attn"]
+    pa_us = t_pa / n_pa * 1e3
+    if dom == "prefill_attn":
+        achieved = counts["full_flops"] / (pa_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "prefill_attn",
+                "flops_per_launch": counts["full_flops"], "avg_us": round(pa_us, 1)}
+    else:
+        n_d, t_d = kt[dom]
+        us = t_d / n_d * 1e3
+        byts = counts["sparse_bytes_per_layer"]
+        achieved = byts / (us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "bytes_per_launch": byts, "avg_us": round(us, 1)}
+    kernels = {k: {"launches_per_step": n / args.steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()}
+    n_sp, t_sp = kt.get("sparse_prefill", (0, 0.0))
+    sp_us = t_sp / max(1, n_sp) * 1e3
+    sparse_prefill = {"avg_us": round(sp_us, 1),
+                      "gather_GBs": round(counts["sparse_bytes_per_layer"] / (sp_us * 1e-6) / 1e9, 1) if sp_us else None,
+                      "tflops": round(counts["sparse_flops_per_layer"] / (sp_us * 1e-6) / 1e12, 2) if sp_us else None}
+    full_layer_ms = sum(tot for k, (n, tot) in kt.items() if k != "sparse_prefill") / args.steps
+
+    case_host = None
+    if not args.no_cpu_baseline:
+        case_host = {"kv": case["kv"].cpu(), "q_full": case["q_full"].cpu(), "q_sparse": [x.cpu() for x in case["q_sparse"]]}
+    del case
+    torch.cuda.empty_cache()
+
+    decode = None
+    if not args.no_decode:
+        decode = run_decode(args, hs, synth, _lib, torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a row sample")
+        cpu = cpu_baseline(args, w, case_host, torch)
+        log(f"[bench] oracle: {cpu}")
+
+    line = {
+        "metric": "prefill tokens/s + decode us/step (sparse attn); % MFMA / HBM roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "n_q": w.n_q, "n_kv": w.n_kv, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": 128, "top_k": w.top_k, "window": w.window,
+                   "sparse_layers": w.sparse_layers, "needles": w.needles, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "full_layer_ms": round(full_layer_ms, 3),
+        "sparse_prefill_layer": sparse_prefill,
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

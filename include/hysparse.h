@@ -171,6 +171,23 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new,
                          int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Diagnostics: per-kernel timing. While enabled (on != 0), every kernel the
+ * library launches is bracketed by a pair of HIP events recorded on the
+ * call's stream, so durations are those of the kernels themselves on the
+ * stream they run on. Accumulates per kernel name until read. Process-wide;
+ * enabling costs two event records per launch. */
+typedef struct {
+  char name[48];     /* kernel name, e.g. "prefill_attn"                     */
+  int64_t launches;  /* launches timed since the last read                   */
+  double total_ms;   /* summed durations                                     */
+} hs_kernel_time;
+
+hs_status hs_timing_enable(int32_t on);
+
+/* Waits for every recorded event, writes up to `max` entries to `out`,
+ * sets *count to the number of distinct kernels, and clears the totals. */
+hs_status hs_timing_read(hs_kernel_time* out, int32_t max, int32_t* count);
+
 /* Static English name of a status code. */
 const char* hs_status_string(hs_status st);
 

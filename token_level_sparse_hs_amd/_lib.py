@@ -21,7 +21,7 @@ HS_OP_FULL_ATTN_SELECT, HS_OP_SPARSE_ATTN_REUSE, HS_OP_DECODE_STEP = range(3)
 HS_FLAG_EXACT_RESCAN = 1
 
 EXPORTED = ("hs_workspace_size", "hs_full_attn_select", "hs_sparse_attn_reuse", "hs_decode_step",
-            "hs_status_string", "hs_last_error", "hs_version")
+            "hs_timing_enable", "hs_timing_read", "hs_status_string", "hs_last_error", "hs_version")
 
 
 class HsShape(ctypes.Structure):
@@ -32,6 +32,10 @@ class HsShape(ctypes.Structure):
         ("kv_stride_b", c_int64), ("kv_stride_h", c_int64), ("kv_stride_t", c_int64), ("kv_v_offset", c_int64),
         ("flags", c_uint32), ("reserved", c_uint32),
     ]
+
+
+class HsKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", c_int64), ("total_ms", ctypes.c_double)]
 
 
 class HsError(RuntimeError):
@@ -68,6 +72,10 @@ def load() -> ctypes.CDLL:
     lib.hs_last_error.restype = ctypes.c_char_p
     lib.hs_version.argtypes = []
     lib.hs_version.restype = c_int32
+    lib.hs_timing_enable.argtypes = [c_int32]
+    lib.hs_timing_enable.restype = c_int32
+    lib.hs_timing_read.argtypes = [POINTER(HsKernelTime), c_int32, POINTER(c_int32)]
+    lib.hs_timing_read.restype = c_int32
     _lib = lib
     return lib
 
@@ -98,3 +106,15 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor | None:
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + nbytes]
+
+
+def timing_enable(on: bool) -> None:
+    check(load().hs_timing_enable(1 if on else 0))
+
+
+def timing_read() -> dict:
+    """{kernel name: (launches, total_ms)} since the last read (waits for the events)."""
+    arr = (HsKernelTime * 64)()
+    n = c_int32(0)
+    check(load().hs_timing_read(arr, 64, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(min(n.value, 64))}

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -186,6 +187,57 @@ DecodePlan plan_decode_sparse(const hs_shape* s) {
   return p;
 }
 
+// ------------------------------------------------------------ timing
+
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  struct Rec {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  std::map<std::string, std::pair<int64_t, double>> acc;
+};
+TimingState g_timing;
+
+hipEvent_t take_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (which enqueues one kernel on stream s); with timing on, the
+// kernel is bracketed by two events on the same stream.
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    on = g_timing.on;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    a = take_event();
+    b = take_event();
+  }
+  if (!a || !b) return launch();
+  hipEventRecord(a, s);
+  hipError_t e = launch();
+  hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.pending.push_back({name, a, b});
+  return e;
+}
+
 #define HIP_TRY(expr)                                                                     \
   do {                                                                                    \
     hipError_t e_ = (expr);                                                               \
@@ -209,6 +261,40 @@ const char* hs_status_string(hs_status st) {
 }
 
 const char* hs_last_error(void) { return g_last_error.c_str(); }
+
+hs_status hs_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  return ok();
+}
+
+hs_status hs_timing_read(hs_kernel_time* out, int32_t max, int32_t* count) {
+  if (!count || (max > 0 && !out)) return fail(HS_ERR_INVALID_ARG, "out/count is NULL");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& r : g_timing.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      return fail(HS_ERR_HIP, "timing event failed for %s", r.name);
+    auto& a = g_timing.acc[r.name];
+    a.first += 1;
+    a.second += ms;
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.pending.clear();
+  int32_t n = 0;
+  for (auto& kv : g_timing.acc) {
+    if (n < max) {
+      std::snprintf(out[n].name, sizeof out[n].name, "%s", kv.first.c_str());
+      out[n].launches = kv.second.first;
+      out[n].total_ms = kv.second.second;
+    }
+    ++n;
+  }
+  *count = n;
+  g_timing.acc.clear();
+  return ok();
+}
 
 int32_t hs_version(void) { return HS_VERSION; }
 
@@ -268,14 +354,14 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
       sp.B = s->batch; sp.n_q = s->n_q; sp.n_kv = s->n_kv; sp.Hq = s->q_heads; sp.Hkv = s->kv_heads;
       sp.window = s->window; sp.scale = scale; sp.stride = plan.stride; sp.max_samples = plan.max_samples;
       sp.samples = reinterpret_cast<float*>(w + plan.off_samples);
-      HIP_TRY(hs::launch_sample_scores(sp, hst));
+      HIP_TRY(timed("sample_scores", hst, [&] { return hs::launch_sample_scores(sp, hst); }));
     }
     hs::ThresholdParams tp{};
     tp.B = s->batch; tp.n_q = s->n_q; tp.n_kv = s->n_kv; tp.Hkv = s->kv_heads; tp.top_k = s->top_k;
     tp.window = s->window; tp.cap = plan.cap; tp.stride = plan.stride; tp.max_samples = plan.max_samples;
     tp.samples = reinterpret_cast<const float*>(w + plan.off_samples);
     tp.theta = theta;
-    HIP_TRY(hs::launch_threshold(tp, plan.rows, hst));
+    HIP_TRY(timed("threshold", hst, [&] { return hs::launch_threshold(tp, plan.rows, hst); }));
   }
 
   hs::PrefillParams pp{};
@@ -291,7 +377,7 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
   pp.buf_j = select ? reinterpret_cast<int32_t*>(w + plan.off_bj) : nullptr;
   pp.counts = select ? reinterpret_cast<int32_t*>(w + plan.off_counts) : nullptr;
   pp.cap = plan.cap;
-  HIP_TRY(hs::launch_prefill_attn(pp, hst));
+  HIP_TRY(timed("prefill_attn", hst, [&] { return hs::launch_prefill_attn(pp, hst); }));
 
   if (select) {
     hs::SelectParams sp{};
@@ -303,7 +389,7 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
     sp.force_rescan = (s->flags & HS_FLAG_EXACT_RESCAN) ? 1 : 0;
     sp.idx = idx;
     sp.rescan_count = nullptr;
-    HIP_TRY(hs::launch_select_prefill(sp, plan.rows, hst));
+    HIP_TRY(timed("select_prefill", hst, [&] { return hs::launch_select_prefill(sp, plan.rows, hst); }));
   }
   return ok();
 }
@@ -351,13 +437,13 @@ hs_status hs_sparse_attn_reuse(const hs_shape* s, const void* q, const void* kv,
     dp.splits = 1;
     dp.split_len = s->top_k + s->window + 32;
   }
-  HIP_TRY(hs::launch_sparse(dp, hst));
+  HIP_TRY(timed(decode ? "sparse_decode" : "sparse_prefill", hst, [&] { return hs::launch_sparse(dp, hst); }));
   if (decode && plan.splits > 1) {
     hs::CombineParams cp{};
     cp.part = dp.part; cp.o = dp.o; cp.lse = nullptr; cp.seq_lens = seq_lens;
     cp.B = s->batch; cp.Hq = s->q_heads; cp.Hkv = s->kv_heads; cp.splits = plan.splits; cp.split_len = plan.split_len;
     cp.sparse_k = s->top_k; cp.window = s->window; cp.max_len = s->kv_capacity;
-    HIP_TRY(hs::launch_combine(cp, hst));
+    HIP_TRY(timed("lse_combine", hst, [&] { return hs::launch_combine(cp, hst); }));
   }
   return ok();
 }
@@ -388,7 +474,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   ap.kv = static_cast<uint16_t*>(kv);
   ap.sb = lay.sb; ap.sh = lay.sh; ap.st = lay.st; ap.voff = lay.voff;
   ap.seq_lens = seq_lens; ap.B = s->batch; ap.Hkv = s->kv_heads; ap.cap = max_seq_len;
-  HIP_TRY(hs::launch_append(ap, hst));
+  HIP_TRY(timed("kv_append", hst, [&] { return hs::launch_append(ap, hst); }));
 
   hs::DecodeParams dp{};
   dp.q = static_cast<const uint16_t*>(q);
@@ -402,19 +488,19 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   dp.part = reinterpret_cast<float*>(w + plan.off_part);
   dp.sigma = s->top_k > 0 ? reinterpret_cast<float*>(w + plan.off_sigma) : nullptr;
   dp.sigma_stride = plan.sigma_stride;
-  HIP_TRY(hs::launch_decode_full(dp, hst));
+  HIP_TRY(timed("decode_full", hst, [&] { return hs::launch_decode_full(dp, hst); }));
   if (plan.splits > 1) {
     hs::CombineParams cp{};
     cp.part = dp.part; cp.o = dp.o; cp.lse = lse; cp.seq_lens = seq_lens;
     cp.B = s->batch; cp.Hq = s->q_heads; cp.Hkv = s->kv_heads; cp.splits = plan.splits; cp.split_len = plan.split_len;
     cp.sparse_k = -1; cp.window = s->window; cp.max_len = max_seq_len;
-    HIP_TRY(hs::launch_combine(cp, hst));
+    HIP_TRY(timed("lse_combine", hst, [&] { return hs::launch_combine(cp, hst); }));
   }
   if (s->top_k > 0) {
     hs::SelectDecodeParams sp{};
     sp.B = s->batch; sp.Hkv = s->kv_heads; sp.top_k = s->top_k; sp.window = s->window;
     sp.seq_lens = seq_lens; sp.sigma = dp.sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = idx;
-    HIP_TRY(hs::launch_select_decode(sp, s->batch * s->kv_heads, hst));
+    HIP_TRY(timed("select_decode", hst, [&] { return hs::launch_select_decode(sp, s->batch * s->kv_heads, hst); }));
   }
   return ok();
 }
