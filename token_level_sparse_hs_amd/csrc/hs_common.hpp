@@ -8,6 +8,7 @@
 //   v_mfma_f32_16x16x32_bf16  A: m = l%16, k = 8*(l/16)+e;  B: n = l%16,
 //                             k = 8*(l/16)+e;  C: reg i -> m = 4*(l/16)+i,
 //                             n = l%16
+//   v_mfma_f32_16x16x16_bf16  as 16x16x32 with k = 4*(l/16)+e, e = 0..3
 // (e = 0..7 indexes the eight bf16 of an operand register quad.)
 #pragma once
 
@@ -21,6 +22,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -53,6 +55,12 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x16_bf16: A: m = l%16, k = 4*(l/16)+e; B: n = l%16,
+// k = 4*(l/16)+e (e = 0..3); C as for 16x16x32.
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                    0, 0, 0);
 }
 
 // ---------------------------------------------------------------- cross-lane

@@ -33,7 +33,7 @@ namespace hs {
 
 namespace {
 
-constexpr int kVtS = 36;  // per-wave V^T tile row stride in bf16 (72 B)
+constexpr int kVtS = 20;  // per-wave V^T tile row stride in bf16 (16 keys + pad, 40 B)
 
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -60,12 +60,25 @@ struct KeyList {
   }
 };
 
+constexpr int kSeg = 256;  // resolved key-list entries staged per wave
+
+// One 16-key chunk in flight: K rows as MFMA A operands (lane: key l%16, dims
+// 32s + 8(l/16)..+8) and V rows for the LDS transpose (lane: keys
+// 4(l/16)..+3, dims 8(l%16)..+7), plus the validity mask of its 16 keys.
+struct Chunk {
+  bf16x8 ka[4];
+  u32x4 vw[4];
+  uint32_t vmask;
+};
+
 template <int G, bool SPARSE>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t Vt_all[4][128 * kVtS];
+  __shared__ __attribute__((aligned(16))) int32_t klist_all[4][SPARSE ? kSeg : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, gq = lane >> 4;
   uint16_t* Vt = Vt_all[wave];
+  int32_t* klist = klist_all[wave];
 
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
   const bool decode = P.seq_lens != nullptr;
@@ -129,113 +142,110 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   float* sig_row = nullptr;
   if (!SPARSE && P.sigma) sig_row = P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride;
 
-  for (int v0 = vbeg; v0 < vend; v0 += 32) {
-    // --- gather K rows (A operands): tile c row r = n + 16c
-    bf16x8 ka[2][4];
-    bool rv[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int j = kl.key(v0 + n + 16 * c);
-      rv[c] = j >= 0;
-      const uint16_t* kr = P.kv.k_row(b, g, j >= 0 ? j : 0) + 8 * gq;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ka[c][s] = as_bf16x8(rv[c] ? ld16(kr + 32 * s) : u32x4{0u, 0u, 0u, 0u});
-    }
-    // --- gather V rows: key groups kg = gq and gq+4 (4 keys each), dims 8n..8n+7
-    u32x4 vw[2][4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = kl.key(v0 + 4 * (gq + 4 * hh) + r);
-        vw[hh][r] = j >= 0 ? ld16(P.kv.v_row(b, g, j) + 8 * n) : u32x4{0u, 0u, 0u, 0u};
-      }
-    const uint64_t m0 = ballot(rv[0]), m1 = ballot(rv[1]);
-    const uint32_t vmask = (uint32_t)(m0 & 0xffffu) | ((uint32_t)(m1 & 0xffffu) << 16);
+  int seg0 = vbeg - kSeg;  // SPARSE: virtual start of the staged key-list segment
 
-    // --- S^T tiles
-    f32x4 acc[2];
+  // Issues the gathers of the chunk starting at virtual key v0.
+  auto load = [&](Chunk& ch, int v0) {
+    if constexpr (SPARSE) {
+      if (v0 + 16 > seg0 + kSeg) {
+        seg0 = v0;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f32x4 a = {};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a = mfma16x16x32(ka[c][s], qb[s], a);
-      acc[c] = a;
+        for (int i = 0; i < kSeg / 64; ++i) klist[lane + 64 * i] = kl.key(seg0 + lane + 64 * i);
+        lds_wait();
+      }
     }
-    // lane holds query column n, chunk keys 16c + 4*gq + i
+    auto key = [&](int v) -> int {
+      if constexpr (SPARSE) return klist[v - seg0];
+      else return v < vend ? v : -1;
+    };
+    const int jk = key(v0 + n);
+    const bool rv = jk >= 0;
+    const uint16_t* kr = P.kv.k_row(b, g, rv ? jk : 0) + 8 * gq;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int s = 0; s < 4; ++s) ch.ka[s] = as_bf16x8(rv ? ld16(kr + 32 * s) : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = key(v0 + 4 * gq + r);
+      ch.vw[r] = j >= 0 ? ld16(P.kv.v_row(b, g, j) + 8 * n) : u32x4{0u, 0u, 0u, 0u};
+    }
+    ch.vmask = (uint32_t)(ballot(rv) & 0xffffu);
+  };
+
+  // Attention update with the chunk starting at virtual key v0.
+  auto compute = [&](const Chunk& ch, int v0) {
+    f32x4 acc = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma16x16x32(ch.ka[s], qb[s], acc);
+    // lane holds query column n, chunk keys 4*gq + i
+    if (ch.vmask != 0xffffu) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (!((vmask >> (16 * c + 4 * gq + i)) & 1u)) acc[c][i] = kNegInf;
-
+        if (!((ch.vmask >> (4 * gq + i)) & 1u)) acc[i] = kNegInf;
+    }
     if (!SPARSE && sig_row && v0 <= cand_end) {
+      f32x4 mxh;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
+      const int j = v0 + 4 * gq;
+      if (n == 0) {
+        if (j + 3 <= cand_end && ((j & 3) == 0)) {
+          *reinterpret_cast<f32x4*>(sig_row + j) = mxh;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float mxh = group_max<G>(acc[c][i]);
-          const int j = v0 + 16 * c + 4 * gq + i;
-          if (n == 0 && j <= cand_end) sig_row[j] = mxh * P.scale;
+          for (int i = 0; i < 4; ++i)
+            if (j + i <= cand_end) sig_row[j + i] = mxh[i];
         }
       }
     }
-
-    // --- V^T into LDS
+    // V^T into LDS: dims 8n+c, keys 4gq..4gq+3
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int kg = gq + 4 * hh;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int w = c >> 1;
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 tv;
-        tv[0] = __builtin_amdgcn_perm(vw[hh][1][w], vw[hh][0][w], sel);
-        tv[1] = __builtin_amdgcn_perm(vw[hh][3][w], vw[hh][2][w], sel);
-        *reinterpret_cast<u32x2*>(&Vt[(8 * n + c) * kVtS + 4 * kg]) = tv;
-      }
+    for (int c = 0; c < 8; ++c) {
+      const int w = c >> 1;
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 tv;
+      tv[0] = __builtin_amdgcn_perm(ch.vw[1][w], ch.vw[0][w], sel);
+      tv[1] = __builtin_amdgcn_perm(ch.vw[3][w], ch.vw[2][w], sel);
+      *reinterpret_cast<u32x2*>(&Vt[(8 * n + c) * kVtS + 4 * gq]) = tv;
     }
-
-    // --- online softmax
-    float mx = kNegInf;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[c][i]);
+    // online softmax
+    float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     mx = xor32_max(xor16_max(mx));
     const float m_new = fmaxf(m_run, mx * cexp);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float psum = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(acc[c][i], cexp, -m_use));
-        acc[c][i] = pv;
-        psum += pv;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(acc[i], cexp, -m_use));
+      acc[i] = pv;
+      psum += pv;
+    }
     l_part = l_part * alpha + psum;
     m_run = m_new;
 #pragma unroll
     for (int bk = 0; bk < 8; ++bk) oacc[bk] *= alpha;
-    u32x4 pw;
-    pw[0] = pack_bf16x2(acc[0][0], acc[0][1]);
-    pw[1] = pack_bf16x2(acc[0][2], acc[0][3]);
-    pw[2] = pack_bf16x2(acc[1][0], acc[1][1]);
-    pw[3] = pack_bf16x2(acc[1][2], acc[1][3]);
-    const bf16x8 pb = as_bf16x8(pw);
-
+    u32x2 pb;
+    pb[0] = pack_bf16x2(acc[0], acc[1]);
+    pb[1] = pack_bf16x2(acc[2], acc[3]);
     lds_wait();
 #pragma unroll
     for (int bk = 0; bk < 8; ++bk) {
-      const uint16_t* vr = &Vt[(16 * bk + n) * kVtS];
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 4 * gq);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 + 4 * gq);
-      const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-      oacc[bk] = mfma16x16x32(as_bf16x8(w), pb, oacc[bk]);
+      const u32x2 a = *reinterpret_cast<const u32x2*>(&Vt[(16 * bk + n) * kVtS + 4 * gq]);
+      oacc[bk] = mfma16x16x16(a, pb, oacc[bk]);
     }
-    lds_wait();
+  };
+
+  // Two chunks in flight: the next chunk's gathers are issued before the
+  // current chunk is consumed.
+  Chunk A, B;
+  load(A, vbeg);
+  for (int v0 = vbeg; v0 < vend; v0 += 32) {
+    const bool hasB = v0 + 16 < vend;
+    if (hasB) load(B, v0 + 16);
+    compute(A, v0);
+    if (!hasB) break;
+    if (v0 + 32 < vend) load(A, v0 + 32);
+    compute(B, v0 + 16);
   }
 
   const float l_tot = xor32_sum(xor16_sum(l_part));
