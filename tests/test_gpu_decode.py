@@ -77,3 +77,14 @@ def test_decode_exact_ties():
     o, lse, idx = hs.decode_step(q, kv_new, kv, seq_lens, L + 1, top_k=k, window=W)
     torch.cuda.synchronize()
     assert idx[0, 0].tolist() == [3, 9, 10, 30]
+
+
+def test_decode_long_rows_filtered_select():
+    """Rows longer than the register capacity take the sampled-threshold
+    filter inside the decode select."""
+    run_decode([20000, 70000], 2, 8, 1, 512, 64, seed=13, n_sparse=1)
+
+
+def test_decode_streaming_select():
+    """k close to the row length defeats the sample filter: streaming select."""
+    run_decode([9000], 1, 4, 1, 8000, 16, seed=14, n_sparse=1)

@@ -103,3 +103,17 @@ def test_threshold_path_long_rows():
     n = 6000
     rows = [0, 40, 41, 42, 100, 1000, 2047, 3000, 4500, 5998, 5999]
     run(1, n, n, 8, 2, 64, 32, seed=700, rows=rows)
+
+
+def test_large_k_buffer_path():
+    """Buffer capacity above the register capacity (large k)."""
+    n = 12000
+    rows = [0, 3063, 3064, 5000, 9000, 11999]
+    run(1, n, n, 8, 1, 3000, 64, seed=800, rows=rows)
+
+
+def test_rescan_streaming_long_rows():
+    """Exact rescan of rows longer than the register capacity."""
+    n = 9500
+    rows = [100, 8000, 9499]
+    run(1, n, n, 4, 1, 64, 16, seed=900, rows=rows, flags=hs.HS_FLAG_EXACT_RESCAN)
