@@ -60,7 +60,7 @@ struct KeyList {
   }
 };
 
-constexpr int kSeg = 256;  // resolved key-list entries staged per wave
+constexpr int kSeg = 2048;  // idx-row entries staged per wave (refilled only when k > kSeg)
 
 // One 16-key chunk in flight: K rows as MFMA A operands (lane: key l%16, dims
 // 32s + 8(l/16)..+8) and V rows for the LDS transpose (lane: keys
@@ -75,7 +75,8 @@ template <int G, bool SPARSE>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t Vt_all[4][128 * kVtS];
   __shared__ __attribute__((aligned(16))) int32_t klist_all[4][SPARSE ? kSeg : 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int n = lane & 15, gq = lane >> 4;
   uint16_t* Vt = Vt_all[wave];
   int32_t* klist = klist_all[wave];
@@ -142,31 +143,58 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   float* sig_row = nullptr;
   if (!SPARSE && P.sigma) sig_row = P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride;
 
-  int seg0 = vbeg - kSeg;  // SPARSE: virtual start of the staged key-list segment
+  // SPARSE: the idx row is staged in LDS, kSeg entries at a time; window
+  // tokens (virtual keys >= k) are computed.
+  int seg0 = -kSeg;
+  auto refill = [&](int base) {
+    seg0 = base;
+    const int cnt = imin(kSeg, kl.k - base);  // >= 1
+    const int32_t* src = kl.sel + base;
+    // All loads are issued before any is consumed (clamped, unconditional);
+    // entries beyond cnt are never looked up as selected tokens.
+    constexpr int kBatch = 8;
+#pragma unroll 1
+    for (int i0 = 0; i0 < cnt; i0 += 64 * kBatch) {
+      int32_t vals[kBatch];
+#pragma unroll
+      for (int it = 0; it < kBatch; ++it) vals[it] = src[imin(i0 + lane + 64 * it, cnt - 1)];
+#pragma unroll
+      for (int it = 0; it < kBatch; ++it) klist[imin(i0 + lane + 64 * it, kSeg - 1)] = vals[it];
+    }
+    lds_wait();
+  };
+  if constexpr (SPARSE) {
+    if (vbeg < kl.k) refill(vbeg - (vbeg % kSeg));
+  }
 
   // Issues the gathers of the chunk starting at virtual key v0.
   auto load = [&](Chunk& ch, int v0) {
     if constexpr (SPARSE) {
-      if (v0 + 16 > seg0 + kSeg) {
-        seg0 = v0;
-#pragma unroll
-        for (int i = 0; i < kSeg / 64; ++i) klist[lane + 64 * i] = kl.key(seg0 + lane + 64 * i);
-        lds_wait();
-      }
+      if (v0 < kl.k && v0 + 16 > seg0 + kSeg) refill(v0 - (v0 % kSeg));
     }
+    // Branch-free (selects only), so no gather ends up under an exec mask.
     auto key = [&](int v) -> int {
-      if constexpr (SPARSE) return klist[v - seg0];
-      else return v < vend ? v : -1;
+      int j = v;
+      if constexpr (SPARSE) {
+        const int vi = imin(imax(v - seg0, 0), kSeg - 1);
+        const int e = klist[vi];
+        const int js = (e >= 0 && e <= kl.lim) ? e : -1;
+        j = v < kl.k ? js : kl.w0 + (v - kl.k);
+      }
+      return v < vend ? j : -1;
     };
+    // Invalid slots read row 0 (always a valid row): their scores are masked
+    // to -inf, so their probabilities are exactly 0. Keeping every gather
+    // unconditional lets the compiler wait only for the chunk it consumes.
     const int jk = key(v0 + n);
     const bool rv = jk >= 0;
     const uint16_t* kr = P.kv.k_row(b, g, rv ? jk : 0) + 8 * gq;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ch.ka[s] = as_bf16x8(rv ? ld16(kr + 32 * s) : u32x4{0u, 0u, 0u, 0u});
+    for (int s = 0; s < 4; ++s) ch.ka[s] = as_bf16x8(ld16(kr + 32 * s));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = key(v0 + 4 * gq + r);
-      ch.vw[r] = j >= 0 ? ld16(P.kv.v_row(b, g, j) + 8 * n) : u32x4{0u, 0u, 0u, 0u};
+      ch.vw[r] = ld16(P.kv.v_row(b, g, j >= 0 ? j : 0) + 8 * n);
     }
     ch.vmask = (uint32_t)(ballot(rv) & 0xffffu);
   };
@@ -237,15 +265,22 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
 
   // Two chunks in flight: the next chunk's gathers are issued before the
   // current chunk is consumed.
+  // The next chunk is always issued (past the end its slots are invalid and
+  // read row 0), so every path carries the same loads in flight and the
+  // compiler waits only for the chunk being consumed.
+  // sched_barrier keeps each batch of gathers ahead of the previous chunk's
+  // math, so the waits before that math cover only the previous chunk.
   Chunk A, B;
   load(A, vbeg);
-  for (int v0 = vbeg; v0 < vend; v0 += 32) {
-    const bool hasB = v0 + 16 < vend;
-    if (hasB) load(B, v0 + 16);
+  for (int v0 = vbeg;; v0 += 32) {
+    load(B, v0 + 16);
+    __builtin_amdgcn_sched_barrier(0);
     compute(A, v0);
-    if (!hasB) break;
-    if (v0 + 32 < vend) load(A, v0 + 32);
+    if (v0 + 16 >= vend) break;
+    load(A, v0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
     compute(B, v0 + 16);
+    if (v0 + 32 >= vend) break;
   }
 
   const float l_tot = xor32_sum(xor16_sum(l_part));

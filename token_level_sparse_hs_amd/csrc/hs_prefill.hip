@@ -45,36 +45,43 @@ __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
-// Cooperative load of 64 key rows [key0, key0+64) of (b, g): K row-major into
-// Ks, V transposed into Vt. Rows at or beyond `valid_end` are zero-filled.
-// 256 threads; thread (kq = tid/16, dq = tid%16) moves rows 4kq..4kq+3,
-// dims 8dq..8dq+7.
-__device__ __forceinline__ void load_kv_tile(const KvView& kv, int b, int g, int key0, int valid_end,
-                                             uint16_t* Ks, uint16_t* Vt, bool with_v) {
+// Global -> register part of a 64-key tile [key0, key0+64) of (b, g): thread
+// (kq = tid/16, dq = tid%16) fetches rows 4kq..4kq+3, dims 8dq..8dq+7, of K
+// and (with_v) V. Rows at or beyond `valid_end` are clamped to the last valid
+// row (finite data; every such key is masked by causality), which keeps all
+// loads unconditional.
+struct TileRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+template <bool WITH_V>
+__device__ __forceinline__ void tile_fetch(const KvView& kv, int b, int g, int key0, int valid_end, TileRegs& r) {
   const int tid = threadIdx.x;
-  const int dq = tid & 15, kq = tid >> 4;
-  u32x4 kw[4], vw[4];
+  const int dq = tid & 15, kq = (tid >> 4) & 15;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int j = key0 + 4 * kq + r;
-    if (j < valid_end) {
-      kw[r] = ld16(kv.k_row(b, g, j) + 8 * dq);
-      if (with_v) vw[r] = ld16(kv.v_row(b, g, j) + 8 * dq);
-    } else {
-      kw[r] = u32x4{0u, 0u, 0u, 0u};
-      vw[r] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int j = imin(key0 + 4 * kq + i, valid_end - 1);
+    r.k[i] = ld16(kv.k_row(b, g, j) + 8 * dq);
+    if (WITH_V) r.v[i] = ld16(kv.v_row(b, g, j) + 8 * dq);
   }
+}
+
+// Register -> LDS part: K row-major into Ks, V transposed into Vt.
+template <bool WITH_V>
+__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* Ks, uint16_t* Vt) {
+  const int tid = threadIdx.x;
+  const int dq = tid & 15, kq = (tid >> 4) & 15;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) st16(&Ks[(4 * kq + r) * kKS + 8 * dq], kw[r]);
-  if (with_v) {
+  for (int i = 0; i < 4; ++i) st16(&Ks[(4 * kq + i) * kKS + 8 * dq], r.k[i]);
+  if (WITH_V) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int w = c >> 1;
       const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
       u32x2 t;
-      t[0] = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
-      t[1] = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
+      t[0] = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
+      t[1] = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
       *reinterpret_cast<u32x2*>(&Vt[(8 * dq + c) * kVS + 4 * kq]) = t;
     }
   }
@@ -137,11 +144,12 @@ template <int G>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   constexpr int TPW = 32 / G;
   constexpr int TPB = 4 * TPW;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[128 * kVS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][128 * kVS];
   __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
   const int ntq = (P.n_q + TPB - 1) / TPB;
   int L = blockIdx.x;
@@ -180,13 +188,21 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   const int p_bhi = off + imin(t0 + TPB, P.n_q) - 1;
   const int ntiles = p_bhi / 64 + 1;
 
+  // Tile kt+1 is fetched into registers while tile kt is consumed from LDS;
+  // one barrier per tile separates the LDS writes of tile kt+1 from the reads
+  // of tile kt-1 in the same buffer.
+  TileRegs tr;
+  tile_fetch<true>(P.kv, b, g, 0, P.n_kv, tr);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int key0 = kt * 64;
-    load_kv_tile(P.kv, b, g, key0, P.n_kv, Ks, Vt, true);
+    const int buf = kt & 1;
+    tile_store<true>(tr, Ks[buf], Vt[buf]);
     __syncthreads();
+    if (kt + 1 < ntiles) tile_fetch<true>(P.kv, b, g, key0 + 64, P.n_kv, tr);
+    __builtin_amdgcn_sched_barrier(0);
     if (wave_live && key0 <= p_whi) {
       f32x16 acc[2];
-      qk_tile(Ks, qb, acc);
+      qk_tile(Ks[buf], qb, acc);
       if (key0 + 63 > p_wlo) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -218,7 +234,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           }
         }
       }
-      // online softmax (exp2 domain)
+      // online softmax (exp2 domain); O is rescaled only when some row's
+      // running maximum moved
       float mx = kNegInf;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -227,7 +244,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       mx = xor32_max(mx);
       const float m_new = fmaxf(m_run, mx * cexp);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      if (ballot(m_new != m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[bk][i] *= alpha;
+        m_run = m_new;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -237,35 +262,30 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           acc[c][i] = pv;
           psum += pv;
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[bk][i] *= alpha;
+      l_run += psum;
       bf16x8 pb[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = s >> 1, base = 8 * (s & 1);
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int c = s2 >> 1, base = 8 * (s2 & 1);
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[c][base + 2 * e], acc[c][base + 2 * e + 1]);
-        pb[s] = as_bf16x8(w);
+        pb[s2] = as_bf16x8(w);
       }
+      const uint16_t* vt = Vt[buf];
 #pragma unroll
       for (int bk = 0; bk < 4; ++bk) {
-        const uint16_t* vrow = &Vt[(32 * bk + n) * kVS];
+        const uint16_t* vrow = &vt[(32 * bk + n) * kVS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kb = 32 * (s >> 1) + 16 * (s & 1) + 4 * h;
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1) + 4 * h;
           const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
           const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s], oacc[bk]);
+          oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s2], oacc[bk]);
         }
       }
     }
-    __syncthreads();
   }
 
   const float l_tot = xor32_sum(l_run);
@@ -332,8 +352,8 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
       u32x4 kw[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = s0 + 4 * kq + r;
-        kw[r] = s < ns_hi ? ld16(P.kv.k_row(b, g, s * P.stride) + 8 * dq) : u32x4{0u, 0u, 0u, 0u};
+        const int sidx = imin(s0 + 4 * kq + r, ns_hi - 1);
+        kw[r] = ld16(P.kv.k_row(b, g, sidx * P.stride) + 8 * dq);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) st16(&Ks[(4 * kq + r) * kKS + 8 * dq], kw[r]);
