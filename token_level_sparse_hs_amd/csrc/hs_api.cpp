@@ -99,6 +99,9 @@ hs_status validate_common(const hs_shape* s, Layout* lay) {
     if (l.sb % 8 || l.sh % 8 || l.st % 8 || l.voff % 8)
       return fail(HS_ERR_INVALID_ARG, "cache strides and V offset must be multiples of 8 elements (16-byte rows)");
   }
+  // Rows of one (b, g) slab are addressed with 32-bit element offsets.
+  if ((double)l.st * (double)s->kv_capacity + (double)l.voff + 128.0 > 2147483647.0)
+    return fail(HS_ERR_UNSUPPORTED, "one (batch, kv head) cache slab must span < 2^31 elements");
   *lay = l;
   return HS_OK;
 }
@@ -106,7 +109,7 @@ hs_status validate_common(const hs_shape* s, Layout* lay) {
 float eff_scale(const hs_shape* s) { return s->scale == 0.f ? 1.0f / std::sqrt((float)s->head_dim) : s->scale; }
 
 hs::KvView kv_view(const void* kv, const Layout& l) {
-  return hs::KvView{static_cast<const uint16_t*>(kv), l.sb, l.sh, l.st, l.voff};
+  return hs::KvView{static_cast<const uint16_t*>(kv), l.sb, l.sh, (int32_t)l.st, (int32_t)l.voff};
 }
 
 // ------------------------------------------------------------ plans

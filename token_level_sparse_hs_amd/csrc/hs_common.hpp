@@ -70,9 +70,11 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
 
+// With NaN-free, non-IEEE-mode compilation (see the build flags) a DPP move
+// feeding a max folds into a single v_max_f32_dpp.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+  return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(v), CTRL, 0xF, 0xF, true));
 }
 
 // Max over aligned groups of N consecutive lanes (N in {1,2,4,8}); every lane
@@ -128,15 +130,21 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
-// Position of cache row t of (b, g), in bf16 elements.
+// Cache addressing. One (b, g) slab spans fewer than 2^31 elements (checked
+// on the host), so rows inside a slab use 32-bit offsets from a 64-bit slab
+// base computed once.
 struct KvView {
   const uint16_t* base;
-  int64_t sb, sh, st, voff;
+  int64_t sb, sh;
+  int32_t st, voff;
+  __device__ __forceinline__ const uint16_t* slab(int b, int g) const {
+    return base + (int64_t)b * sb + (int64_t)g * sh;
+  }
   __device__ __forceinline__ const uint16_t* k_row(int b, int g, int t) const {
-    return base + (int64_t)b * sb + (int64_t)g * sh + (int64_t)t * st;
+    return slab(b, g) + (uint32_t)(t * st);
   }
   __device__ __forceinline__ const uint16_t* v_row(int b, int g, int t) const {
-    return k_row(b, g, t) + voff;
+    return slab(b, g) + (uint32_t)(t * st + voff);
   }
 };
 

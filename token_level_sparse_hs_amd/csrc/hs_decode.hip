@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     for (int s = 0; s < 4; ++s) qb[s] = as_bf16x8(n < G ? ld16(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u});
   }
 
+  const uint16_t* slab = P.kv.slab(b, g);
   f32x4 oacc[8] = {};
   float m_run = kNegInf, l_part = 0.f;
   const float cexp = P.scale * kLog2e;
@@ -188,13 +189,13 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     // unconditional lets the compiler wait only for the chunk it consumes.
     const int jk = key(v0 + n);
     const bool rv = jk >= 0;
-    const uint16_t* kr = P.kv.k_row(b, g, rv ? jk : 0) + 8 * gq;
+    const uint16_t* kr = slab + (uint32_t)((rv ? jk : 0) * P.kv.st + 8 * gq);
 #pragma unroll
     for (int s = 0; s < 4; ++s) ch.ka[s] = as_bf16x8(ld16(kr + 32 * s));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = key(v0 + 4 * gq + r);
-      ch.vw[r] = ld16(P.kv.v_row(b, g, j >= 0 ? j : 0) + 8 * n);
+      ch.vw[r] = ld16(slab + (uint32_t)((j >= 0 ? j : 0) * P.kv.st + P.kv.voff + 8 * n));
     }
     ch.vmask = (uint32_t)(ballot(rv) & 0xffffu);
   };

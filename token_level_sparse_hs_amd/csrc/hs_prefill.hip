@@ -56,14 +56,16 @@ struct TileRegs {
 };
 
 template <bool WITH_V>
-__device__ __forceinline__ void tile_fetch(const KvView& kv, int b, int g, int key0, int valid_end, TileRegs& r) {
+__device__ __forceinline__ void tile_fetch(const uint16_t* slab, int st, int voff, int key0, int valid_end,
+                                           TileRegs& r) {
   const int tid = threadIdx.x;
   const int dq = tid & 15, kq = (tid >> 4) & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = imin(key0 + 4 * kq + i, valid_end - 1);
-    r.k[i] = ld16(kv.k_row(b, g, j) + 8 * dq);
-    if (WITH_V) r.v[i] = ld16(kv.v_row(b, g, j) + 8 * dq);
+    const uint16_t* row = slab + (uint32_t)(j * st + 8 * dq);
+    r.k[i] = ld16(row);
+    if (WITH_V) r.v[i] = ld16(row + voff);
   }
 }
 
@@ -123,21 +125,16 @@ template <int G>
 __device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, n = lane & 31;
-  float mx[2][16];
+  float* row = sig + (n / G) * 64;
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx[c][i] = group_max<G>(acc[c][i]);
-  if (n % G == 0) {
-    float* row = sig + (n / G) * 64;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 v;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v = {mx[c][4 * q4], mx[c][4 * q4 + 1], mx[c][4 * q4 + 2], mx[c][4 * q4 + 3]};
-        *reinterpret_cast<f32x4*>(row + 32 * c + 8 * q4 + 4 * h) = v;
-      }
-  }
+      for (int i = 0; i < 4; ++i) v[i] = group_max<G>(acc[c][4 * q4 + i]);
+      if (n % G == 0) *reinterpret_cast<f32x4*>(row + 32 * c + 8 * q4 + 4 * h) = v;
+    }
 }
 
 template <int G>
@@ -174,10 +171,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 
   float theta[TPW];
   int cnt[TPW];
+  float* bs_row[TPW];
+  int32_t* bj_row[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tk = wt0 + u;
-    theta[u] = (P.select && tk < P.n_q) ? P.theta[((int64_t)b * P.n_q + tk) * P.Hkv + g] : kNegInf;
+    const int64_t row = ((int64_t)b * P.n_q + tk) * P.Hkv + g;
+    theta[u] = (P.select && tk < P.n_q) ? P.theta[row] : kNegInf;
+    bs_row[u] = P.buf_sigma + row * P.cap;
+    bj_row[u] = P.buf_j + row * P.cap;
     cnt[u] = 0;
   }
 
@@ -191,14 +193,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   // Tile kt+1 is fetched into registers while tile kt is consumed from LDS;
   // one barrier per tile separates the LDS writes of tile kt+1 from the reads
   // of tile kt-1 in the same buffer.
+  const uint16_t* slab = P.kv.slab(b, g);
   TileRegs tr;
-  tile_fetch<true>(P.kv, b, g, 0, P.n_kv, tr);
+  tile_fetch<true>(slab, P.kv.st, P.kv.voff, 0, P.n_kv, tr);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int key0 = kt * 64;
     const int buf = kt & 1;
     tile_store<true>(tr, Ks[buf], Vt[buf]);
     __syncthreads();
-    if (kt + 1 < ntiles) tile_fetch<true>(P.kv, b, g, key0 + 64, P.n_kv, tr);
+    if (kt + 1 < ntiles) tile_fetch<true>(slab, P.kv.st, P.kv.voff, key0 + 64, P.n_kv, tr);
     __builtin_amdgcn_sched_barrier(0);
     if (wave_live && key0 <= p_whi) {
       f32x16 acc[2];
@@ -226,9 +229,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           if (m) {
             const int pos = cnt[u] + (int)lane_prefix(m);
             if (pass && pos < P.cap) {
-              const int64_t row = ((int64_t)b * P.n_q + tk) * P.Hkv + g;
-              P.buf_sigma[row * P.cap + pos] = v;
-              P.buf_j[row * P.cap + pos] = j;
+              bs_row[u][pos] = v;
+              bj_row[u][pos] = j;
             }
             cnt[u] += __popcll(m);
           }
@@ -346,6 +348,7 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
   const int ns_whi = wt0 < P.n_q ? (imax(0, off + wlast - P.window + 1) + P.stride - 1) / P.stride : 0;
 
   const int dq = tid & 15, kq = tid >> 4;
+  const uint16_t* slab = P.kv.slab(b, g);
   for (int st = 0; st < ntiles; ++st) {
     const int s0 = st * 64;
     {
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int sidx = imin(s0 + 4 * kq + r, ns_hi - 1);
-        kw[r] = ld16(P.kv.k_row(b, g, sidx * P.stride) + 8 * dq);
+        kw[r] = ld16(slab + (uint32_t)(sidx * P.stride * P.kv.st + 8 * dq));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) st16(&Ks[(4 * kq + r) * kKS + 8 * dq], kw[r]);

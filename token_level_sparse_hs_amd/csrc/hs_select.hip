@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kSelThreads) void select_prefill_kernel(SelectParam
     qs[i] = __uint_as_float((uint32_t)v << 16);
   }
   __syncthreads();
-  RescanSrc src{qs, P.kv.k_row(b, g, 0), P.kv.st, G, P.scale};
+  RescanSrc src{qs, P.kv.slab(b, g), P.kv.st, G, P.scale};
   topk_any<BIG>(sh, lds.key, lds.idx, src, ncand, P.top_k, out);
   if (threadIdx.x == 0 && P.rescan_count) atomicAdd(P.rescan_count, 1u);
 }
