@@ -101,7 +101,9 @@ def attention_over_set(q: np.ndarray, K: np.ndarray, V: np.ndarray,
 
     Definition [SSA-3.6]: o = sum_j softmax_j(scale * q.k_j) v_j, evaluated in
     float64 with the row maximum subtracted before exponentiation. Returns
-    (o [H][d], lse [H]) with lse = m + ln(sum exp(s - m)).
+    (o [H][d], lse [H]) with lse = m + ln(sum exp(s - m)). `keys` is an index
+    array or a slice (a contiguous range, taken as a view: callers may pass
+    float64 caches to avoid per-call conversion of long contexts).
     """
     q = np.asarray(q, dtype=np.float64)
     Ks = np.asarray(K[keys], dtype=np.float64)          # [n][d]
@@ -136,7 +138,7 @@ def full_attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
     lse = np.zeros((rows, Hq), dtype=np.float64)
     for r in range(rows):
         p = int(positions[r])
-        keys = np.arange(p + 1)
+        keys = slice(0, p + 1)
         for g in range(Hkv):
             hs = slice(g * G, (g + 1) * G)
             o[r, hs], lse[r, hs] = attention_over_set(q[r, hs], K[g], V[g], keys, scale)

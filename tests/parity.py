@@ -69,10 +69,27 @@ def check_idx_row(got: np.ndarray, ref: np.ndarray, sigma: np.ndarray, tau: floa
 
 
 def cache_np(kv: torch.Tensor, b: int, n: int):
-    """K, V of sequence b as float32 numpy [Hkv][n][d]."""
-    K = kv[b, :, :n, 0].float().cpu().numpy()
-    V = kv[b, :, :n, 1].float().cpu().numpy()
+    """K, V of sequence b as float64 numpy [Hkv][n][d] (exact widening of bf16;
+    float64 so that the oracle takes contiguous ranges as views)."""
+    K = kv[b, :, :n, 0].cpu().double().numpy()
+    V = kv[b, :, :n, 1].cpu().double().numpy()
     return K, V
+
+
+def sample_rows(n_q: int, n_kv: int, top_k: int, window: int, spans=(), evenly=8):
+    """Deterministic query-row sample: first and last rows, the rows at the
+    window and top-k boundaries (p = W-1, W, W+k-1, W+k when inside the
+    chunk), the first row of some needle spans, and evenly spaced rows."""
+    off = n_kv - n_q
+    rows = {0, n_q - 1}
+    for p in (window - 1, window, window + top_k - 1, window + top_k):
+        if off <= p < n_kv:
+            rows.add(p - off)
+    for t0 in list(spans)[:4]:
+        rows.add(int(t0))
+    for i in range(evenly):
+        rows.add(int(i * (n_q - 1) / max(1, evenly - 1)))
+    return sorted(r for r in rows if 0 <= r < n_q)
 
 
 def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_sparse=(), o_sparse=(), scale=None):
