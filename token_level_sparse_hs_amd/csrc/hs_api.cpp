@@ -156,9 +156,10 @@ struct DecodePlan {
 };
 
 // Splits a per-(b, g) key stream of up to `nkeys` keys so that the grid holds
-// roughly 8192 waves (32 per CU), in multiples of 32 keys.
-void plan_splits(int64_t bg, int64_t nkeys, int* splits, int* split_len) {
-  const int64_t target = std::max<int64_t>(1, (8192 + bg - 1) / bg);
+// roughly `waves` waves, in multiples of 32 keys. Many short splits keep the
+// last round of resident waves small relative to the whole.
+void plan_splits(int64_t bg, int64_t nkeys, int* splits, int* split_len, int64_t waves = 8192) {
+  const int64_t target = std::max<int64_t>(1, (waves + bg - 1) / bg);
   int64_t len = round_up(std::max<int64_t>(1, (nkeys + target - 1) / target), 32);
   len = std::max<int64_t>(len, 32);
   *split_len = (int)len;
@@ -169,7 +170,11 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   DecodePlan p;
   const int G = s->q_heads / s->kv_heads;
   const int64_t bg = (int64_t)s->batch * s->kv_heads;
-  plan_splits(bg, max_seq_len, &p.splits, &p.split_len);
+  plan_splits(bg, max_seq_len, &p.splits, &p.split_len, 32768);
+  if (p.splits > 4096) {  // bound of the combine kernel's weight table
+    p.split_len = (int)round_up((max_seq_len + 4095) / 4096, 32);
+    p.splits = (int)((max_seq_len + p.split_len - 1) / p.split_len);
+  }
   p.sigma_stride = round_up(max_seq_len, 64);
   size_t o = 0;
   p.off_sigma = o;

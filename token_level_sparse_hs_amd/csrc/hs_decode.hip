@@ -96,11 +96,14 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     p = imin(P.seq_lens[b], P.n_kv) - 1;  // n_kv carries the host bound max_seq_len
     if (p < 0) return;
   } else {
-    total = (int64_t)P.B * P.n_q * P.Hkv;
-    if (item >= total) return;
+    // A block holds four consecutive query rows of one KV group, and the group
+    // varies fastest over blocks: with blocks dealt round-robin to the XCDs,
+    // each XCD's L2 then serves one group, and neighbouring rows (which share
+    // their window and often popular keys) run side by side.
     split = 0;
-    g = (int)(item % P.Hkv);
-    const int64_t bt = item / P.Hkv;
+    g = (int)(blockIdx.x % P.Hkv);
+    const int64_t bt = (int64_t)(blockIdx.x / P.Hkv) * 4 + wave;
+    if (bt >= (int64_t)P.B * P.n_q) return;
     t = (int)(bt % P.n_q);
     b = (int)(bt / P.n_q);
     p = P.n_kv - P.n_q + t;
@@ -192,11 +195,28 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     const uint16_t* kr = slab + (uint32_t)((rv ? jk : 0) * P.kv.st + 8 * gq);
 #pragma unroll
     for (int s = 0; s < 4; ++s) ch.ka[s] = as_bf16x8(ld16(kr + 32 * s));
+    // the four V keys of this lane are consecutive virtual keys: one 16-byte
+    // LDS read of the staged idx row
+    int jv[4];
+    const int vb = v0 + 4 * gq;
+    if constexpr (SPARSE) {
+      const int vi = imin(imax(vb - seg0, 0), kSeg - 4);
+      const int4 e4 = *reinterpret_cast<const int4*>(&klist[vi]);
+      const int e[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = key(v0 + 4 * gq + r);
-      ch.vw[r] = ld16(slab + (uint32_t)((j >= 0 ? j : 0) * P.kv.st + P.kv.voff + 8 * n));
+      for (int r = 0; r < 4; ++r) {
+        const int v = vb + r;
+        const int js = (e[r] >= 0 && e[r] <= kl.lim) ? e[r] : -1;
+        const int j = v < kl.k ? js : kl.w0 + (v - kl.k);
+        jv[r] = v < vend ? j : -1;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) jv[r] = vb + r < vend ? vb + r : -1;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      ch.vw[r] = ld16(slab + (uint32_t)((jv[r] >= 0 ? jv[r] : 0) * P.kv.st + P.kv.voff + 8 * n));
     ch.vmask = (uint32_t)(ballot(rv) & 0xffffu);
   };
 
@@ -239,9 +259,20 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     // online softmax
     float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     mx = xor32_max(xor16_max(mx));
-    const float m_new = fmaxf(m_run, mx * cexp);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // Deferred rescaling: the reference maximum moves only when a score
+    // exceeds it by more than 2^kRescaleLog2, so P stays <= 2^8 and O, l are
+    // rarely touched; numerator and denominator share the reference, so the
+    // normalised result is the same.
+    const float m_cand = mx * cexp;
+    if (ballot(m_cand > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == kNegInf ? 0.f : m_new));  // -inf -> 0
+      l_part *= alpha;
+#pragma unroll
+      for (int bk = 0; bk < 8; ++bk) oacc[bk] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -249,10 +280,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
       acc[i] = pv;
       psum += pv;
     }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int bk = 0; bk < 8; ++bk) oacc[bk] *= alpha;
+    l_part += psum;
     u32x2 pb;
     pb[0] = pack_bf16x2(acc[0], acc[1]);
     pb[1] = pack_bf16x2(acc[2], acc[3]);
@@ -266,22 +294,28 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
 
   // Two chunks in flight: the next chunk's gathers are issued before the
   // current chunk is consumed.
-  // The next chunk is always issued (past the end its slots are invalid and
+  // Later chunks are always issued (past the end their slots are invalid and
   // read row 0), so every path carries the same loads in flight and the
   // compiler waits only for the chunk being consumed.
   // sched_barrier keeps each batch of gathers ahead of the previous chunk's
   // math, so the waits before that math cover only the previous chunk.
-  Chunk A, B;
+  // Three chunks in flight.
+  Chunk A, B, C;
   load(A, vbeg);
-  for (int v0 = vbeg;; v0 += 32) {
-    load(B, v0 + 16);
+  load(B, vbeg + 16);
+  for (int v0 = vbeg;; v0 += 48) {
+    load(C, v0 + 32);
     __builtin_amdgcn_sched_barrier(0);
     compute(A, v0);
     if (v0 + 16 >= vend) break;
-    load(A, v0 + 32);
+    load(A, v0 + 48);
     __builtin_amdgcn_sched_barrier(0);
     compute(B, v0 + 16);
     if (v0 + 32 >= vend) break;
+    load(B, v0 + 64);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(C, v0 + 32);
+    if (v0 + 48 >= vend) break;
   }
 
   const float l_tot = xor32_sum(xor16_sum(l_part));
@@ -328,7 +362,13 @@ __global__ void append_kernel(AppendParams P) {
 }
 
 // Log-sum-exp merge of split partials; one 128-thread block per (b, head).
+// Pass 1 (threads over splits): M = max m_s, then weights w_s = 2^(m_s - M)
+// into LDS and l = sum w_s l_s. Pass 2 (threads over dims): o = sum w_s acc_s / l
+// with independent loads.
+constexpr int kMaxCombineSplits = 4096;
 __global__ __launch_bounds__(128) void combine_kernel(CombineParams P) {
+  __shared__ float wsh[kMaxCombineSplits];
+  __shared__ float red[2][4];
   const int bh = blockIdx.x;
   const int head = bh % P.Hq, b = bh / P.Hq;
   const int G = P.Hq / P.Hkv;
@@ -336,28 +376,48 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams P) {
   const int L = imin(P.seq_lens[b], P.max_len);
   if (L < 1) return;
   const int nv = P.sparse_k >= 0 ? P.sparse_k + (L < P.window ? L : P.window) : L;
-  const int ns = imin(P.splits, (nv + P.split_len - 1) / P.split_len);
+  const int ns = imin(imin(P.splits, (nv + P.split_len - 1) / P.split_len), kMaxCombineSplits);
   const float* base = P.part + (((int64_t)b * P.Hkv + g) * P.splits * G + n) * (kHeadDim + 2);
   const int64_t sstride = (int64_t)G * (kHeadDim + 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * sstride + kHeadDim]);
+  for (int s = tid; s < ns; s += 128) M = fmaxf(M, base[s * sstride + kHeadDim]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
   const float Mu = M == kNegInf ? 0.f : M;
-  float acc = 0.f, l = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* pp = base + s * sstride;
-    const float w = __builtin_amdgcn_exp2f(pp[kHeadDim] - Mu);
-    acc += w * pp[threadIdx.x];
-    l += w * pp[kHeadDim + 1];
+  float l = 0.f;
+  for (int s = tid; s < ns; s += 128) {
+    const float w = __builtin_amdgcn_exp2f(base[s * sstride + kHeadDim] - Mu);
+    wsh[s] = w;
+    l += w * base[s * sstride + kHeadDim + 1];
   }
-  const float o = acc / l;
-  P.o[((int64_t)b * P.Hq + head) * kHeadDim + threadIdx.x] = (uint16_t)f32_to_bf16_bits(o);
-  if (P.lse && threadIdx.x == 0) P.lse[(int64_t)b * P.Hq + head] = M * kLn2 + __logf(l);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+  if (lane == 0) red[1][wave] = l;
+  __syncthreads();
+  l = red[1][0] + red[1][1];
+  float acc = 0.f;
+  const float* pd = base + tid;
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pd[(s + u) * sstride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += wsh[s + u] * v[u];
+  }
+  for (; s < ns; ++s) acc += wsh[s] * pd[s * sstride];
+  P.o[((int64_t)b * P.Hq + head) * kHeadDim + tid] = (uint16_t)f32_to_bf16_bits(acc / l);
+  if (P.lse && tid == 0) P.lse[(int64_t)b * P.Hq + head] = M * kLn2 + __logf(l);
 }
 
 template <int G, bool SPARSE>
 hipError_t launch_gather_g(const DecodeParams& p, hipStream_t s) {
-  const int64_t items = p.seq_lens ? (int64_t)p.B * p.Hkv * p.splits : (int64_t)p.B * p.n_q * p.Hkv;
-  const int64_t blocks = (items + 3) / 4;
+  const int64_t blocks = p.seq_lens ? ((int64_t)p.B * p.Hkv * p.splits + 3) / 4
+                                    : (((int64_t)p.B * p.n_q + 3) / 4) * p.Hkv;
   flash_gather_kernel<G, SPARSE><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }

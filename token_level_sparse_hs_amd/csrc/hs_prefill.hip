@@ -244,10 +244,11 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[c][i]);
       mx = xor32_max(mx);
-      const float m_new = fmaxf(m_run, mx * cexp);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      if (ballot(m_new != m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // deferred rescaling (see the gather kernel): P <= 2^kRescaleLog2
+      const float m_cand = mx * cexp;
+      if (ballot(m_cand > m_run + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run, m_cand);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == kNegInf ? 0.f : m_new));
         l_run *= alpha;
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk)
@@ -255,6 +256,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           for (int i = 0; i < 16; ++i) oacc[bk][i] *= alpha;
         m_run = m_new;
       }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
       float psum = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
