@@ -63,6 +63,17 @@ __device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                     0, 0, 0);
 }
 
+// ds_read_b64_tr_b16: within each group of 16 lanes, the lanes' 8-byte
+// pieces (4 bf16 each, read at each lane's own address, in lane order) form a
+// 4 x 16 matrix; lane i of the group receives column i. With a row-major tile
+// T[row][col] and lane j = 4r + c of a group addressing T[row0 + r][col0 + 4c],
+// lane i receives T[row0 + 0..3][col0 + i].
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // ---------------------------------------------------------------- cross-lane
 
 // DPP controls (gfx9 encoding).

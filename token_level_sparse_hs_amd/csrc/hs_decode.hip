@@ -21,9 +21,10 @@
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K rows gathered straight
 //    from the cache into A operands (16 B per lane); the G query heads of the
 //    group occupy MFMA columns 0..G-1, so one K/V row read serves all heads.
-//  * V rows are gathered 4 keys x 8 dims per lane, transposed with byte
-//    permutes into a per-wave LDS tile, and read back as the A operand of
-//    O^T = V^T P^T; P^T is already in B-operand layout in registers.
+//  * V rows are gathered 4 keys x 8 dims per lane into a row-major per-wave
+//    LDS tile and read back transposed (ds_read_b64_tr_b16) as the A operand
+//    of O^T = V^T P^T on v_mfma_f32_16x16x16_bf16; P^T is already in B-operand
+//    layout in registers.
 //  * Softmax state is per lane (query column = lane%16) with two cross-lane
 //    exchanges (lane^16, lane^32) per chunk; accumulation is fp32.
 #include "hs_common.hpp"
@@ -33,7 +34,7 @@ namespace hs {
 
 namespace {
 
-constexpr int kVtS = 20;  // per-wave V^T tile row stride in bf16 (16 keys + pad, 40 B)
+constexpr int kVS16 = 144;  // per-wave V tile row stride in bf16 (128 dims + pad: 288 B)
 
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -73,7 +74,7 @@ struct Chunk {
 
 template <int G, bool SPARSE>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t Vt_all[4][128 * kVtS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt_all[4][16 * kVS16];
   __shared__ __attribute__((aligned(16))) int32_t klist_all[4][SPARSE ? kSeg : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
@@ -246,16 +247,9 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
         }
       }
     }
-    // V^T into LDS: dims 8n+c, keys 4gq..4gq+3
+    // V rows into LDS, row-major (key 4gq + r, dims 8n..8n+7)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int w = c >> 1;
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 tv;
-      tv[0] = __builtin_amdgcn_perm(ch.vw[1][w], ch.vw[0][w], sel);
-      tv[1] = __builtin_amdgcn_perm(ch.vw[3][w], ch.vw[2][w], sel);
-      *reinterpret_cast<u32x2*>(&Vt[(8 * n + c) * kVtS + 4 * gq]) = tv;
-    }
+    for (int r = 0; r < 4; ++r) st16(&Vt[(4 * gq + r) * kVS16 + 8 * n], ch.vw[r]);
     // online softmax
     float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     mx = xor32_max(xor16_max(mx));
@@ -285,11 +279,11 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     pb[0] = pack_bf16x2(acc[0], acc[1]);
     pb[1] = pack_bf16x2(acc[2], acc[3]);
     lds_wait();
+    // A operand of O^T = V^T P^T: lane (n, gq) needs V[4gq + e][16bk + n];
+    // lane n of group gq addresses V[4gq + n/4][16bk + 4(n%4)].
+    const uint16_t* vrd = &Vt[(4 * gq + (n >> 2)) * kVS16 + 4 * (n & 3)];
 #pragma unroll
-    for (int bk = 0; bk < 8; ++bk) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(&Vt[(16 * bk + n) * kVtS + 4 * gq]);
-      oacc[bk] = mfma16x16x16(a, pb, oacc[bk]);
-    }
+    for (int bk = 0; bk < 8; ++bk) oacc[bk] = mfma16x16x16(lds_read_tr16(vrd + 16 * bk), pb, oacc[bk]);
   };
 
   // Two chunks in flight: the next chunk's gathers are issued before the

@@ -18,8 +18,9 @@
 //    axis on MFMA rows and the query rows on lanes, every per-row softmax
 //    quantity (running max, sum, rescale) is lane-local apart from one
 //    lane^32 exchange, and the S^T accumulator is already laid out as the B
-//    operand of the PV product. K tiles live row-major in LDS, V tiles
-//    transposed (written transposed once per tile, read as 2x8-byte pieces).
+//    operand of the PV product. K and V tiles live row-major in LDS; V is
+//    read back with LDS transpose reads (ds_read_b64_tr_b16) as the A
+//    operand of O^T = V^T P^T.
 //  * Online softmax in fp32 on exp2 with the scale folded into one FMA.
 //  * Selection: the per-lane scaled logits are maxed over the G head lanes
 //    (DPP), staged per wave in LDS, and every candidate (j <= p - W) whose
@@ -38,7 +39,7 @@ namespace hs {
 namespace {
 
 constexpr int kKS = 136;  // K tile row stride in bf16 (272 B: conflict-free 16-B reads)
-constexpr int kVS = 68;   // V^T tile row stride in bf16 (136 B)
+constexpr int kVS = 144;  // V tile row stride in bf16 (288 B: row r starts at bank 8r)
 
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -69,23 +70,16 @@ __device__ __forceinline__ void tile_fetch(const uint16_t* slab, int st, int vof
   }
 }
 
-// Register -> LDS part: K row-major into Ks, V transposed into Vt.
+// Register -> LDS part: K and V row-major (V is read back transposed).
 template <bool WITH_V>
-__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* Ks, uint16_t* Vt) {
+__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* Ks, uint16_t* Vs) {
   const int tid = threadIdx.x;
   const int dq = tid & 15, kq = (tid >> 4) & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) st16(&Ks[(4 * kq + i) * kKS + 8 * dq], r.k[i]);
   if (WITH_V) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int w = c >> 1;
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 t;
-      t[0] = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
-      t[1] = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
-      *reinterpret_cast<u32x2*>(&Vt[(8 * dq + c) * kVS + 4 * kq]) = t;
-    }
+    for (int i = 0; i < 4; ++i) st16(&Vs[(4 * kq + i) * kVS + 8 * dq], r.v[i]);
   }
 }
 
@@ -142,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   constexpr int TPW = 32 / G;
   constexpr int TPB = 4 * TPW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][128 * kVS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][64 * kVS];
   __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -276,15 +270,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[c][base + 2 * e], acc[c][base + 2 * e + 1]);
         pb[s2] = as_bf16x8(w);
       }
-      const uint16_t* vt = Vt[buf];
+      // A operand of O^T = V^T P^T (lane: dim 32bk + l%32, keys kb + 0..3 and
+      // kb + 8 + 0..3 of the permuted k order): two transpose reads; lane j of
+      // each 16-lane group addresses V[kb + j/4][dim0 + 4(j%4)].
+      const uint16_t* vrd = Vt[buf] + ((lane & 15) >> 2) * kVS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int bk = 0; bk < 4; ++bk) {
-        const uint16_t* vrow = &vt[(32 * bk + n) * kVS];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
           const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1) + 4 * h;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
+          const u32x2 lo = lds_read_tr16(vrd + kb * kVS + 32 * bk);
+          const u32x2 hi = lds_read_tr16(vrd + (kb + 8) * kVS + 32 * bk);
           const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
           oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s2], oacc[bk]);
         }
