@@ -18,13 +18,15 @@
 //  * A work item walks a virtual key list in chunks of 32 keys. FULL: keys
 //    [k0, k1) of a decode row. SPARSE: the idx row (entries < 0 are padding)
 //    followed by the window Win(p).
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K rows gathered straight
-//    from the cache into A operands (16 B per lane); the G query heads of the
-//    group occupy MFMA columns 0..G-1, so one K/V row read serves all heads.
-//  * V rows are gathered 4 keys x 8 dims per lane into a row-major per-wave
-//    LDS tile and read back transposed (ds_read_b64_tr_b16) as the A operand
-//    of O^T = V^T P^T on v_mfma_f32_16x16x16_bf16; P^T is already in B-operand
-//    layout in registers.
+//  * K and V rows are gathered 4 keys x 8 dims per lane, so consecutive
+//    lanes read consecutive bytes of a row (full cache lines, one address
+//    quad per row segment: the texture addresser, not the memory, was the
+//    limit with operand-shaped gathers), and staged in row-major per-wave LDS
+//    tiles. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 reads its A operand from
+//    the K tile; the G query heads of the group occupy MFMA columns 0..G-1,
+//    so one K/V row read serves all heads. V is read back transposed
+//    (ds_read_b64_tr_b16) as the A operand of O^T = V^T P^T on
+//    v_mfma_f32_16x16x16_bf16; P^T is already in B-operand layout.
 //  * Softmax state is per lane (query column = lane%16) with two cross-lane
 //    exchanges (lane^16, lane^32) per chunk; accumulation is fp32.
 #include "hs_common.hpp"
@@ -35,6 +37,7 @@ namespace hs {
 namespace {
 
 constexpr int kVS16 = 144;  // per-wave V tile row stride in bf16 (128 dims + pad: 288 B)
+constexpr int kKS16 = 136;  // per-wave K tile row stride in bf16 (272 B: 16-B reads of 16 rows hit distinct banks)
 
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -67,19 +70,21 @@ constexpr int kSeg = 2048;  // idx-row entries staged per wave (refilled only wh
 // 32s + 8(l/16)..+8) and V rows for the LDS transpose (lane: keys
 // 4(l/16)..+3, dims 8(l%16)..+7), plus the validity mask of its 16 keys.
 struct Chunk {
-  bf16x8 ka[4];
-  u32x4 vw[4];
-  uint32_t vmask;
+  u32x4 kw[4];     // K rows 4gq + r, dims 8n..8n+7 (row-coalesced gather)
+  u32x4 vw[4];     // V rows, same keys
+  uint32_t valid;  // bit r: key 4gq + r is valid
 };
 
 template <int G, bool SPARSE>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t Vt_all[4][16 * kVS16];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt_all[4][16 * kKS16];
   __shared__ __attribute__((aligned(16))) int32_t klist_all[4][SPARSE ? kSeg : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int n = lane & 15, gq = lane >> 4;
   uint16_t* Vt = Vt_all[wave];
+  uint16_t* Kt = Kt_all[wave];
   int32_t* klist = klist_all[wave];
 
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
@@ -177,27 +182,13 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     if constexpr (SPARSE) {
       if (v0 < kl.k && v0 + 16 > seg0 + kSeg) refill(v0 - (v0 % kSeg));
     }
-    // Branch-free (selects only), so no gather ends up under an exec mask.
-    auto key = [&](int v) -> int {
-      int j = v;
-      if constexpr (SPARSE) {
-        const int vi = imin(imax(v - seg0, 0), kSeg - 1);
-        const int e = klist[vi];
-        const int js = (e >= 0 && e <= kl.lim) ? e : -1;
-        j = v < kl.k ? js : kl.w0 + (v - kl.k);
-      }
-      return v < vend ? j : -1;
-    };
-    // Invalid slots read row 0 (always a valid row): their scores are masked
-    // to -inf, so their probabilities are exactly 0. Keeping every gather
-    // unconditional lets the compiler wait only for the chunk it consumes.
-    const int jk = key(v0 + n);
-    const bool rv = jk >= 0;
-    const uint16_t* kr = slab + (uint32_t)((rv ? jk : 0) * P.kv.st + 8 * gq);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) ch.ka[s] = as_bf16x8(ld16(kr + 32 * s));
-    // the four V keys of this lane are consecutive virtual keys: one 16-byte
-    // LDS read of the staged idx row
+    // Each lane gathers keys 4gq..4gq+3 of the chunk (consecutive virtual
+    // keys: one 16-byte LDS read of the staged idx row), 16 bytes of K and of
+    // V per key, so that consecutive lanes read consecutive bytes of one row
+    // (row-coalesced, full cache lines). Invalid slots read row 0 (always a
+    // valid row); their scores are masked to -inf, so their probabilities
+    // are exactly 0. Keeping every gather unconditional lets the compiler
+    // wait only for the chunk it consumes.
     int jv[4];
     const int vb = v0 + 4 * gq;
     if constexpr (SPARSE) {
@@ -215,22 +206,35 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) jv[r] = vb + r < vend ? vb + r : -1;
     }
+    uint32_t valid = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      ch.vw[r] = ld16(slab + (uint32_t)((jv[r] >= 0 ? jv[r] : 0) * P.kv.st + P.kv.voff + 8 * n));
-    ch.vmask = (uint32_t)(ballot(rv) & 0xffffu);
+    for (int r = 0; r < 4; ++r) {
+      const uint16_t* row = slab + (uint32_t)((jv[r] >= 0 ? jv[r] : 0) * P.kv.st + 8 * n);
+      ch.kw[r] = ld16(row);
+      ch.vw[r] = ld16(row + P.kv.voff);
+      valid |= (jv[r] >= 0 ? 1u : 0u) << r;
+    }
+    ch.valid = valid;
   };
 
   // Attention update with the chunk starting at virtual key v0.
   auto compute = [&](const Chunk& ch, int v0) {
+    // K and V rows into the per-wave LDS tiles (row-major, key 4gq + r)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
+      st16(&Vt[(4 * gq + r) * kVS16 + 8 * n], ch.vw[r]);
+    }
+    lds_wait();
+    // S^T = K Q^T: A operand lane (n, gq) = K[key n][32s + 8gq .. +8]
     f32x4 acc = {};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma16x16x32(ch.ka[s], qb[s], acc);
-    // lane holds query column n, chunk keys 4*gq + i
-    if (ch.vmask != 0xffffu) {
+    for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(ld16(&Kt[n * kKS16 + 32 * s + 8 * gq])), qb[s], acc);
+    // lane holds query column n, chunk keys 4*gq + i: the keys it gathered
+    if (ch.valid != 0xfu) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (!((ch.vmask >> (4 * gq + i)) & 1u)) acc[i] = kNegInf;
+        if (!((ch.valid >> i) & 1u)) acc[i] = kNegInf;
     }
     if (!SPARSE && sig_row && v0 <= cand_end) {
       f32x4 mxh;
@@ -247,9 +251,6 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
         }
       }
     }
-    // V rows into LDS, row-major (key 4gq + r, dims 8n..8n+7)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st16(&Vt[(4 * gq + r) * kVS16 + 8 * n], ch.vw[r]);
     // online softmax
     float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     mx = xor32_max(xor16_max(mx));
