@@ -22,6 +22,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-honor-nans", "-mno-amdgpu-ieee",
+    # MFMA accumulators in arch VGPRs: the online-softmax rescale and the
+    # epilogue then touch them in place instead of copying AGPRs every chunk.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-result",
 ]
 

@@ -119,6 +119,18 @@ __device__ __forceinline__ float xor16_sum(float v) {
 }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+// Marks a wave-uniform value as such (keeps it in a scalar register, so that
+// branches on it stay scalar).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Raw buffer over [base, base + 4 GiB): 16-byte loads at a 32-bit byte
+// offset with no per-lane 64-bit address arithmetic (gfx9 resource word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {  // set bits below this lane
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }

@@ -36,63 +36,40 @@ namespace hs {
 
 namespace {
 
-constexpr int kVS16 = 144;  // per-wave V tile row stride in bf16 (128 dims + pad: 288 B)
 constexpr int kKS16 = 136;  // per-wave K tile row stride in bf16 (272 B: 16-B reads of 16 rows hit distinct banks)
+constexpr int kList = 2048;     // staged key offsets per wave (SPARSE)
+constexpr int kListPad = 64;    // zero tail read by the chunks issued past the end
 
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
-template <bool SPARSE>
-struct KeyList {
-  // SPARSE: virtual v < k -> idx[v] (if >= 0), else window token w0 + (v-k).
-  // FULL: v -> v.
-  // Selected entries outside [0, lim] (padding, or a malformed row) are
-  // skipped, so no gather leaves the sequence's valid rows.
-  const int32_t* sel;
-  int k;
-  int w0;
-  int lim;
-  int end;  // virtual end (exclusive)
-  __device__ __forceinline__ int key(int v) const {
-    if (v >= end) return -1;
-    if constexpr (!SPARSE) return v;
-    if (v >= k) return w0 + (v - k);
-    const int j = sel[v];
-    return (j >= 0 && j <= lim) ? j : -1;
-  }
-};
-
-constexpr int kSeg = 2048;  // idx-row entries staged per wave (refilled only when k > kSeg)
-
-// One 16-key chunk in flight: K rows as MFMA A operands (lane: key l%16, dims
-// 32s + 8(l/16)..+8) and V rows for the LDS transpose (lane: keys
-// 4(l/16)..+3, dims 8(l%16)..+7), plus the validity mask of its 16 keys.
+// One 16-key chunk in flight. Lane (n = l%16, gq = l/16) gathers keys
+// 4gq..4gq+3 of the chunk, dims 8n..8n+7 of each K and V row (consecutive
+// lanes read consecutive bytes of a row: full cache lines, one address quad
+// per row segment).
 struct Chunk {
-  u32x4 kw[4];     // K rows 4gq + r, dims 8n..8n+7 (row-coalesced gather)
-  u32x4 vw[4];     // V rows, same keys
-  uint32_t valid;  // bit r: key 4gq + r is valid
+  u32x4 kw[4];  // K rows 4gq + r
+  u32x4 vw[4];  // V rows 4gq + r
+  int nv;       // wave-uniform: keys 0..nv-1 of the chunk are real, the rest masked
 };
 
 template <int G, bool SPARSE>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t Vt_all[4][16 * kVS16];
   __shared__ __attribute__((aligned(16))) uint16_t Kt_all[4][16 * kKS16];
-  __shared__ __attribute__((aligned(16))) int32_t klist_all[4][SPARSE ? kSeg : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t klist_all[4][SPARSE ? kList + kListPad : 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int n = lane & 15, gq = lane >> 4;
-  uint16_t* Vt = Vt_all[wave];
   uint16_t* Kt = Kt_all[wave];
-  int32_t* klist = klist_all[wave];
+  uint32_t* klist = klist_all[wave];
 
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
   const bool decode = P.seq_lens != nullptr;
   int b, t, g, split, p;
-  int64_t total;
   if (decode) {
-    total = (int64_t)P.B * P.Hkv * P.splits;
+    const int64_t total = (int64_t)P.B * P.Hkv * P.splits;
     if (item >= total) return;
     split = (int)(item % P.splits);
     const int64_t bg = item / P.splits;
@@ -116,26 +93,19 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   }
   const int64_t qrow = (int64_t)b * P.n_q + t;  // decode: n_q == 1
 
-  KeyList<SPARSE> kl;
-  int vbeg, vend;
-  if (SPARSE) {
-    kl.sel = P.idx + (qrow * P.Hkv + g) * (int64_t)P.top_k;
-    kl.k = P.top_k;
-    kl.w0 = imax(0, p - P.window + 1);
-    kl.lim = p - P.window;
-    const int nv = P.top_k + (p - kl.w0 + 1);
-    vbeg = split * P.split_len;
-    vend = imin(nv, vbeg + P.split_len);
-  } else {
-    kl.sel = nullptr;
-    kl.k = 0;
-    kl.w0 = 0;
-    kl.lim = p;
-    vbeg = split * P.split_len;
-    vend = imin(p + 1, vbeg + P.split_len);
-  }
-  kl.end = vend;
-  if (vbeg >= vend) return;  // split beyond this row: the combine skips it
+  // Key source. SPARSE: source position i < k is idx entry i (kept when it
+  // lies in [0, p - W], dropped otherwise: padding or a malformed entry);
+  // i >= k is window token w0 + (i - k). A split covers source positions
+  // [sbeg, send); its kept keys are compacted, in source order, into the
+  // wave's LDS list as byte offsets of their cache rows. FULL: keys
+  // [sbeg, send) of the row, in order.
+  const int k = SPARSE ? P.top_k : 0;
+  const int w0 = imax(0, p - P.window + 1);
+  const int lim = p - P.window;  // last selectable token
+  const int ns = SPARSE ? k + (p - w0 + 1) : p + 1;
+  const int sbeg = uniform(split * P.split_len);
+  const int send = uniform(imin(ns, sbeg + P.split_len));
+  if (sbeg >= send) return;  // split beyond this row: the combine skips it
 
   // Query operand: column n = head g*G + n (n < G), dims 32s + 8*gq .. +8.
   bf16x8 qb[4];
@@ -145,102 +115,111 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     for (int s = 0; s < 4; ++s) qb[s] = as_bf16x8(n < G ? ld16(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u});
   }
 
-  const uint16_t* slab = P.kv.slab(b, g);
+  b = uniform(b);
+  g = uniform(g);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(P.kv.slab(b, g));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(P.kv.slab(b, g) + P.kv.voff);
+  const uint32_t rowb = 2u * (uint32_t)P.kv.st;  // bytes per token
+  const uint32_t colb = 16u * (uint32_t)n;       // this lane's 16 bytes of a row
   f32x4 oacc[8] = {};
   float m_run = kNegInf, l_part = 0.f;
   const float cexp = P.scale * kLog2e;
-  const int cand_end = p - P.window;  // last candidate position (FULL score row)
+  const int cand_end = lim;  // last candidate position (FULL score row)
   float* sig_row = nullptr;
   if (!SPARSE && P.sigma) sig_row = P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride;
 
-  // SPARSE: the idx row is staged in LDS, kSeg entries at a time; window
-  // tokens (virtual keys >= k) are computed.
-  int seg0 = -kSeg;
-  auto refill = [&](int base) {
-    seg0 = base;
-    const int cnt = imin(kSeg, kl.k - base);  // >= 1
-    const int32_t* src = kl.sel + base;
-    // All loads are issued before any is consumed (clamped, unconditional);
-    // entries beyond cnt are never looked up as selected tokens.
-    constexpr int kBatch = 8;
+  // SPARSE list state (wave-uniform): klist[0 .. cnt) holds the offsets of
+  // virtual keys vseg0 .. vseg0 + cnt - 1; keys below lend are published to
+  // the chunk loop; spos is the next source position.
+  int vseg0 = 0, cnt = 0, lend = 0, spos = sbeg;
+  const int32_t* sel = SPARSE ? P.idx + (qrow * P.Hkv + g) * (int64_t)P.top_k : nullptr;
+  // Stages the next segment while no gathers are in flight: carries the
+  // unpublished tail [lend, vseg0 + cnt) (fewer than 16 entries) to the
+  // front, appends compacted source entries until the list is nearly full or
+  // the source is exhausted, and publishes whole chunks (all entries once the
+  // source is exhausted). kListPad zero offsets (row 0) follow the entries:
+  // chunks issued past the end read them.
+  auto refill = [&]() {
+    const int keep = vseg0 + cnt - lend;
+    const uint32_t kept = klist[imin(lend - vseg0 + lane, kList + kListPad - 1)];
+    if (lane < keep) klist[lane] = kept;  // one wave: LDS ops stay in order
+    vseg0 = lend;
+    cnt = keep;
+    constexpr int kBatch = 16;
 #pragma unroll 1
-    for (int i0 = 0; i0 < cnt; i0 += 64 * kBatch) {
-      int32_t vals[kBatch];
+    while (spos < send && cnt <= kList - 64 * kBatch) {
+      int ent[kBatch];
+      if (spos < k) {
 #pragma unroll
-      for (int it = 0; it < kBatch; ++it) vals[it] = src[imin(i0 + lane + 64 * it, cnt - 1)];
+        for (int it = 0; it < kBatch; ++it) ent[it] = sel[imin(spos + lane + 64 * it, k - 1)];
+      }
 #pragma unroll
-      for (int it = 0; it < kBatch; ++it) klist[imin(i0 + lane + 64 * it, kSeg - 1)] = vals[it];
+      for (int it = 0; it < kBatch; ++it) {
+        const int i = spos + lane + 64 * it;
+        int e = 0;
+        bool ok = i < send;
+        if (i < k) {
+          e = ent[it];
+          ok = ok && lim >= 0 && (unsigned)e <= (unsigned)lim;
+        } else {
+          e = w0 + (i - k);
+        }
+        const uint64_t m = ballot(ok);
+        if (ok) klist[cnt + (int)lane_prefix(m)] = (uint32_t)e * rowb;
+        cnt = uniform(cnt + __popcll(m));
+      }
+      spos = uniform(spos + 64 * kBatch);
     }
+    klist[cnt + lane] = 0u;
+    lend = uniform(vseg0 + (spos >= send ? cnt : (cnt & ~15)));
     lds_wait();
   };
-  if constexpr (SPARSE) {
-    if (vbeg < kl.k) refill(vbeg - (vbeg % kSeg));
-  }
 
-  // Issues the gathers of the chunk starting at virtual key v0.
-  auto load = [&](Chunk& ch, int v0) {
+  // Issues the gathers of the chunk starting at virtual key v (keys below
+  // vend are real).
+  auto load = [&](Chunk& ch, int v, int vend) {
+    uint32_t off[4];
     if constexpr (SPARSE) {
-      if (v0 < kl.k && v0 + 16 > seg0 + kSeg) refill(v0 - (v0 % kSeg));
-    }
-    // Each lane gathers keys 4gq..4gq+3 of the chunk (consecutive virtual
-    // keys: one 16-byte LDS read of the staged idx row), 16 bytes of K and of
-    // V per key, so that consecutive lanes read consecutive bytes of one row
-    // (row-coalesced, full cache lines). Invalid slots read row 0 (always a
-    // valid row); their scores are masked to -inf, so their probabilities
-    // are exactly 0. Keeping every gather unconditional lets the compiler
-    // wait only for the chunk it consumes.
-    int jv[4];
-    const int vb = v0 + 4 * gq;
-    if constexpr (SPARSE) {
-      const int vi = imin(imax(vb - seg0, 0), kSeg - 4);
-      const int4 e4 = *reinterpret_cast<const int4*>(&klist[vi]);
-      const int e[4] = {e4.x, e4.y, e4.z, e4.w};
+      const u32x4 e4 = *reinterpret_cast<const u32x4*>(&klist[v - vseg0 + 4 * gq]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) off[r] = e4[r] + colb;
+    } else {
+      const int vb = sbeg + v;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int v = vb + r;
-        const int js = (e[r] >= 0 && e[r] <= kl.lim) ? e[r] : -1;
-        const int j = v < kl.k ? js : kl.w0 + (v - kl.k);
-        jv[r] = v < vend ? j : -1;
+        const int j = vb + 4 * gq + r;
+        off[r] = (uint32_t)(j < send ? j : 0) * rowb + colb;
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) jv[r] = vb + r < vend ? vb + r : -1;
     }
-    uint32_t valid = 0;
+    ch.nv = uniform(imin(imax(vend - v, 0), 16));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint16_t* row = slab + (uint32_t)((jv[r] >= 0 ? jv[r] : 0) * P.kv.st + 8 * n);
-      ch.kw[r] = ld16(row);
-      ch.vw[r] = ld16(row + P.kv.voff);
-      valid |= (jv[r] >= 0 ? 1u : 0u) << r;
+      ch.kw[r] = buf_ld16(krs, off[r]);
+      ch.vw[r] = buf_ld16(vrs, off[r]);
     }
-    ch.valid = valid;
   };
 
-  // Attention update with the chunk starting at virtual key v0.
-  auto compute = [&](const Chunk& ch, int v0) {
-    // K and V rows into the per-wave LDS tiles (row-major, key 4gq + r)
+  // Attention update with the chunk starting at virtual key v.
+  auto compute = [&](const Chunk& ch, int v) {
+    // K rows into the per-wave LDS tile (row-major, key 4gq + r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
-      st16(&Vt[(4 * gq + r) * kVS16 + 8 * n], ch.vw[r]);
-    }
+    for (int r = 0; r < 4; ++r) st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
     lds_wait();
     // S^T = K Q^T: A operand lane (n, gq) = K[key n][32s + 8gq .. +8]
     f32x4 acc = {};
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(ld16(&Kt[n * kKS16 + 32 * s + 8 * gq])), qb[s], acc);
     // lane holds query column n, chunk keys 4*gq + i: the keys it gathered
-    if (ch.valid != 0xfu) {
+    if (ch.nv < 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (!((ch.valid >> i) & 1u)) acc[i] = kNegInf;
+        if (4 * gq + i >= ch.nv) acc[i] = kNegInf;
     }
-    if (!SPARSE && sig_row && v0 <= cand_end) {
+    if (!SPARSE && sig_row && sbeg + v <= cand_end) {
       f32x4 mxh;
 #pragma unroll
       for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
-      const int j = v0 + 4 * gq;
+      const int j = sbeg + v + 4 * gq;
       if (n == 0) {
         if (j + 3 <= cand_end && ((j & 3) == 0)) {
           *reinterpret_cast<f32x4*>(sig_row + j) = mxh;
@@ -279,59 +258,80 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     u32x2 pb;
     pb[0] = pack_bf16x2(acc[0], acc[1]);
     pb[1] = pack_bf16x2(acc[2], acc[3]);
-    lds_wait();
-    // A operand of O^T = V^T P^T: lane (n, gq) needs V[4gq + e][16bk + n];
-    // lane n of group gq addresses V[4gq + n/4][16bk + 4(n%4)].
-    const uint16_t* vrd = &Vt[(4 * gq + (n >> 2)) * kVS16 + 4 * (n & 3)];
+    // O^T = V^T P^T with the head dimension permuted: tile bk, row r stands
+    // for dim 8r + bk, so the A operand (row n, keys 4gq..4gq+3) is element
+    // bk of this lane's own four V rows; no data leaves the lane.
 #pragma unroll
-    for (int bk = 0; bk < 8; ++bk) oacc[bk] = mfma16x16x16(lds_read_tr16(vrd + 16 * bk), pb, oacc[bk]);
+    for (int bk = 0; bk < 8; ++bk) {
+      const uint32_t sel2 = (bk & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 a;
+      a[0] = __builtin_amdgcn_perm(ch.vw[1][bk >> 1], ch.vw[0][bk >> 1], sel2);
+      a[1] = __builtin_amdgcn_perm(ch.vw[3][bk >> 1], ch.vw[2][bk >> 1], sel2);
+      oacc[bk] = mfma16x16x16(a, pb, oacc[bk]);
+    }
   };
 
-  // Two chunks in flight: the next chunk's gathers are issued before the
-  // current chunk is consumed.
-  // Later chunks are always issued (past the end their slots are invalid and
-  // read row 0), so every path carries the same loads in flight and the
-  // compiler waits only for the chunk being consumed.
+  // Three chunks in flight: chunks are issued two ahead of the one consumed
+  // (unconditionally: past the end they are masked and read row 0), and
   // sched_barrier keeps each batch of gathers ahead of the previous chunk's
-  // math, so the waits before that math cover only the previous chunk.
-  // Three chunks in flight.
-  Chunk A, B, C;
-  load(A, vbeg);
-  load(B, vbeg + 16);
-  for (int v0 = vbeg;; v0 += 48) {
-    load(C, v0 + 32);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(A, v0);
-    if (v0 + 16 >= vend) break;
-    load(A, v0 + 48);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(B, v0 + 16);
-    if (v0 + 32 >= vend) break;
-    load(B, v0 + 64);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(C, v0 + 32);
-    if (v0 + 48 >= vend) break;
+  // math. The steady-state loop runs whole triples and has a single
+  // exit at its end (a mid-loop exit would make the compiler assume gathers
+  // still in flight at the loop head and wait for all of them there); the
+  // last one or two chunks are consumed after it. SPARSE rows run segment by
+  // segment (the pipeline drains at each refill).
+  for (;;) {
+    int vs = 0, ve = send - sbeg;
+    if constexpr (SPARSE) {
+      refill();
+      vs = vseg0;
+      ve = lend;
+    }
+    const int nch = uniform((ve - vs + 15) >> 4);
+    const int ntrip = uniform(nch / 3);
+    Chunk A, B, C;
+    load(A, vs, ve);
+    load(B, vs + 16, ve);
+    int v = vs;
+#pragma unroll 1
+    for (int it = 0; it < ntrip; ++it, v += 48) {
+      load(C, v + 32, ve);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, v);
+      load(A, v + 48, ve);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B, v + 16);
+      load(B, v + 64, ve);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(C, v + 32);
+    }
+    const int rem = nch - 3 * ntrip;
+    if (rem >= 1) compute(A, v);
+    if (rem >= 2) compute(B, v + 16);
+    if (!SPARSE || spos >= send) break;
   }
 
   const float l_tot = xor32_sum(xor16_sum(l_part));
   if (n >= G) return;
   const int head = g * G + n;
+  // oacc[bk][i] is dim 8(4gq + i) + bk: eight consecutive dims per i.
   if (P.splits == 1) {
     const float inv = 1.f / l_tot;
-    uint16_t* op = P.o + (qrow * P.Hq + head) * kHeadDim;
+    uint16_t* op = P.o + (qrow * P.Hq + head) * kHeadDim + 32 * gq;
 #pragma unroll
-    for (int bk = 0; bk < 8; ++bk) {
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[bk][0] * inv, oacc[bk][1] * inv);
-      w[1] = pack_bf16x2(oacc[bk][2] * inv, oacc[bk][3] * inv);
-      *reinterpret_cast<u32x2*>(op + 16 * bk + 4 * gq) = w;
+    for (int i = 0; i < 4; ++i) {
+      u32x4 w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = pack_bf16x2(oacc[2 * c][i] * inv, oacc[2 * c + 1][i] * inv);
+      st16(op + 8 * i, w);
     }
     if (P.lse && gq == 0) P.lse[((int64_t)b * P.Hq + head) * P.n_q + t] = m_run * kLn2 + __logf(l_tot);
   } else {
     float* pp = P.part + ((((int64_t)b * P.Hkv + g) * P.splits + split) * G + n) * (kHeadDim + 2);
 #pragma unroll
-    for (int bk = 0; bk < 8; ++bk)
-      *reinterpret_cast<f32x4*>(pp + 16 * bk + 4 * gq) = oacc[bk];
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f32x4*>(pp + 32 * gq + 8 * i) = f32x4{oacc[0][i], oacc[1][i], oacc[2][i], oacc[3][i]};
+      *reinterpret_cast<f32x4*>(pp + 32 * gq + 8 * i + 4) = f32x4{oacc[4][i], oacc[5][i], oacc[6][i], oacc[7][i]};
+    }
     if (gq == 0) {
       pp[kHeadDim] = m_run;
       pp[kHeadDim + 1] = l_tot;
