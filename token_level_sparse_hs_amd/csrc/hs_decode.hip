@@ -55,7 +55,8 @@ struct Chunk {
   int nv;       // wave-uniform: keys 0..nv-1 of the chunk are real, the rest masked
 };
 
-template <int G, bool SPARSE>
+// SIGMA (full rows only): also write the group score row of the candidates.
+template <int G, bool SPARSE, bool SIGMA>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t Kt_all[4][16 * kKS16];
   __shared__ __attribute__((aligned(16))) uint32_t klist_all[4][SPARSE ? kList + kListPad : 4];
@@ -125,8 +126,17 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   float m_run = kNegInf, l_part = 0.f;
   const float cexp = P.scale * kLog2e;
   const int cand_end = lim;  // last candidate position (FULL score row)
-  float* sig_row = nullptr;
-  if (!SPARSE && P.sigma) sig_row = P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride;
+  // Score row: the group maxima of a chunk reach every lane n < G of group
+  // gq; the chunk in slot c (0..2) of a triple is kept by lanes n == c, so
+  // after a triple lanes (n < 3, gq) hold keys 16n + 4gq .. +3 of its 48
+  // keys, written by one 192-byte store. Pieces past the candidates or the
+  // split aim past the buffer's range (the hardware drops them), so the
+  // store is unconditional. A piece that starts at a candidate may run into
+  // the window or the row padding (sigma_stride is a multiple of 64 and at
+  // least the longest row): entries the selection never reads.
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc_sized(SIGMA ? P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride : nullptr,
+                      SIGMA ? 4u * (uint32_t)P.sigma_stride : 0u);
 
   // SPARSE list state (wave-uniform): klist[0 .. cnt) holds the offsets of
   // virtual keys vseg0 .. vseg0 + cnt - 1; keys below lend are published to
@@ -200,7 +210,14 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   };
 
   // Attention update with the chunk starting at virtual key v.
-  auto compute = [&](const Chunk& ch, int v) {
+  f32x4 sig_keep = {};
+  const int sig_last = imin(cand_end, send - 1);  // last key this split may write
+  auto sig_flush = [&](int v) {
+    const int j = sbeg + v + 16 * n + 4 * gq;
+    const uint32_t soff = (n < 3 && j <= sig_last) ? 4u * (uint32_t)j : kDropOffset;
+    buf_st16(srs, soff, __builtin_bit_cast(u32x4, sig_keep));
+  };
+  auto compute = [&](const Chunk& ch, int v, int slot) {
     // K rows into the per-wave LDS tile (row-major, key 4gq + r)
 #pragma unroll
     for (int r = 0; r < 4; ++r) st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
@@ -215,19 +232,11 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
       for (int i = 0; i < 4; ++i)
         if (4 * gq + i >= ch.nv) acc[i] = kNegInf;
     }
-    if (!SPARSE && sig_row && sbeg + v <= cand_end) {
-      f32x4 mxh;
+    if constexpr (SIGMA) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
-      const int j = sbeg + v + 4 * gq;
-      if (n == 0) {
-        if (j + 3 <= cand_end && ((j & 3) == 0)) {
-          *reinterpret_cast<f32x4*>(sig_row + j) = mxh;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (j + i <= cand_end) sig_row[j + i] = mxh[i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float mx4 = group_max<G>(acc[i]) * P.scale;
+        sig_keep[i] = n == slot ? mx4 : sig_keep[i];
       }
     }
     // online softmax
@@ -296,17 +305,21 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     for (int it = 0; it < ntrip; ++it, v += 48) {
       load(C, v + 32, ve);
       __builtin_amdgcn_sched_barrier(0);
-      compute(A, v);
+      compute(A, v, 0);
       load(A, v + 48, ve);
       __builtin_amdgcn_sched_barrier(0);
-      compute(B, v + 16);
+      compute(B, v + 16, 1);
       load(B, v + 64, ve);
       __builtin_amdgcn_sched_barrier(0);
-      compute(C, v + 32);
+      compute(C, v + 32, 2);
+      if constexpr (SIGMA) sig_flush(v);
     }
     const int rem = nch - 3 * ntrip;
-    if (rem >= 1) compute(A, v);
-    if (rem >= 2) compute(B, v + 16);
+    if (rem >= 1) compute(A, v, 0);
+    if (rem >= 2) compute(B, v + 16, 1);
+    if constexpr (SIGMA) {
+      if (rem >= 1) sig_flush(v);  // slots beyond rem lie past the split: dropped
+    }
     if (!SPARSE || spos >= send) break;
   }
 
@@ -413,7 +426,10 @@ template <int G, bool SPARSE>
 hipError_t launch_gather_g(const DecodeParams& p, hipStream_t s) {
   const int64_t blocks = p.seq_lens ? ((int64_t)p.B * p.Hkv * p.splits + 3) / 4
                                     : (((int64_t)p.B * p.n_q + 3) / 4) * p.Hkv;
-  flash_gather_kernel<G, SPARSE><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  if (!SPARSE && p.sigma)
+    flash_gather_kernel<G, false, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  else
+    flash_gather_kernel<G, SPARSE, false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }
 
