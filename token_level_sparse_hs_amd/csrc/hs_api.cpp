@@ -120,7 +120,8 @@ struct PrefillPlan {
   int stride = 1;
   int max_samples = 0;
   bool sample = false;
-  size_t off_theta = 0, off_counts = 0, off_bs = 0, off_bj = 0, off_samples = 0, off_stat = 0, total = 0;
+  size_t off_theta = 0, off_counts = 0, off_bs = 0, off_bj = 0, off_samples = 0, off_stat = 0, off_defer = 0,
+         total = 0;
 };
 
 PrefillPlan plan_prefill(const hs_shape* s) {
@@ -145,6 +146,8 @@ PrefillPlan plan_prefill(const hs_shape* s) {
   o = align_up(o + (size_t)p.rows * p.max_samples * 4);
   p.off_stat = o;
   o = align_up(o + 4);
+  p.off_defer = o;  // queued rows of the selection, then their count
+  o = align_up(o + (size_t)p.rows * 4 + 4);
   p.total = o;
   return p;
 }
@@ -370,6 +373,7 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
     tp.window = s->window; tp.cap = plan.cap; tp.stride = plan.stride; tp.max_samples = plan.max_samples;
     tp.samples = reinterpret_cast<const float*>(w + plan.off_samples);
     tp.theta = theta;
+    tp.defer_count = reinterpret_cast<uint32_t*>(w + plan.off_defer + (size_t)plan.rows * 4);
     HIP_TRY(timed("threshold", hst, [&] { return hs::launch_threshold(tp, plan.rows, hst); }));
   }
 
@@ -398,6 +402,8 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
     sp.force_rescan = (s->flags & HS_FLAG_EXACT_RESCAN) ? 1 : 0;
     sp.idx = idx;
     sp.rescan_count = nullptr;
+    sp.defer_rows = reinterpret_cast<int32_t*>(w + plan.off_defer);
+    sp.defer_count = reinterpret_cast<uint32_t*>(w + plan.off_defer + (size_t)plan.rows * 4);
     HIP_TRY(timed("select_prefill", hst, [&] { return hs::launch_select_prefill(sp, plan.rows, hst); }));
   }
   return ok();

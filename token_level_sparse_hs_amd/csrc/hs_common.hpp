@@ -128,14 +128,18 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff, 0x00020000);
 }
+__device__ __forceinline__ uint32_t buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
-// Buffer over [base, base + bytes): a 16-byte store at an offset at or past
-// `bytes` is discarded by the hardware range check, so lanes that must not
-// write still execute the store (no divergent branch around it).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_sized(void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+// Buffer over [base, base + bytes): a store at an offset at or past `bytes`
+// is discarded and a load there returns 0 (hardware range check), so lanes
+// that must not access memory still execute the instruction (no divergent
+// branch around it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_sized(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);

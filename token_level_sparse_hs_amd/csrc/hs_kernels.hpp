@@ -55,10 +55,13 @@ struct SelectParams {
   int force_rescan;
   int32_t* idx;            // [rows][top_k]
   uint32_t* rescan_count;  // optional counter of rows that took the rescan
+  int32_t* defer_rows;     // [rows] rows left to the block-wide path
+  uint32_t* defer_count;   // zeroed by the threshold kernel of the same call
 };
 
 struct ThresholdParams {
   int B, n_q, n_kv, Hkv, top_k, window, cap, stride, max_samples;
+  uint32_t* defer_count;  // zeroed here (block 0) for the selection that follows
   const float* samples;
   float* theta;
 };

@@ -35,6 +35,8 @@
 //            dot products (slow, exact; the fallback and the testing path).
 //   threshold mode: the m-th largest of a dense row of sampled scores (the
 //            per-row filter threshold used by the prefill attention kernel).
+#include <algorithm>
+
 #include "hs_common.hpp"
 #include "hs_kernels.hpp"
 
@@ -411,13 +413,176 @@ struct SelLds {
   int32_t idx[BIG ? kRegCap : 1];
 };
 
-// Top-k over the candidate buffer of each (b, t, g) row of a prefill call.
+// ---------------------------------------------------------------- wave path
+
+// Wave-level radix search over lane-strided register keys (0 = empty) for the
+// element of rank `rank` (1-based, largest first). The bits above the highest
+// bit in which the keys differ are decided up front (scores in one row share
+// sign and leading exponent bits), then 8-bit digits follow from there; the
+// search stops early once a whole bucket is needed. Keys sit at slot e of
+// lane l for element 64e + l < n. `hist` is this wave's LDS histogram in
+// kHistCopies copies (lane l counts into copy l % copies: scores cluster in
+// few digits, and LDS atomics from many lanes to one address serialise),
+// each with 256 digit bins and one dump slot per lane of the copy for the
+// keys outside the current prefix, so every lane adds unconditionally (a
+// wave's LDS operations execute in order).
+constexpr int kHistCopies = 8;
+constexpr int kHistStride = 256 + 64 / kHistCopies;  // words per copy: bins + dump slots
+
+template <int E>
+__device__ RadixResult wave_radix(uint32_t* hist, const uint32_t (&key)[E], int n, uint32_t rank) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kmax = key[e] > kmax ? key[e] : kmax;
+    kmin = (key[e] && key[e] < kmin) ? key[e] : kmin;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)kmax, o, 64), c = (uint32_t)__shfl_xor((int)kmin, o, 64);
+    kmax = a > kmax ? a : kmax;
+    kmin = c < kmin ? c : kmin;
+  }
+  kmax = (uint32_t)uniform((int)kmax);
+  kmin = (uint32_t)uniform((int)kmin);
+  RadixResult r{kmax, 0xffffffffu, rank, false};
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0u) return r;  // every key equal: the first `rank` in index order
+  int hi = 31 - __builtin_clz(diff);
+  r.mask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+  r.prefix = kmax & r.mask;
+  uint32_t* my = hist + (lane % kHistCopies) * kHistStride;
+#pragma unroll 1
+  while (hi >= 0) {
+    const int shift = imax(hi - 7, 0);
+    const uint32_t dmask = (2u << (hi - shift)) - 1u;
+    for (int i = lane; i < kHistCopies * kHistStride / 4; i += 64)
+      reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
+    // key in the current prefix <=> key - prefix <= lim = 2^(hi+1) - 1; its
+    // digit is then (key - prefix) >> shift. Anything else (empty slots
+    // included, prefix being nonzero) goes to the dump bin.
+    const uint32_t lim = hi == 31 ? 0xffffffffu : (2u << hi) - 1u;
+    const uint32_t dump = 256u + (uint32_t)(lane / kHistCopies);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (64 * e < n) {  // wave-uniform: slots past the row are skipped
+        const uint32_t d = key[e] - r.prefix;
+        atomicAdd(&my[(key[e] != 0u && d <= lim) ? d >> shift : dump], 1u);
+      }
+    }
+    // lane l owns digits 255 - 4l - q (descending): bins 252 - 4l .. 255 - 4l
+    u32x4 cv = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int cp = 0; cp < kHistCopies; ++cp) cv += *reinterpret_cast<const u32x4*>(hist + cp * kHistStride + 252 - 4 * lane);
+    const uint32_t c[4] = {cv[3], cv[2], cv[1], cv[0]};
+    const int local = (int)(c[0] + c[1] + c[2] + c[3]);
+    const int incl = wave_incl_scan(local);
+    const uint64_t hit = ballot((uint32_t)incl >= r.need);
+    const int L = __builtin_ctzll(hit);  // first lane reaching the rank
+    uint32_t acc = (uint32_t)(incl - local), dsel = 0u, gt = 0u, eq = 0u;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && acc + c[q] >= r.need) {
+        found = true;
+        dsel = 255u - 4u * (uint32_t)lane - (uint32_t)q;
+        gt = acc;
+        eq = c[q];
+      }
+      acc += c[q];
+    }
+    dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, L);
+    gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+    eq = (uint32_t)__builtin_amdgcn_readlane((int)eq, L);
+    r.prefix |= dsel << shift;
+    r.mask |= dmask << shift;
+    r.need -= gt;
+    if (eq == r.need) {
+      r.take_all = true;
+      break;
+    }
+    hi = shift - 1;
+  }
+  return r;
+}
+
+constexpr int kWaveE = 80;  // candidates per lane of the wave path (rows of up to 5120)
+
+// One wave per (b, t, g) row: the candidate buffer is read lane-strided
+// (coalesced) into registers, the k-th key is found by wave_radix, and the
+// selection is written in ascending token order with one ballot per
+// register slot (ties at the k-th key are taken in token order). Rows the
+// wave path cannot take (forced rescan, a count outside [k, cap], or more
+// candidates than it holds) are queued for the block-wide path.
+__global__ __launch_bounds__(256, 3) void select_prefill_wave_kernel(SelectParams P, int64_t rows) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kHistCopies * kHistStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = uniform((int)blockIdx.x * 4 + wave);  // rows < 2^31
+  if (row >= rows) return;
+  const int64_t bt = row / P.Hkv;
+  const int t = (int)(bt % P.n_q);
+  const int p = P.n_kv - P.n_q + t;
+  const int ncand = imax(0, p - P.window + 1);
+  const int k = P.top_k;
+  int32_t* out = P.idx + row * k;
+  if (ncand <= k) {
+    // reading: fewer candidates than k -> all of C(p), then -1 padding
+    for (int i = lane; i < k; i += 64) out[i] = i < ncand ? i : -1;
+    return;
+  }
+  const int cnt = uniform(P.counts[row]);
+  if (P.force_rescan || cnt < k || cnt > P.cap || cnt > 64 * kWaveE) {
+    if (lane == 0) P.defer_rows[atomicAdd(P.defer_count, 1u)] = (int32_t)row;
+    return;
+  }
+  // loads past the row's count return 0 (buffer range check), so no clamping
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc_sized(P.buf_sigma + row * (int64_t)P.cap, 4u * (uint32_t)cnt);
+  const __amdgpu_buffer_rsrc_t rs_j = make_rsrc_sized(P.buf_j + row * (int64_t)P.cap, 4u * (uint32_t)cnt);
+  // selected indices: stores of unselected lanes aim past the row (dropped)
+  const __amdgpu_buffer_rsrc_t rs_o = make_rsrc_sized(out, 4u * (uint32_t)k);
+  if (cnt == k) {
+    for (int i = lane; i < k; i += 64) out[i] = P.buf_j[row * (int64_t)P.cap + i];
+    return;
+  }
+  uint32_t key[kWaveE];
+#pragma unroll
+  for (int e = 0; e < kWaveE; ++e) key[e] = buf_ld4(rs_s, 4u * (uint32_t)lane + 256u * (uint32_t)e);
+#pragma unroll
+  for (int e = 0; e < kWaveE; ++e) key[e] = 64 * e + lane < cnt ? score_key(__uint_as_float(key[e])) : 0u;
+  const RadixResult r = wave_radix<kWaveE>(hist_all[wave], key, cnt, (uint32_t)k);
+  uint32_t out_run = 0, eq_run = 0;
+  constexpr int kGroup = 8;  // index loads in flight per step (bounds register use)
+#pragma unroll
+  for (int e0 = 0; e0 < kWaveE; e0 += kGroup) {
+    if (64 * e0 >= cnt) continue;  // (not break: the loop stays fully unrolled)
+    uint32_t j[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) j[u] = buf_ld4(rs_j, 4u * (uint32_t)lane + 256u * (uint32_t)(e0 + u));
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const uint32_t kk = key[e0 + u];
+      const uint32_t km = kk & r.mask;
+      const bool gt = kk != 0u && km > r.prefix;
+      const bool eq = kk != 0u && km == r.prefix;
+      const uint64_t eqm = ballot(eq);
+      const uint32_t eq_before = eq_run + lane_prefix(eqm);
+      eq_run += (uint32_t)__popcll(eqm);
+      const bool sel = gt || (eq && (r.take_all || eq_before < r.need));
+      const uint64_t selm = ballot(sel);
+      buf_st4(rs_o, sel ? 4u * (out_run + lane_prefix(selm)) : kDropOffset, j[u]);
+      out_run += (uint32_t)__popcll(selm);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Block-wide top-k of one (b, t, g) row of a prefill call (the rows the wave
+// path queued): buffer path when the candidate count proves the buffer holds
+// the top k, exact rescan otherwise.
 template <bool BIG>
-__global__ __launch_bounds__(kSelThreads) void select_prefill_kernel(SelectParams P) {
-  __shared__ SelShared sh;
-  __shared__ SelLds<BIG> lds;
-  __shared__ float qs[8 * kHeadDim];
-  const int64_t row = blockIdx.x;
+__device__ void select_prefill_row(const SelectParams& P, int64_t row, SelShared& sh, SelLds<BIG>& lds, float* qs) {
   const int g = (int)(row % P.Hkv);
   const int64_t bt = row / P.Hkv;
   const int t = (int)(bt % P.n_q);
@@ -426,7 +591,6 @@ __global__ __launch_bounds__(kSelThreads) void select_prefill_kernel(SelectParam
   const int ncand = imax(0, p - P.window + 1);
   int32_t* out = P.idx + row * P.top_k;
   if (ncand <= P.top_k) {
-    // reading: fewer candidates than k -> all of C(p), then -1 padding
     for (int i = threadIdx.x; i < P.top_k; i += kSelThreads) out[i] = i < ncand ? i : -1;
     return;
   }
@@ -454,20 +618,36 @@ __global__ __launch_bounds__(kSelThreads) void select_prefill_kernel(SelectParam
   if (threadIdx.x == 0 && P.rescan_count) atomicAdd(P.rescan_count, 1u);
 }
 
+// Persistent blocks over the queued rows.
+template <bool BIG>
+__global__ __launch_bounds__(kSelThreads) void select_prefill_deferred_kernel(SelectParams P) {
+  __shared__ SelShared sh;
+  __shared__ SelLds<BIG> lds;
+  __shared__ float qs[8 * kHeadDim];
+  const uint32_t n = *reinterpret_cast<volatile const uint32_t*>(P.defer_count);
+  for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
+    select_prefill_row<BIG>(P, P.defer_rows[li], sh, lds, qs);
+    __syncthreads();
+  }
+}
+
 // Per-row filter threshold from sampled scores: theta = the m-th largest valid
 // sample, with m chosen so that, for exchangeable scores, the full candidate
 // set holds at least top_k scores >= theta except with negligible
 // probability (mean + 6 standard deviations of the sampled count above the
-// true k-th score, plus one). Rows whose candidates all fit the buffer get
-// theta = -inf.
+// true k-th score, plus one). Rows whose candidates all fit the buffer (and
+// the wave selection path, when samples exist) get theta = -inf.
 __global__ __launch_bounds__(kSelThreads) void threshold_kernel(ThresholdParams P) {
   __shared__ SelShared sh;
   const int64_t row = blockIdx.x;
+  if (row == 0 && threadIdx.x == 0 && P.defer_count) *P.defer_count = 0u;
   const int64_t bt = row / P.Hkv;
   const int t = (int)(bt % P.n_q);
   const int p = P.n_kv - P.n_q + t;
   const int ncand = imax(0, p - P.window + 1);
-  if (ncand <= P.cap) {
+  // Whole rows go to the buffer when they fit it and, if samples exist, also
+  // fit the wave selection path; longer rows get a sampled threshold.
+  if (ncand <= P.cap && (P.max_samples == 0 || ncand <= 64 * kWaveE)) {
     if (threadIdx.x == 0) P.theta[row] = kNegInf;
     return;
   }
@@ -494,6 +674,41 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(ThresholdParams 
   }
 }
 
+// The same threshold with one wave per row, for calls whose rows hold at
+// most 64 * kWaveE samples (lane-strided register keys, wave_radix).
+__global__ __launch_bounds__(256, 2) void threshold_wave_kernel(ThresholdParams P, int64_t rows) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kHistCopies * kHistStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = uniform((int)blockIdx.x * 4 + wave);  // rows < 2^31
+  if (row >= rows) return;
+  if (row == 0 && lane == 0 && P.defer_count) *P.defer_count = 0u;
+  const int64_t bt = row / P.Hkv;
+  const int t = (int)(bt % P.n_q);
+  const int p = P.n_kv - P.n_q + t;
+  const int ncand = imax(0, p - P.window + 1);
+  if (ncand <= P.cap && (P.max_samples == 0 || ncand <= 64 * kWaveE)) {
+    if (lane == 0) P.theta[row] = kNegInf;
+    return;
+  }
+  const int nsamp = (ncand + P.stride - 1) / P.stride;
+  const double mu = (double)nsamp * (double)P.top_k / (double)ncand;
+  const int m = (int)ceil(mu + 6.0 * sqrt(mu)) + 1;
+  if (m > nsamp) {
+    if (lane == 0) P.theta[row] = kNegInf;
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(P.samples + row * (int64_t)P.max_samples, 4u * (uint32_t)nsamp);
+  uint32_t key[kWaveE];
+#pragma unroll
+  for (int e = 0; e < kWaveE; ++e) key[e] = buf_ld4(rs, 4u * (uint32_t)lane + 256u * (uint32_t)e);
+#pragma unroll
+  for (int e = 0; e < kWaveE; ++e) key[e] = 64 * e + lane < nsamp ? score_key(__uint_as_float(key[e])) : 0u;
+  const RadixResult r = wave_radix<kWaveE>(hist_all[wave], key, nsamp, (uint32_t)m);
+  // take_all leaves the low bits open: prefix is then a lower bound
+  if (lane == 0) P.theta[row] = key_to_score(r.prefix);
+}
+
 // Decode: top-k over the dense score row of each (b, g).
 __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecodeParams P) {
   __shared__ SelShared sh;
@@ -512,14 +727,21 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecode
 }
 
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s) {
+  select_prefill_wave_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)std::min<int64_t>(rows, 1024);
   if (p.cap > kRegCap)
-    select_prefill_kernel<true><<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+    select_prefill_deferred_kernel<true><<<dim3(grid), dim3(kSelThreads), 0, s>>>(p);
   else
-    select_prefill_kernel<false><<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+    select_prefill_deferred_kernel<false><<<dim3(grid), dim3(kSelThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_threshold(const ThresholdParams& p, int64_t rows, hipStream_t s) {
-  threshold_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+  if (p.max_samples <= 64 * kWaveE)
+    threshold_wave_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
+  else
+    threshold_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_select_decode(const SelectDecodeParams& p, int rows, hipStream_t s) {
