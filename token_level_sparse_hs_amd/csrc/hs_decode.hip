@@ -39,6 +39,7 @@ namespace {
 constexpr int kKS16 = 136;  // per-wave K tile row stride in bf16 (272 B: 16-B reads of 16 rows hit distinct banks)
 constexpr int kList = 2048;     // staged key offsets per wave (SPARSE)
 constexpr int kListPad = 64;    // zero tail read by the chunks issued past the end
+constexpr int kSigStage = 2048; // score-row keys staged per wave (FULL segment length)
 
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -60,6 +61,7 @@ template <int G, bool SPARSE, bool SIGMA>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t Kt_all[4][16 * kKS16];
   __shared__ __attribute__((aligned(16))) uint32_t klist_all[4][SPARSE ? kList + kListPad : 4];
+  __shared__ __attribute__((aligned(16))) float sig_all[4][SIGMA ? kSigStage : 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int n = lane & 15, gq = lane >> 4;
@@ -126,17 +128,14 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   float m_run = kNegInf, l_part = 0.f;
   const float cexp = P.scale * kLog2e;
   const int cand_end = lim;  // last candidate position (FULL score row)
-  // Score row: the group maxima of a chunk reach every lane n < G of group
-  // gq; the chunk in slot c (0..2) of a triple is kept by lanes n == c, so
-  // after a triple lanes (n < 3, gq) hold keys 16n + 4gq .. +3 of its 48
-  // keys, written by one 192-byte store. Pieces past the candidates or the
-  // split aim past the buffer's range (the hardware drops them), so the
-  // store is unconditional. A piece that starts at a candidate may run into
-  // the window or the row padding (sigma_stride is a multiple of 64 and at
-  // least the longest row): entries the selection never reads.
-  const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc_sized(SIGMA ? P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride : nullptr,
-                      SIGMA ? 4u * (uint32_t)P.sigma_stride : 0u);
+  // Score row: the group maxima of each chunk are staged in the wave's LDS
+  // segment buffer and written out once the segment's gathers are done: a
+  // store among the gathers would hold up every later wait on them (vector
+  // memory operations retire in order). 16-byte pieces are written when they
+  // start at a candidate of this split; such a piece may run into the window
+  // or the row padding (sigma_stride is a multiple of 64 and at least the
+  // longest row): entries the selection never reads.
+  float* const sig_row = SIGMA ? P.sigma + ((int64_t)b * P.Hkv + g) * P.sigma_stride : nullptr;
 
   // SPARSE list state (wave-uniform): klist[0 .. cnt) holds the offsets of
   // virtual keys vseg0 .. vseg0 + cnt - 1; keys below lend are published to
@@ -210,14 +209,17 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   };
 
   // Attention update with the chunk starting at virtual key v.
-  f32x4 sig_keep = {};
-  const int sig_last = imin(cand_end, send - 1);  // last key this split may write
-  auto sig_flush = [&](int v) {
-    const int j = sbeg + v + 16 * n + 4 * gq;
-    const uint32_t soff = (n < 3 && j <= sig_last) ? 4u * (uint32_t)j : kDropOffset;
-    buf_st16(srs, soff, __builtin_bit_cast(u32x4, sig_keep));
+  float* const sig_stage = sig_all[wave];
+  const int sig_last = imin(cand_end, send - 1);  // last key this split may start a piece at
+  int sig_v0 = 0;                                 // first key of the staged segment
+  // Writes the staged scores of keys [sig_v0, ve) (relative to sbeg).
+  auto sig_flush = [&](int ve) {
+    for (int i = 4 * lane; i < ve - sig_v0; i += 256) {
+      const int j = sbeg + sig_v0 + i;
+      if (j <= sig_last) *reinterpret_cast<f32x4*>(sig_row + j) = *reinterpret_cast<const f32x4*>(&sig_stage[i]);
+    }
   };
-  auto compute = [&](const Chunk& ch, int v, int slot) {
+  auto compute = [&](const Chunk& ch, int v) {
     // K rows into the per-wave LDS tile (row-major, key 4gq + r)
 #pragma unroll
     for (int r = 0; r < 4; ++r) st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
@@ -233,11 +235,10 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
         if (4 * gq + i >= ch.nv) acc[i] = kNegInf;
     }
     if constexpr (SIGMA) {
+      f32x4 mxh;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mx4 = group_max<G>(acc[i]) * P.scale;
-        sig_keep[i] = n == slot ? mx4 : sig_keep[i];
-      }
+      for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
+      if (n == 0) *reinterpret_cast<f32x4*>(&sig_stage[v - sig_v0 + 4 * gq]) = mxh;
     }
     // online softmax
     float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
@@ -294,6 +295,9 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
       refill();
       vs = vseg0;
       ve = lend;
+    } else if constexpr (SIGMA) {
+      vs = sig_v0;
+      ve = imin(send - sbeg, sig_v0 + kSigStage);
     }
     const int nch = uniform((ve - vs + 15) >> 4);
     const int ntrip = uniform(nch / 3);
@@ -305,22 +309,26 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     for (int it = 0; it < ntrip; ++it, v += 48) {
       load(C, v + 32, ve);
       __builtin_amdgcn_sched_barrier(0);
-      compute(A, v, 0);
+      compute(A, v);
       load(A, v + 48, ve);
       __builtin_amdgcn_sched_barrier(0);
-      compute(B, v + 16, 1);
+      compute(B, v + 16);
       load(B, v + 64, ve);
       __builtin_amdgcn_sched_barrier(0);
-      compute(C, v + 32, 2);
-      if constexpr (SIGMA) sig_flush(v);
+      compute(C, v + 32);
     }
     const int rem = nch - 3 * ntrip;
-    if (rem >= 1) compute(A, v, 0);
-    if (rem >= 2) compute(B, v + 16, 1);
-    if constexpr (SIGMA) {
-      if (rem >= 1) sig_flush(v);  // slots beyond rem lie past the split: dropped
+    if (rem >= 1) compute(A, v);
+    if (rem >= 2) compute(B, v + 16);
+    if constexpr (SPARSE) {
+      if (spos >= send) break;
+    } else if constexpr (SIGMA) {
+      sig_flush(ve);
+      sig_v0 = ve;
+      if (sig_v0 >= send - sbeg) break;
+    } else {
+      break;
     }
-    if (!SPARSE || spos >= send) break;
   }
 
   const float l_tot = xor32_sum(xor16_sum(l_part));

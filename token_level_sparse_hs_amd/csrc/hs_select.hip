@@ -336,18 +336,25 @@ __device__ bool topk_filtered(SelShared& sh, uint32_t* lkey, int32_t* lidx, cons
   constexpr int kRegion = kRegCap / kSelWaves;
   const int q0 = (int)(((int64_t)n * wave) / kSelWaves), q1 = (int)(((int64_t)n * (wave + 1)) / kSelWaves);
   uint32_t cnt = 0;
-  for (int i0 = q0; i0 < q1; i0 += 64) {
-    const int i = i0 + lane;
-    uint32_t kk = 0;
-    if (i < q1) kk = src.key(i);
-    const bool pass = i < q1 && kk >= theta;
-    const uint64_t bm = ballot(pass);
-    const uint32_t pos = cnt + lane_prefix(bm);
-    if (pass && pos < (uint32_t)kRegion) {
-      lkey[wave * kRegion + pos] = kk;
-      lidx[wave * kRegion + pos] = src.index(i);
+  // kFilterBatch loads in flight per lane: a long row is read at memory
+  // throughput rather than one latency per 64 elements
+  constexpr int kFilterBatch = 16;
+  for (int i0 = q0; i0 < q1; i0 += 64 * kFilterBatch) {
+    uint32_t kb[kFilterBatch];
+#pragma unroll
+    for (int u = 0; u < kFilterBatch; ++u) kb[u] = src.key(imin(i0 + 64 * u + lane, q1 - 1));  // clamped
+#pragma unroll
+    for (int u = 0; u < kFilterBatch; ++u) {
+      const int i = i0 + 64 * u + lane;
+      const bool pass = i < q1 && kb[u] >= theta;
+      const uint64_t bm = ballot(pass);
+      const uint32_t pos = cnt + lane_prefix(bm);
+      if (pass && pos < (uint32_t)kRegion) {
+        lkey[wave * kRegion + pos] = kb[u];
+        lidx[wave * kRegion + pos] = src.index(i);
+      }
+      cnt += (uint32_t)__popcll(bm);
     }
-    cnt += (uint32_t)__popcll(bm);
   }
   if (lane == 0) sh.cnt[wave] = cnt;
   __syncthreads();
