@@ -30,6 +30,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+L1_FILL_GBS = 256 * 64 * 2.4  # 256 CUs x 64 B/clk x 2.4 GHz: vector-memory fill rate of the CUs
+# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by a copy
+# kernel's reading); kept with the profile summaries and refreshed by hand.
+TRAFFIC = {}
 
 
 def log(*a):
@@ -177,10 +181,12 @@ def cpu_baseline(args, w, case, torch):
             orc.sparse_attention_rows(x[rows], K, V, res["idx"], pos, w.window, scale)
         return time.perf_counter() - t0
 
-    # rows spread evenly over the chunk so the mean context matches the workload
-    probe = [w.n_q // 2]
-    t_one = rows_time(probe)
-    R = int(max(4, min(256, args.cpu_seconds / max(t_one, 1e-3))))
+    # rows spread evenly over the chunk so the mean context matches the
+    # workload; a small evenly spaced calibration sample sizes the timed one
+    rows_time([w.n_q // 2])  # first-call warm-up
+    calib = sorted(set(int(x) for x in np.linspace(0, w.n_q - 1, 8)))
+    t_row = rows_time(calib) / len(calib)
+    R = int(max(8, min(2048, args.cpu_seconds / max(t_row, 1e-4))))
     rows = sorted(set(int(x) for x in np.linspace(0, w.n_q - 1, R)))
     t = rows_time(rows)
     return {"value": round(len(rows) / t, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
@@ -223,16 +229,23 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "prefill_attn",
                 "flops_per_launch": counts["full_flops"], "avg_us": round(pa_us, 1)}
     else:
+        # The sparse-reuse layer is a dense matrix-core contraction over
+        # gathered rows; it is priced against the bf16 matrix peak with its
+        # algorithmic FLOPs. The gathered bytes are reported beside it: the
+        # 67 MB cache of this workload stays resident in the 256 MB last-level
+        # cache, so the gather rate is measured against the CUs' L1 fill rate
+        # (256 CUs x 64 B/clk x 2.4 GHz), not HBM.
         n_d, t_d = kt[dom]
         us = t_d / n_d * 1e3
+        fl = counts["sparse_flops_per_layer"]
+        achieved = fl / (us * 1e-6) / 1e12
         byts = counts["sparse_bytes_per_layer"]
-        achieved = byts / (us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
-                "bytes_per_launch": byts, "avg_us": round(us, 1),
-                "note": "algorithmic gather bytes (selected + window rows x 512 B per KV head, idx, q/o); the "
-                        "67 MB cache of this workload stays resident in the 256 MB last-level cache and L2 "
-                        "serves about half of the requests, so the rate can exceed the HBM peak"}
+        gb = byts / (us * 1e-6) / 1e9
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": TRAFFIC.get(dom), "kernel": dom,
+                "flops_per_launch": fl, "avg_us": round(us, 1),
+                "gather": {"achieved_GBs": round(gb, 1), "bytes_per_launch": byts,
+                           "l1_fill_peak_GBs": L1_FILL_GBS, "frac": round(gb / L1_FILL_GBS, 4)}}
     kernels = {k: {"launches_per_step": n / args.steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()}
     full_ach = counts["full_flops"] / (pa_us * 1e-6) / 1e12
     roof_full = {"bound": "mfma", "achieved": round(full_ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
