@@ -31,9 +31,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 L1_FILL_GBS = 256 * 64 * 2.4  # 256 CUs x 64 B/clk x 2.4 GHz: vector-memory fill rate of the CUs
-# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by a copy
-# kernel's reading); kept with the profile summaries and refreshed by hand.
-TRAFFIC = {}
+# Bytes per launch past L2 from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
+# a calibration copy's reading (bench.py --traffic-probe); taken for the
+# current kernels and refreshed by hand whenever they change.
+TRAFFIC = {"sparse_prefill": 1.127e10, "prefill_attn": 6.38e9}
 
 
 def log(*a):
@@ -94,6 +95,24 @@ def run_prefill(args, hs, synth, _lib, torch):
     for k, (n, tot) in sorted(kt.items(), key=lambda x: -x[1][1]):
         log(f"[bench]   {k:16s} launches={n:5d} avg={tot / n * 1e3:10.1f} us  share/step={tot / args.steps:8.3f} ms")
     return w, ms_per_step, kt, case
+
+
+def traffic_probe(args, hs, synth, _lib, torch):
+    """For HBM counter runs (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE): one
+    prefill block, then a plain elementwise copy of known size (reads and
+    writes 1 GiB) whose counter reading calibrates bytes per counter unit."""
+    w = synth.WORKLOADS[args.workload]
+    case = synth.make_prefill_case(w, "cuda:0", sparse_layers=1)
+    q, kv, qs = case["q_full"], case["kv"], case["q_sparse"][0]
+    o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window)
+    hs.sparse_attn_reuse(qs, kv, idx, top_k=w.top_k, window=w.window, n_kv=w.n_kv)
+    torch.cuda.synchronize()
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    y = x * 1.0  # one elementwise kernel: 1 GiB read, 1 GiB written
+    torch.cuda.synchronize()
+    log(f"[bench] traffic probe done: copy {x.numel() * 4} bytes read and written")
+    del y
 
 
 def run_decode(args, hs, synth, _lib, torch):
@@ -204,6 +223,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="one prefill block and a 1 GiB calibration copy, for HBM counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the hot path is single-GPU by design); --gpus {args.gpus} "
@@ -214,6 +235,9 @@ def main():
     import token_level_sparse_hs_amd as hs
     from token_level_sparse_hs_amd import _lib, synth
     _lib.load()
+    if args.traffic_probe:
+        traffic_probe(args, hs, synth, _lib, torch)
+        return
 
     w, ms_step, kt, case = run_prefill(args, hs, synth, _lib, torch)
     counts = prefill_counts(w)
@@ -226,7 +250,8 @@ def main():
     if dom == "prefill_attn":
         achieved = counts["full_flops"] / (pa_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "prefill_attn",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": TRAFFIC.get("prefill_attn"),
+                "kernel": "prefill_attn",
                 "flops_per_launch": counts["full_flops"], "avg_us": round(pa_us, 1)}
     else:
         # The sparse-reuse layer is a dense matrix-core contraction over
