@@ -59,18 +59,23 @@ struct Chunk {
 // SIGMA (full rows only): also write the group score row of the candidates.
 template <int G, bool SPARSE, bool SIGMA>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t Kt_all[4][16 * kKS16];
-  __shared__ __attribute__((aligned(16))) uint32_t klist_all[4][SPARSE ? kList + kListPad : 4];
+  // Per-wave K tiles and key lists; in prefill SPARSE mode the block's
+  // shared window tiles alias this region before the lists are built.
+  constexpr int kKtBytes = 16 * kKS16 * 2;
+  constexpr int kListBytes = (SPARSE ? kList + kListPad : 4) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[4 * (kKtBytes + kListBytes)];
   __shared__ __attribute__((aligned(16))) float sig_all[4][SIGMA ? kSigStage : 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int n = lane & 15, gq = lane >> 4;
-  uint16_t* Kt = Kt_all[wave];
-  uint32_t* klist = klist_all[wave];
+  uint16_t* Kt = reinterpret_cast<uint16_t*>(lds_raw + wave * kKtBytes);
+  uint32_t* klist = reinterpret_cast<uint32_t*>(lds_raw + 4 * kKtBytes + wave * kListBytes);
 
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
   const bool decode = P.seq_lens != nullptr;
   int b, t, g, split, p;
+  bool row_ok = true, win_shared = false;  // prefill: row exists; window gathered by the block
+  int b0 = 0, t0 = 0;
   if (decode) {
     const int64_t total = (int64_t)P.B * P.Hkv * P.splits;
     if (item >= total) return;
@@ -89,10 +94,16 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     split = 0;
     g = (int)(blockIdx.x % P.Hkv);
     const int64_t bt = (int64_t)(blockIdx.x / P.Hkv) * 4 + wave;
-    if (bt >= (int64_t)P.B * P.n_q) return;
-    t = (int)(bt % P.n_q);
-    b = (int)(bt / P.n_q);
+    row_ok = bt < (int64_t)P.B * P.n_q;  // rows past the end join the block's shared phase only
+    const int64_t btc = row_ok ? bt : (int64_t)P.B * P.n_q - 1;
+    t = (int)(btc % P.n_q);
+    b = (int)(btc / P.n_q);
     p = P.n_kv - P.n_q + t;
+    // the block's first row: the rows of its batch entry share one window
+    const int64_t bt0 = (int64_t)(blockIdx.x / P.Hkv) * 4;
+    b0 = (int)(bt0 / P.n_q);
+    t0 = (int)(bt0 % P.n_q);
+    win_shared = SPARSE && row_ok && b == b0;
   }
   const int64_t qrow = (int64_t)b * P.n_q + t;  // decode: n_q == 1
 
@@ -105,10 +116,10 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   const int k = SPARSE ? P.top_k : 0;
   const int w0 = imax(0, p - P.window + 1);
   const int lim = p - P.window;  // last selectable token
-  const int ns = SPARSE ? k + (p - w0 + 1) : p + 1;
+  const int ns = SPARSE ? k + (win_shared ? 0 : p - w0 + 1) : p + 1;
   const int sbeg = uniform(split * P.split_len);
   const int send = uniform(imin(ns, sbeg + P.split_len));
-  if (sbeg >= send) return;  // split beyond this row: the combine skips it
+  if (decode && sbeg >= send) return;  // split beyond this row: the combine skips it
 
   // Query operand: column n = head g*G + n (n < G), dims 32s + 8*gq .. +8.
   bf16x8 qb[4];
@@ -219,28 +230,10 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
       if (j <= sig_last) *reinterpret_cast<f32x4*>(sig_row + j) = *reinterpret_cast<const f32x4*>(&sig_stage[i]);
     }
   };
-  auto compute = [&](const Chunk& ch, int v) {
-    // K rows into the per-wave LDS tile (row-major, key 4gq + r)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
-    lds_wait();
-    // S^T = K Q^T: A operand lane (n, gq) = K[key n][32s + 8gq .. +8]
-    f32x4 acc = {};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(ld16(&Kt[n * kKS16 + 32 * s + 8 * gq])), qb[s], acc);
-    // lane holds query column n, chunk keys 4*gq + i: the keys it gathered
-    if (ch.nv < 16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * gq + i >= ch.nv) acc[i] = kNegInf;
-    }
-    if constexpr (SIGMA) {
-      f32x4 mxh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
-      if (n == 0) *reinterpret_cast<f32x4*>(&sig_stage[v - sig_v0 + 4 * gq]) = mxh;
-    }
-    // online softmax
+  // Online-softmax update and O^T += V^T P^T for one 16-key chunk: acc holds
+  // its raw dot products (masked keys at -inf) as S^T (lane: query column n,
+  // keys 4gq + i), vw its V rows (keys 4gq + r, dims 8n..8n+7).
+  auto finish = [&](f32x4 acc, const u32x4* vw) __attribute__((always_inline)) {
     float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     mx = xor32_max(xor16_max(mx));
     // Deferred rescaling: the reference maximum moves only when a score
@@ -275,11 +268,115 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     for (int bk = 0; bk < 8; ++bk) {
       const uint32_t sel2 = (bk & 1) ? 0x07060302u : 0x05040100u;
       u32x2 a;
-      a[0] = __builtin_amdgcn_perm(ch.vw[1][bk >> 1], ch.vw[0][bk >> 1], sel2);
-      a[1] = __builtin_amdgcn_perm(ch.vw[3][bk >> 1], ch.vw[2][bk >> 1], sel2);
+      a[0] = __builtin_amdgcn_perm(vw[1][bk >> 1], vw[0][bk >> 1], sel2);
+      a[1] = __builtin_amdgcn_perm(vw[3][bk >> 1], vw[2][bk >> 1], sel2);
       oacc[bk] = mfma16x16x16(a, pb, oacc[bk]);
     }
   };
+  auto compute = [&](const Chunk& ch, int v) __attribute__((always_inline)) {
+    // K rows into the per-wave LDS tile (row-major, key 4gq + r)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
+    lds_wait();
+    // S^T = K Q^T: A operand lane (n, gq) = K[key n][32s + 8gq .. +8]
+    f32x4 acc = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(ld16(&Kt[n * kKS16 + 32 * s + 8 * gq])), qb[s], acc);
+    // lane holds query column n, chunk keys 4*gq + i: the keys it gathered
+    if (ch.nv < 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * gq + i >= ch.nv) acc[i] = kNegInf;
+    }
+    if constexpr (SIGMA) {
+      f32x4 mxh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
+      if (n == 0) *reinterpret_cast<f32x4*>(&sig_stage[v - sig_v0 + 4 * gq]) = mxh;
+    }
+    finish(acc, ch.vw);
+  };
+
+  // Prefill: the forced windows of the block's rows (consecutive tokens of
+  // one batch entry and KV group) overlap in all but a few keys, so the four
+  // waves gather their union once, in 32-key tiles loaded straight into LDS
+  // (buffer_load ... lds; three buffers, two tiles in flight, one barrier
+  // per tile), and each wave scores its own window from there; the selected
+  // keys follow, gathered per wave. K rows sit with their 16-byte chunks
+  // permuted (chunk c of row r at c ^ (r % 16)) so that the score operand
+  // reads of 16 rows hit distinct banks.
+  if constexpr (SPARSE) {
+    if (!decode) {
+      constexpr int kWinKeys = 32;
+      constexpr int kWinTile = 2 * kWinKeys * 256;  // K then V, 256-byte rows
+      static_assert(3 * kWinTile <= 4 * (kKtBytes + kListBytes), "window tiles exceed the aliased LDS");
+      const int t_last = imin(t0 + 3, P.n_q - 1);
+      const int off = P.n_kv - P.n_q;
+      const int lo = imax(0, off + t0 - P.window + 1), hi = off + t_last;
+      const int ntw = uniform((hi - lo + kWinKeys) / kWinKeys);
+      const __amdgpu_buffer_rsrc_t krs0 = make_rsrc(P.kv.slab(uniform(b0), g));
+      const __amdgpu_buffer_rsrc_t vrs0 = make_rsrc(P.kv.slab(uniform(b0), g) + P.kv.voff);
+      typedef __attribute__((address_space(3))) void lds_void;
+      // wave w loads tile rows 8w + 4h + l/16 (h = 0, 1), 16 bytes each lane
+      auto fetch = [&](int j) __attribute__((always_inline)) {
+        uint8_t* tb = lds_raw + (j % 3) * kWinTile;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r0 = 8 * wave + 4 * h;
+          const int row = r0 + (lane >> 4);
+          const int key = imin(lo + j * kWinKeys + row, hi);  // past the union: clamped, masked
+          const uint32_t base = (uint32_t)key * rowb;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs0, (lds_void*)(tb + r0 * 256), 16,
+                                                   base + 16u * (uint32_t)(n ^ (row & 15)), 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs0, (lds_void*)(tb + kWinKeys * 256 + r0 * 256), 16,
+                                                   base + 16u * (uint32_t)n, 0, 0, 0);
+        }
+      };
+      fetch(0);
+      if (ntw > 1) {
+        fetch(1);
+        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): tile 0 landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int j = 0; j < ntw; ++j) {
+        if (j + 2 < ntw) fetch(j + 2);  // into tile j-1's buffer, free since the last barrier
+        if (win_shared) {
+          const uint8_t* tb = lds_raw + (j % 3) * kWinTile;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int kb = lo + j * kWinKeys + 16 * c;  // first key of the chunk
+            if (kb > p || kb + 15 < w0) continue;       // wave-uniform
+            f32x4 acc = {};
+            const uint8_t* krow = tb + (16 * c + n) * 256;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+              acc = mfma16x16x32(as_bf16x8(ld16(krow + 16 * ((4 * s2 + gq) ^ n))), qb[s2], acc);
+            if (kb < w0 || kb + 15 > p) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int jk = kb + 4 * gq + i;
+                if (jk < w0 || jk > p) acc[i] = kNegInf;
+              }
+            }
+            u32x4 vw[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vw[r] = ld16(tb + kWinKeys * 256 + (16 * c + 4 * gq + r) * 256 + 16 * n);
+            finish(acc, vw);
+          }
+        }
+        // tile j+1 landed (the loads of tile j+2, if any, may still fly)
+        if (j + 2 < ntw)
+          __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+      }
+    }
+    if (!row_ok) return;
+  }
 
   // Three chunks in flight: chunks are issued two ahead of the one consumed
   // (unconditionally: past the end they are masked and read row 0), and
