@@ -104,7 +104,14 @@ def test_workspace_sizes(lib):
     assert _lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, s) == 0
     s = base_shape(n_q=1)
     assert _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s, 0) == 0
-    assert _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s, 64) > 0
+    # decode sparse: one split per row needs no merge buffer; a long row split
+    # over many waves does; a batch of 256 (b, g) rows merges inside blocks
+    assert _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s, 64) == 0
+    s_long = base_shape(n_q=1, n_kv=0, kv_capacity=1 << 17, top_k=2048, window=512)
+    assert _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s_long, 1 << 17) > 0
+    s_batch = base_shape(batch=64, n_q=1, n_kv=0, kv_capacity=1 << 17, q_heads=32, kv_heads=4, top_k=2048,
+                         window=512)
+    assert _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s_batch, 1 << 17) == 0
     assert _lib.workspace_size(_lib.HS_OP_DECODE_STEP, s, 64) > 0
     with pytest.raises(_lib.HsError):
         _lib.workspace_size(_lib.HS_OP_DECODE_STEP, s, 0)

@@ -88,3 +88,13 @@ def test_decode_long_rows_filtered_select():
 def test_decode_streaming_select():
     """k close to the row length defeats the sample filter: streaming select."""
     run_decode([9000], 1, 4, 1, 8000, 16, seed=14, n_sparse=1)
+
+
+def test_decode_batch_block_merge():
+    """256 (b, g) rows: each sparse row is split over the four waves of one
+    block, which merge their partials in LDS. Short rows leave splits with no
+    kept key (all idx entries padding) or no source position at all."""
+    rng = np.random.default_rng(15)
+    lengths = [1, 5, 30, 63, 64, 65, 200, 319, 320, 321, 1000, 2500]
+    lengths += [int(x) for x in rng.integers(1, 2500, size=64 - len(lengths))]
+    run_decode(lengths, 1, 32, 4, 256, 64, seed=15, n_sparse=1)

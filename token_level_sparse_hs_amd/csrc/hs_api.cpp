@@ -154,6 +154,7 @@ PrefillPlan plan_prefill(const hs_shape* s) {
 
 struct DecodePlan {
   int splits = 1, split_len = 32;
+  bool in_block = false;  // sparse decode: splits merged inside the block
   int64_t sigma_stride = 0;
   size_t off_sigma = 0, off_part = 0, total = 0;
 };
@@ -188,13 +189,32 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   return p;
 }
 
+// SIMDs of the chip (256 CUs x 4): the sparse decode grid is sized in these.
+constexpr int64_t kChipSimds = 1024;
+
+// Sparse decode: each (b, g) row gathers top_k + W keys. When the batch has
+// at least a quarter as many rows as the chip has SIMDs, every row is split
+// four ways over the waves of one block, which merge their partials in LDS
+// (no workspace, no merge kernel); the split-per-wave grid then holds at
+// least one long-running wave per SIMD, which measured faster than more,
+// shorter waves (the per-wave start-up is paid once per 640 keys at
+// decode64). Smaller batches split finer for about one wave per SIMD and
+// merge in a separate kernel.
 DecodePlan plan_decode_sparse(const hs_shape* s) {
   DecodePlan p;
   const int G = s->q_heads / s->kv_heads;
   const int64_t bg = (int64_t)s->batch * s->kv_heads;
-  plan_splits(bg, (int64_t)s->top_k + s->window, &p.splits, &p.split_len);
+  const int64_t ns = (int64_t)s->top_k + s->window;
+  if (bg * 4 >= kChipSimds) {
+    p.in_block = true;
+    p.splits = 4;
+    p.split_len = (int)round_up((ns + 3) / 4, 32);
+    p.total = 0;
+    return p;
+  }
+  plan_splits(bg, ns, &p.splits, &p.split_len, kChipSimds);
   p.off_part = 0;
-  p.total = align_up((size_t)bg * p.splits * G * (128 + 2) * 4);
+  p.total = p.splits > 1 ? align_up((size_t)bg * p.splits * G * (128 + 2) * 4) : 0;
   return p;
 }
 
@@ -426,7 +446,7 @@ hs_status hs_sparse_attn_reuse(const hs_shape* s, const void* q, const void* kv,
   DecodePlan plan;
   if (decode) {
     plan = plan_decode_sparse(s);
-    if (!ws || ws_bytes < plan.total)
+    if (plan.total > 0 && (!ws || ws_bytes < plan.total))
       return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, ws_bytes);
     if (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) return fail(HS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   }
@@ -446,14 +466,15 @@ hs_status hs_sparse_attn_reuse(const hs_shape* s, const void* q, const void* kv,
   if (decode) {
     dp.splits = plan.splits;
     dp.split_len = plan.split_len;
-    dp.part = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_part);
-    if (plan.splits == 1) dp.part = nullptr;
+    dp.combine_in_block = plan.in_block ? 1 : 0;
+    dp.part = plan.in_block || plan.splits == 1 ? nullptr
+                                                : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_part);
   } else {
     dp.splits = 1;
     dp.split_len = s->top_k + s->window + 32;
   }
   HIP_TRY(timed(decode ? "sparse_decode" : "sparse_prefill", hst, [&] { return hs::launch_sparse(dp, hst); }));
-  if (decode && plan.splits > 1) {
+  if (decode && plan.splits > 1 && !plan.in_block) {
     hs::CombineParams cp{};
     cp.part = dp.part; cp.o = dp.o; cp.lse = nullptr; cp.seq_lens = seq_lens;
     cp.B = s->batch; cp.Hq = s->q_heads; cp.Hkv = s->kv_heads; cp.splits = plan.splits; cp.split_len = plan.split_len;

@@ -12,23 +12,26 @@
 // are merged by the log-sum-exp correction ("Simplified Sparse Attention via
 // Gist Tokens", section 3.6, three-kernel split-K decode).
 //
-// Design (MI355X): one wave per work item (row or split), so thousands of
-// independent waves keep enough 16-byte gathers in flight to cover HBM
-// latency; no block-level synchronisation.
-//  * A work item walks a virtual key list in chunks of 32 keys. FULL: keys
-//    [k0, k1) of a decode row. SPARSE: the idx row (entries < 0 are padding)
-//    followed by the window Win(p).
-//  * K and V rows are gathered 4 keys x 8 dims per lane, so consecutive
+// Design (MI355X): one wave per work item (a query row, or a split of a
+// decode row), so thousands of independent waves keep enough 16-byte gathers
+// in flight to cover memory latency.
+//  * A work item walks a virtual key list in chunks of 16 keys, three chunks
+//    in flight. FULL: keys [k0, k1) of a decode row. SPARSE: the idx row
+//    (entries < 0 are padding) followed by the window Win(p), compacted into
+//    a per-wave LDS list of byte offsets.
+//  * Each lane gathers 16 bytes of four K and four V rows, so consecutive
 //    lanes read consecutive bytes of a row (full cache lines, one address
 //    quad per row segment: the texture addresser, not the memory, was the
-//    limit with operand-shaped gathers), and staged in row-major per-wave LDS
-//    tiles. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 reads its A operand from
-//    the K tile; the G query heads of the group occupy MFMA columns 0..G-1,
-//    so one K/V row read serves all heads. V is read back transposed
-//    (ds_read_b64_tr_b16) as the A operand of O^T = V^T P^T on
-//    v_mfma_f32_16x16x16_bf16; P^T is already in B-operand layout.
+//    limit with operand-shaped gathers). K goes through a per-wave LDS tile
+//    into S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the G query heads of the
+//    group in MFMA columns 0..G-1, so one K/V row read serves all heads.
+//    V never leaves the lane: O^T = V^T P^T on v_mfma_f32_16x16x16_bf16 runs
+//    with the head dimension permuted, and P^T already is the B operand.
 //  * Softmax state is per lane (query column = lane%16) with two cross-lane
 //    exchanges (lane^16, lane^32) per chunk; accumulation is fp32.
+//  * Block-level cooperation only where rows share data: in prefill the four
+//    rows of a block gather their common forced window once; in decode the
+//    four splits of one row may merge their partials in LDS.
 #include "hs_common.hpp"
 #include "hs_kernels.hpp"
 
@@ -119,7 +122,10 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   const int ns = SPARSE ? k + (win_shared ? 0 : p - w0 + 1) : p + 1;
   const int sbeg = uniform(split * P.split_len);
   const int send = uniform(imin(ns, sbeg + P.split_len));
-  if (decode && sbeg >= send) return;  // split beyond this row: the combine skips it
+  // A split beyond this row: the global merge skips it; a block merge needs
+  // the wave at its barrier, contributing an empty partial (m = -inf, l = 0).
+  const bool empty = sbeg >= send;
+  if (decode && empty && !P.combine_in_block) return;
 
   // Query operand: column n = head g*G + n (n < G), dims 32s + 8*gq .. +8.
   bf16x8 qb[4];
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   // still in flight at the loop head and wait for all of them there); the
   // last one or two chunks are consumed after it. SPARSE rows run segment by
   // segment (the pipeline drains at each refill).
-  for (;;) {
+  if (!empty) for (;;) {
     int vs = 0, ve = send - sbeg;
     if constexpr (SPARSE) {
       refill();
@@ -429,6 +435,57 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   }
 
   const float l_tot = xor32_sum(xor16_sum(l_part));
+  if (decode && P.combine_in_block) {
+    // The block's waves are splits 0..3 of one (b, g) row. Each wave leaves
+    // its partial (acc[G][128], m, l) in its own K tile, then thread
+    // (head hn, dims 4c..4c+3) merges the four: M = max m_s,
+    // o = sum 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s.
+    constexpr int kPartStride = kHeadDim + 4;  // floats per head; 16-byte aligned rows
+    static_assert(G * kPartStride * 4 <= kKtBytes, "block-merge partials exceed the K tile");
+    float* mine = reinterpret_cast<float*>(Kt);
+    if (n < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* d = mine + n * kPartStride + 32 * gq + 8 * i;
+        *reinterpret_cast<f32x4*>(d) = f32x4{oacc[0][i], oacc[1][i], oacc[2][i], oacc[3][i]};
+        *reinterpret_cast<f32x4*>(d + 4) = f32x4{oacc[4][i], oacc[5][i], oacc[6][i], oacc[7][i]};
+      }
+      if (gq == 0) {
+        mine[n * kPartStride + kHeadDim] = m_run;
+        mine[n * kPartStride + kHeadDim + 1] = l_tot;
+      }
+    }
+    __syncthreads();
+    if (tid >= G * 32) return;
+    const int hn = tid >> 5, d0 = 4 * (tid & 31);
+    float ms[4], ls[4];
+    f32x4 av[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const float* src = reinterpret_cast<const float*>(lds_raw + s2 * kKtBytes) + hn * kPartStride;
+      ms[s2] = src[kHeadDim];
+      ls[s2] = src[kHeadDim + 1];
+      av[s2] = *reinterpret_cast<const f32x4*>(src + d0);
+    }
+    const float M = fmaxf(fmaxf(ms[0], ms[1]), fmaxf(ms[2], ms[3]));
+    const float Mu = M == kNegInf ? 0.f : M;
+    float lsum = 0.f;
+    f32x4 o4 = {};
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const float w = __builtin_amdgcn_exp2f(ms[s2] - Mu);  // empty split: 0
+      lsum += w * ls[s2];
+      o4 += w * av[s2];
+    }
+    const float inv = 1.f / lsum;
+    const int head = g * G + hn;
+    u32x2 ow;
+    ow[0] = pack_bf16x2(o4[0] * inv, o4[1] * inv);
+    ow[1] = pack_bf16x2(o4[2] * inv, o4[3] * inv);
+    *reinterpret_cast<u32x2*>(P.o + (qrow * P.Hq + head) * kHeadDim + d0) = ow;
+    if (P.lse && (tid & 31) == 0) P.lse[((int64_t)b * P.Hq + head) * P.n_q + t] = Mu * kLn2 + __logf(lsum);
+    return;
+  }
   if (n >= G) return;
   const int head = g * G + n;
   // oacc[bk][i] is dim 8(4gq + i) + bk: eight consecutive dims per i.

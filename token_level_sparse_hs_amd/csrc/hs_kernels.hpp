@@ -93,7 +93,9 @@ struct DecodeParams {
   // outputs
   uint16_t* o;              // used when splits == 1
   float* lse;               // [B][Hq][n_q] or null (splits == 1)
-  float* part;              // splits > 1: [B][Hkv][splits][G][128 + 2]
+  float* part;              // splits > 1 (global merge): [B][Hkv][splits][G][128 + 2]
+  int combine_in_block;     // decode, splits == 4: a block's four waves are the four
+                            // splits of one (b, g) row and merge in LDS (part unused)
   float* sigma;             // FULL: [B*Hkv][sigma_stride]
   int64_t sigma_stride;
 };
