@@ -81,6 +81,8 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppRowRor4 = 0x124;    // lane i <- lane (i+4) mod 16 within 16
+constexpr int kDppRowRor8 = 0x128;    // lane i <- lane (i+8) mod 16 within 16
 
 // With NaN-free, non-IEEE-mode compilation (see the build flags) a DPP move
 // feeding a max folds into a single v_max_f32_dpp.
@@ -100,6 +102,14 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 // Combine lane l with lane l^32 (max / sum).
+// Transposing max across lane rows: with rows of 16 lanes, returns
+// max(a[l], a[l ^ 16]) in even rows and max(b[l], b[l ^ 16]) in odd rows
+// (one v_permlane16_swap and one max for two values).
+__device__ __forceinline__ float row_pair_max(float a, float b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float xor32_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

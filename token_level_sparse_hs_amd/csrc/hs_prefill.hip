@@ -12,8 +12,9 @@
 //  * One 256-thread block = 4 waves = one KV group g and 4*(32/G) query
 //    tokens. Each wave owns 32 MFMA rows = 32/G tokens x the G query heads of
 //    group g, so the group's heads share every K/V tile staged in LDS and the
-//    group maximum over heads (the selection score) is a reduction over G
-//    adjacent lanes.
+//    group maximum over heads (the selection score) is a reduction across
+//    lanes: heads sit 32/G lanes apart, so its first step swaps lane rows
+//    (v_permlane16_swap) and halves the values each lane carries.
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: with the key
 //    axis on MFMA rows and the query rows on lanes, every per-row softmax
 //    quantity (running max, sum, rescale) is lane-local apart from one
@@ -100,35 +101,98 @@ __device__ __forceinline__ void qk_tile(const uint16_t* Ks, const bf16x8* qb, f3
   }
 }
 
-// Loads this lane's query operand: row n = l%32 of the wave (token n/G, head
-// g*G + n%G), dims 16s + 8h .. +8 for s = 0..7.
+// MFMA row n (= lane % 32) of a wave stands for token tok_of(n) of the
+// wave's 32/G tokens and head g*G + head_of(n). Each 16-lane row of the wave
+// holds 16/G tokens, and a token's G heads sit 16/G lanes apart inside one
+// row, so the group maximum runs on DPP within rows.
+template <int G>
+__device__ __forceinline__ int tok_of(int n) {
+  constexpr int TR = 16 / (G > 16 ? 16 : G);
+  return (n >> 4) * TR + (n & 15) % TR;
+}
+template <int G>
+__device__ __forceinline__ int head_of(int n) {
+  constexpr int TR = 16 / (G > 16 ? 16 : G);
+  return (n & 15) / TR;
+}
+
+// Loads this lane's query operand: row n = l%32 of the wave (token
+// tok_of(n), head g*G + head_of(n)), dims 16s + 8h .. +8 for s = 0..7.
 template <int G>
 __device__ __forceinline__ void load_q(const uint16_t* q, int b, int n_q, int Hq, int g, int tok, bf16x8* qb) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, n = lane & 31;
   const bool ok = tok < n_q;
-  const int head = g * G + (n % G);
+  const int head = g * G + head_of<G>(n);
   const uint16_t* qp = q + (((int64_t)b * n_q + (ok ? tok : 0)) * Hq + head) * kHeadDim + 8 * h;
 #pragma unroll
   for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(ok ? ld16(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u});
 }
 
+// dst = max(src[partner], src) in the lanes of the DPP banks (4-lane groups
+// of a row) named by BANKS; the other lanes of dst keep their value. Row
+// rotations: ror:8 pairs lane i with i^8; ror:4 feeds lane i from i-4,
+// ror:12 from i+4. The first form defines dst, the second updates it.
+#define HS_DPP_MAX_DEF(dst, src, ROR, BANKS, dep)                                                        \
+  asm volatile("v_max_f32_dpp %0, %1, %1 row_ror:" #ROR " row_mask:0xf bank_mask:" #BANKS : "=v"(dst) \
+               : "v"(src), "v"(dep))
+#define HS_DPP_MAX_UPD(dst, src, ROR, BANKS, dep)                                                        \
+  asm volatile("v_max_f32_dpp %0, %1, %1 row_ror:" #ROR " row_mask:0xf bank_mask:" #BANKS : "+v"(dst) \
+               : "v"(src), "v"(dep))
+
 // Writes the group-max scores of the wave's tile into sig[TPW][64] (raw,
-// unscaled). Lanes with n%G == 0 hold each token's maxima.
+// unscaled). acc[c][i] holds key 32c + 8(i/4) + 4h + i%4 of MFMA row n.
+// Transposing steps halve the values each lane carries instead of
+// reducing all 32 in every lane: across lane^8 (banks 0-1 keep the keys of
+// acc[0], banks 2-3 those of acc[1]), then across lane^4 (even banks keep
+// i < 8, odd banks i >= 8), then a plain step across lane^2 for G = 8. `dep`
+// is any value computed after the last use of acc by ordinary code (the
+// DPP sources must not be read before the matrix results have landed).
 template <int G>
-__device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig) {
+__device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig, float dep) {
   const int lane = threadIdx.x & 63;
-  const int h = lane >> 5, n = lane & 31;
-  float* row = sig + (n / G) * 64;
+  const int h = lane >> 5, q = lane & 15;
+  if constexpr (G == 1) {
+    float* row = sig + (lane & 31) * 64;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 v;
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(row + 32 * c + 8 * q4 + 4 * h) =
+            f32x4{acc[c][4 * q4], acc[c][4 * q4 + 1], acc[c][4 * q4 + 2], acc[c][4 * q4 + 3]};
+  } else {
+    const int c = (q >> 3) & 1;
+    float r[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = group_max<G>(acc[c][4 * q4 + i]);
-      if (n % G == 0) *reinterpret_cast<f32x4*>(row + 32 * c + 8 * q4 + 4 * h) = v;
+    for (int i = 0; i < 16; ++i) {
+      HS_DPP_MAX_DEF(r[i], acc[1][i], 8, 0xc, dep);
+      HS_DPP_MAX_UPD(r[i], acc[0][i], 8, 0x3, dep);
     }
+    float* trow = sig + tok_of<G>(lane & 31) * 64 + 32 * c + 4 * h;
+    if constexpr (G == 2) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(trow + 8 * q4) = f32x4{r[4 * q4], r[4 * q4 + 1], r[4 * q4 + 2], r[4 * q4 + 3]};
+    } else {
+      const int ih = (q >> 2) & 1;
+      float r2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        HS_DPP_MAX_DEF(r2[i], r[8 + i], 4, 0xa, dep);
+        HS_DPP_MAX_UPD(r2[i], r[i], 12, 0x5, dep);
+      }
+      if constexpr (G == 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r2[i] = fmaxf(r2[i], dpp<kDppXor2>(r2[i]));
+      }
+      f32x4 v0 = {r2[0], r2[1], r2[2], r2[3]}, v1 = {r2[4], r2[5], r2[6], r2[7]};
+      asm volatile("" : "+v"(v0), "+v"(v1));  // computed by all lanes before the writer branch
+      if (G == 4 || (q & 2) == 0) {
+        *reinterpret_cast<f32x4*>(trow + 16 * ih) = v0;
+        *reinterpret_cast<f32x4*>(trow + 16 * ih + 8) = v1;
+      }
+    }
+  }
 }
 
 template <int G>
@@ -152,9 +216,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   const int off = P.n_kv - P.n_q;
 
   const int wt0 = t0 + wave * TPW;
-  const int tok = wt0 + n / G;
+  const int tok = wt0 + tok_of<G>(n);
   const bool tok_ok = tok < P.n_q;
-  const int head = g * G + (n % G);
+  const int head = g * G + head_of<G>(n);
   const int p_lane = tok_ok ? off + tok : -1;
   const int p_wlo = off + wt0;
   const int p_whi = off + imin(wt0 + TPW, P.n_q) - 1;
@@ -163,17 +227,19 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   bf16x8 qb[8];
   load_q<G>(P.q, b, P.n_q, P.Hq, g, tok, qb);
 
+  // Selection state of the wave's tokens, all wave-uniform (scalar
+  // registers): threshold, last selectable key (-1: none) and count.
+  // Row (b, wt0 + u, g) is row0 + u * Hkv.
+  const int64_t row0 = ((int64_t)b * P.n_q + wt0) * P.Hkv + g;
   float theta[TPW];
-  int cnt[TPW];
-  float* bs_row[TPW];
-  int32_t* bj_row[TPW];
+  int lim[TPW], cnt[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tk = wt0 + u;
-    const int64_t row = ((int64_t)b * P.n_q + tk) * P.Hkv + g;
-    theta[u] = (P.select && tk < P.n_q) ? P.theta[row] : kNegInf;
-    bs_row[u] = P.buf_sigma + row * P.cap;
-    bj_row[u] = P.buf_j + row * P.cap;
+    const bool ok = P.select && tk < P.n_q;
+    theta[u] = ok ? __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, P.theta[row0 + (int64_t)u * P.Hkv])))
+                  : kNegInf;
+    lim[u] = ok ? off + tk - P.window : -1;
     cnt[u] = 0;
   }
 
@@ -209,27 +275,6 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
             if (j > p_lane) acc[c][i] = kNegInf;
           }
       }
-      if (P.select && key0 <= p_whi - P.window) {
-        float* ws = sig[wave];
-        stage_group_max<G>(acc, ws);
-        lds_wait();
-        const int j = key0 + lane;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const int tk = wt0 + u;
-          const float v = ws[u * 64 + lane] * P.scale;
-          const bool pass = tk < P.n_q && j <= off + tk - P.window && v >= theta[u];
-          const uint64_t m = ballot(pass);
-          if (m) {
-            const int pos = cnt[u] + (int)lane_prefix(m);
-            if (pass && pos < P.cap) {
-              bs_row[u][pos] = v;
-              bj_row[u][pos] = j;
-            }
-            cnt[u] += __popcll(m);
-          }
-        }
-      }
       // online softmax (exp2 domain); O is rescaled only when some row's
       // running maximum moved
       float mx = kNegInf;
@@ -237,6 +282,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[c][i]);
+      // Selection, part 1: the group maxima of the tile's candidate keys go
+      // to the wave's LDS rows now, while the raw scores are still in place.
+      const bool sel_tile = P.select && key0 <= p_whi - P.window;
+      if (sel_tile) stage_group_max<G>(acc, sig[wave], mx);
       mx = xor32_max(mx);
       // deferred rescaling (see the gather kernel): P <= 2^kRescaleLog2
       const float m_cand = mx * cexp;
@@ -285,6 +334,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s2], oacc[bk]);
         }
       }
+      // Selection, part 2, once the PV products are issued (it does not
+      // depend on them, so it overlaps the matrix pipe): every candidate key
+      // whose score reaches the row's threshold is appended, in ascending key
+      // order, to the row's buffer.
+      if (sel_tile) {
+        const float* ws = sig[wave];
+        const int j = key0 + lane;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const float v = ws[u * 64 + lane] * P.scale;
+          const bool pass = j <= lim[u] && v >= theta[u];
+          const uint64_t m = ballot(pass);
+          if (m) {
+            const int pos = cnt[u] + (int)lane_prefix(m);
+            if (pass && pos < P.cap) {
+              const int64_t e = (row0 + (int64_t)u * P.Hkv) * P.cap + pos;
+              P.buf_sigma[e] = v;
+              P.buf_j[e] = j;
+            }
+            cnt[u] = uniform(cnt[u] + __popcll(m));
+          }
+        }
+      }
     }
   }
 
@@ -305,10 +377,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   }
   if (P.select && lane == 0) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int tk = wt0 + u;
-      if (tk < P.n_q) P.counts[((int64_t)b * P.n_q + tk) * P.Hkv + g] = cnt[u];
-    }
+    for (int u = 0; u < TPW; ++u)
+      if (wt0 + u < P.n_q) P.counts[row0 + (int64_t)u * P.Hkv] = cnt[u];
   }
 }
 
@@ -333,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
   const int t0 = (ntq - 1 - L) * TPB;
   const int off = P.n_kv - P.n_q;
   const int wt0 = t0 + wave * TPW;
-  const int tok = wt0 + n / G;
+  const int tok = wt0 + tok_of<G>(n);
 
   bf16x8 qb[8];
   load_q<G>(P.q, b, P.n_q, P.Hq, g, tok, qb);
@@ -364,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
       f32x16 acc[2];
       qk_tile(Ks, qb, acc);
       float* ws = sig[wave];
-      stage_group_max<G>(acc, ws);
+      stage_group_max<G>(acc, ws, fmaxf(acc[0][15], acc[1][15]));
       lds_wait();
       const int s = s0 + lane;
 #pragma unroll
