@@ -34,7 +34,7 @@ L1_FILL_GBS = 256 * 64 * 2.4  # 256 CUs x 64 B/clk x 2.4 GHz: vector-memory fill
 # Bytes per launch past L2 from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
 # a calibration copy's reading (bench.py --traffic-probe); taken for the
 # current kernels and refreshed by hand whenever they change.
-TRAFFIC = {"sparse_prefill": 1.093e+10, "prefill_attn": 6.38e9}
+TRAFFIC = {"sparse_prefill": 1.162e10, "prefill_attn": 6.405e9, "decode_full": 2.064e10, "sparse_decode": 3.39e8}
 
 
 def log(*a):
@@ -98,15 +98,31 @@ def run_prefill(args, hs, synth, _lib, torch):
 
 
 def traffic_probe(args, hs, synth, _lib, torch):
-    """For HBM counter runs (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE): one
-    prefill block, then a plain elementwise copy of known size (reads and
-    writes 1 GiB) whose counter reading calibrates bytes per counter unit."""
+    """For counter runs (rocprofv3 --pmc ...): one prefill32k full layer and
+    one sparse layer, one decode64 step (full layer, selection, three sparse
+    layers), then a plain elementwise copy of known size (reads and writes
+    1 GiB) whose counter reading calibrates bytes per counter unit."""
     w = synth.WORKLOADS[args.workload]
     case = synth.make_prefill_case(w, "cuda:0", sparse_layers=1)
     q, kv, qs = case["q_full"], case["kv"], case["q_sparse"][0]
     o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window)
     hs.sparse_attn_reuse(qs, kv, idx, top_k=w.top_k, window=w.window, n_kv=w.n_kv)
     torch.cuda.synchronize()
+    log("[bench] traffic probe: prefill layers done")
+    del case, q, kv, qs, o, lse, idx
+    wd = synth.WORKLOADS["decode64"]
+    lengths = synth.decode_lengths(wd)
+    dcase = synth.make_decode_case(wd, "cuda:0", lengths, 1, sparse_layers=3)
+    st = dcase["steps"][0]
+    seq = torch.tensor([L + 1 for L in lengths], dtype=torch.int32, device="cuda:0")
+    o, lse, idx = hs.decode_step(st["q_full"], st["kv_new"], dcase["kv"], seq, max(lengths) + 1,
+                                 top_k=wd.top_k, window=wd.window)
+    for x in st["q_sparse"]:
+        hs.sparse_attn_reuse(x, dcase["kv"], idx, top_k=wd.top_k, window=wd.window, seq_lens=seq)
+    torch.cuda.synchronize()
+    log("[bench] traffic probe: decode step done")
+    del dcase, st, o, lse, idx
+    torch.cuda.empty_cache()
     x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     torch.cuda.synchronize()
     y = x * 1.0  # one elementwise kernel: 1 GiB read, 1 GiB written
@@ -164,11 +180,11 @@ def run_decode(args, hs, synth, _lib, torch):
         "sparse_decode_roofline": {"bound": "hbm", "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": round(sp_bytes / (sp_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                                   "bytes_per_launch": sp_bytes},
+                                   "bytes_per_launch": sp_bytes, "traffic": TRAFFIC.get("sparse_decode")},
         "decode_full_roofline": {"bound": "hbm", "achieved": round(full_bytes / (df_us * 1e-6) / 1e9, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(full_bytes / (df_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                                 "bytes_per_launch": full_bytes},
+                                 "bytes_per_launch": full_bytes, "traffic": TRAFFIC.get("decode_full")},
     }
     del case, kv
     torch.cuda.empty_cache()
@@ -224,7 +240,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="one prefill block and a 1 GiB calibration copy, for HBM counter runs")
+                    help="one prefill32k full + sparse layer, one decode64 step and a 1 GiB calibration copy, for counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the hot path is single-GPU by design); --gpus {args.gpus} "

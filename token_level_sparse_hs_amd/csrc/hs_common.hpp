@@ -132,6 +132,11 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 // Marks a wave-uniform value as such (keeps it in a scalar register, so that
 // branches on it stay scalar).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Raw buffer over [base, base + 4 GiB): 16-byte loads at a 32-bit byte
 // offset with no per-lane 64-bit address arithmetic (gfx9 resource word 3).

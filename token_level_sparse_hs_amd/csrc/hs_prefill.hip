@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   // Selection state of the wave's tokens, all wave-uniform (scalar
   // registers): threshold, last selectable key (-1: none) and count.
   // Row (b, wt0 + u, g) is row0 + u * Hkv.
-  const int64_t row0 = ((int64_t)b * P.n_q + wt0) * P.Hkv + g;
+  const int64_t row0 = uniform64(((int64_t)b * P.n_q + wt0) * P.Hkv + g);
   float theta[TPW];
   int lim[TPW], cnt[TPW];
 #pragma unroll
@@ -347,12 +347,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           const bool pass = j <= lim[u] && v >= theta[u];
           const uint64_t m = ballot(pass);
           if (m) {
-            const int pos = cnt[u] + (int)lane_prefix(m);
-            if (pass && pos < P.cap) {
-              const int64_t e = (row0 + (int64_t)u * P.Hkv) * P.cap + pos;
-              P.buf_sigma[e] = v;
-              P.buf_j[e] = j;
-            }
+            // range-checked stores: lanes that fail, and positions past the
+            // buffer's capacity, aim beyond the row's range and are dropped
+            const uint32_t off = pass ? 4u * ((uint32_t)cnt[u] + lane_prefix(m)) : kDropOffset;
+            const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap;  // wave-uniform row base
+            buf_st4(make_rsrc_sized(P.buf_sigma + rb, 4u * (uint32_t)P.cap), off, __float_as_uint(v));
+            buf_st4(make_rsrc_sized(P.buf_j + rb, 4u * (uint32_t)P.cap), off, (uint32_t)j);
             cnt[u] = uniform(cnt[u] + __popcll(m));
           }
         }
