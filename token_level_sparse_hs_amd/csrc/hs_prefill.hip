@@ -32,6 +32,8 @@
 //  * Blocks run late (long) query tiles first; the group index varies
 //    fastest over blockIdx so that, with blocks dealt round-robin to the 8
 //    XCDs, each XCD's L2 serves one KV head.
+#include <type_traits>
+
 #include "hs_common.hpp"
 #include "hs_kernels.hpp"
 
@@ -39,49 +41,16 @@ namespace hs {
 
 namespace {
 
-constexpr int kKS = 136;  // K tile row stride in bf16 (272 B: conflict-free 16-B reads)
-constexpr int kVS = 144;  // V tile row stride in bf16 (288 B: row r starts at bank 8r)
+constexpr int kKS = 136;  // sampled-key tile row stride in bf16 (272 B: conflict-free 16-B reads)
+constexpr int kRowB = 256;                 // attention tiles: unpadded 256-byte rows
+constexpr int kTileB = 64 * kRowB;         // one 64-key K or V tile
+
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding; n <= 63).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-}
-
-// Global -> register part of a 64-key tile [key0, key0+64) of (b, g): thread
-// (kq = tid/16, dq = tid%16) fetches rows 4kq..4kq+3, dims 8dq..8dq+7, of K
-// and (with_v) V. Rows at or beyond `valid_end` are clamped to the last valid
-// row (finite data; every such key is masked by causality), which keeps all
-// loads unconditional.
-struct TileRegs {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-template <bool WITH_V>
-__device__ __forceinline__ void tile_fetch(const uint16_t* slab, int st, int voff, int key0, int valid_end,
-                                           TileRegs& r) {
-  const int tid = threadIdx.x;
-  const int dq = tid & 15, kq = (tid >> 4) & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = imin(key0 + 4 * kq + i, valid_end - 1);
-    const uint16_t* row = slab + (uint32_t)(j * st + 8 * dq);
-    r.k[i] = ld16(row);
-    if (WITH_V) r.v[i] = ld16(row + voff);
-  }
-}
-
-// Register -> LDS part: K and V row-major (V is read back transposed).
-template <bool WITH_V>
-__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* Ks, uint16_t* Vs) {
-  const int tid = threadIdx.x;
-  const int dq = tid & 15, kq = (tid >> 4) & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st16(&Ks[(4 * kq + i) * kKS + 8 * dq], r.k[i]);
-  if (WITH_V) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st16(&Vs[(4 * kq + i) * kVS + 8 * dq], r.v[i]);
-  }
 }
 
 // S^T tile (64 keys x 32 query rows) of this wave: acc[c][i] holds the raw
@@ -199,8 +168,12 @@ template <int G>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   constexpr int TPW = 32 / G;
   constexpr int TPB = 4 * TPW;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][64 * kVS];
+  // K and V tiles of 64 keys, two stages, unpadded 256-byte rows written by
+  // direct global->LDS loads. 16-byte chunks are XOR-permuted within a row
+  // so that both operand read patterns hit distinct banks: chunk c of K row r
+  // sits at c ^ (r % 16) (16 rows read the same chunk), chunk c of V row r at
+  // c ^ 4(r % 4) (the transpose reads take 4 rows x 64 bytes at a time).
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2][2][kTileB];
   __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -250,115 +223,173 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   const int p_bhi = off + imin(t0 + TPB, P.n_q) - 1;
   const int ntiles = p_bhi / 64 + 1;
 
-  // Tile kt+1 is fetched into registers while tile kt is consumed from LDS;
-  // one barrier per tile separates the LDS writes of tile kt+1 from the reads
-  // of tile kt-1 in the same buffer.
-  const uint16_t* slab = P.kv.slab(b, g);
-  TileRegs tr;
-  tile_fetch<true>(slab, P.kv.st, P.kv.voff, 0, P.n_kv, tr);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // Tile loads: wave w fetches tile rows 16w + 4i + lane/16 (i = 0..3) of K
+  // and of V, 16 bytes per lane, straight into LDS (lane l lands at byte 16l
+  // of a 1 KB run of 4 rows, i.e. chunk position l % 16); each lane reads the
+  // global chunk that belongs at its position. Rows past the cache's valid
+  // rows read as zeros (range-checked), and causality masks them.
+  const uint16_t* slab = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<int64_t>(P.kv.slab(b, g))));
+  const uint32_t rowb = 2u * (uint32_t)P.kv.st;
+  const uint32_t span = (uint32_t)(P.n_kv - 1) * rowb + 2u * kHeadDim;  // bytes up to the last valid row's end
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc_sized(slab, span);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc_sized(slab + P.kv.voff, span);
+  uint32_t dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t r = 16u * wave + 4u * i + (lane >> 4);
+    dk[i] = r * rowb + 16u * ((lane & 15) ^ (r & 15));
+    dv[i] = r * rowb + 16u * ((lane & 15) ^ (4u * (r & 3)));
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto fetch = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
+    const uint32_t soff = (uint32_t)uniform(kt * 64) * rowb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kv_lds[S][0][(16 * wave + 4 * i) * kRowB], 16, dk[i],
+                                               soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&kv_lds[S][1][(16 * wave + 4 * i) * kRowB], 16, dv[i],
+                                               soff, 0, 0);
+    }
+  };
+  // Operand read offsets within a tile. K (S^T = K Q^T, A operand): lane
+  // (n, h) reads dims 16s + 8h .. +8 of key n (+32 for the second MFMA block).
+  // V (O^T = V^T P^T, A operand, transpose reads): lane l reads 4 dims of key
+  // row kb + (l % 16) / 4 + 4h, dims 32bk + 16((l / 16) % 2) + 4(l % 4).
+  uint32_t kad[8], vad[4];
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) kad[s2] = n * kRowB + 16u * ((2u * s2 + h) ^ (n & 15));
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk)
+    vad[bk] = (((lane & 15) >> 2) + 4 * h) * kRowB +
+              16u * (4u * (bk ^ ((lane >> 2) & 3)) + 2u * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8u * (lane & 1);
+
+  // Candidate stores of the last tile still in flight: the wait for a tile's
+  // loads then allows that many later operations to remain outstanding
+  // (vector memory operations complete in order).
+  constexpr int kStores = 2 * TPW;
+  bool stores_pending = false;
+
+  auto tile = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
     const int key0 = kt * 64;
-    const int buf = kt & 1;
-    tile_store<true>(tr, Ks[buf], Vt[buf]);
-    __syncthreads();
-    if (kt + 1 < ntiles) tile_fetch<true>(slab, P.kv.st, P.kv.voff, key0 + 64, P.n_kv, tr);
-    __builtin_amdgcn_sched_barrier(0);
-    if (wave_live && key0 <= p_whi) {
-      f32x16 acc[2];
-      qk_tile(Ks[buf], qb, acc);
-      if (key0 + 63 > p_wlo) {
+    if (stores_pending)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStores < 63 ? kStores : 63));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // every wave's part of tile kt has landed, and every wave is done with
+    // tile kt-1, whose stage the next loads overwrite
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 1 < ntiles) fetch(kt + 1, std::integral_constant<int, 1 - S>{});
+    const bool sel_tile = P.select && wave_live && key0 <= p_whi - P.window;
+    stores_pending = sel_tile;
+    if (!(wave_live && key0 <= p_whi)) return;
+    const uint8_t* Kb = kv_lds[S][0];
+    const uint8_t* Vb = kv_lds[S][1];
+    f32x16 acc[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c) {
+      f32x16 a = {};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = key0 + 32 * c + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (j > p_lane) acc[c][i] = kNegInf;
-          }
-      }
-      // online softmax (exp2 domain); O is rescaled only when some row's
-      // running maximum moved
-      float mx = kNegInf;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[c][i]);
-      // Selection, part 1: the group maxima of the tile's candidate keys go
-      // to the wave's LDS rows now, while the raw scores are still in place.
-      const bool sel_tile = P.select && key0 <= p_whi - P.window;
-      if (sel_tile) stage_group_max<G>(acc, sig[wave], mx);
-      mx = xor32_max(mx);
-      // deferred rescaling (see the gather kernel): P <= 2^kRescaleLog2
-      const float m_cand = mx * cexp;
-      if (ballot(m_cand > m_run + kRescaleLog2)) {
-        const float m_new = fmaxf(m_run, m_cand);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == kNegInf ? 0.f : m_new));
-        l_run *= alpha;
-#pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[bk][i] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == kNegInf ? 0.f : m_run;
-      float psum = 0.f;
+      for (int s2 = 0; s2 < 8; ++s2) a = mfma32x32x16(as_bf16x8(ld16(Kb + c * 32 * kRowB + kad[s2])), qb[s2], a);
+      acc[c] = a;
+    }
+    if (key0 + 63 > p_wlo) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(acc[c][i], cexp, -m_use));
-          acc[c][i] = pv;
-          psum += pv;
+          const int j = key0 + 32 * c + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (j > p_lane) acc[c][i] = kNegInf;
         }
-      l_run += psum;
-      bf16x8 pb[4];
+    }
+    // online softmax (exp2 domain); O is rescaled only when some row's
+    // running maximum moved
+    float mx = kNegInf;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[c][i]);
+    // Selection, part 1: the group maxima of the tile's candidate keys go
+    // to the wave's LDS rows now, while the raw scores are still in place.
+    if (sel_tile) stage_group_max<G>(acc, sig[wave], mx);
+    mx = xor32_max(mx);
+    // deferred rescaling (see the gather kernel): P <= 2^kRescaleLog2
+    const float m_cand = mx * cexp;
+    if (ballot(m_cand > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[bk][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(acc[c][i], cexp, -m_use));
+        acc[c][i] = pv;
+        psum += pv;
+      }
+    l_run += psum;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int c = s2 >> 1, base = 8 * (s2 & 1);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[c][base + 2 * e], acc[c][base + 2 * e + 1]);
+      pb[s2] = as_bf16x8(w);
+    }
+    // O^T += V^T P^T: the A operand (dims 32bk + l%32, keys kb + 0..3 and
+    // kb + 8 + 0..3 of the permuted k order) from two transpose reads.
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
-        const int c = s2 >> 1, base = 8 * (s2 & 1);
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[c][base + 2 * e], acc[c][base + 2 * e + 1]);
-        pb[s2] = as_bf16x8(w);
-      }
-      // A operand of O^T = V^T P^T (lane: dim 32bk + l%32, keys kb + 0..3 and
-      // kb + 8 + 0..3 of the permuted k order): two transpose reads; lane j of
-      // each 16-lane group addresses V[kb + j/4][dim0 + 4(j%4)].
-      const uint16_t* vrd = Vt[buf] + ((lane & 15) >> 2) * kVS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-      for (int bk = 0; bk < 4; ++bk) {
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1) + 4 * h;
-          const u32x2 lo = lds_read_tr16(vrd + kb * kVS + 32 * bk);
-          const u32x2 hi = lds_read_tr16(vrd + (kb + 8) * kVS + 32 * bk);
-          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s2], oacc[bk]);
-        }
-      }
-      // Selection, part 2, once the PV products are issued (it does not
-      // depend on them, so it overlaps the matrix pipe): every candidate key
-      // whose score reaches the row's threshold is appended, in ascending key
-      // order, to the row's buffer.
-      if (sel_tile) {
-        const float* ws = sig[wave];
-        const int j = key0 + lane;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const float v = ws[u * 64 + lane] * P.scale;
-          const bool pass = j <= lim[u] && v >= theta[u];
-          const uint64_t m = ballot(pass);
-          if (m) {
-            // range-checked stores: lanes that fail, and positions past the
-            // buffer's capacity, aim beyond the row's range and are dropped
-            const uint32_t off = pass ? 4u * ((uint32_t)cnt[u] + lane_prefix(m)) : kDropOffset;
-            const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap;  // wave-uniform row base
-            buf_st4(make_rsrc_sized(P.buf_sigma + rb, 4u * (uint32_t)P.cap), off, __float_as_uint(v));
-            buf_st4(make_rsrc_sized(P.buf_j + rb, 4u * (uint32_t)P.cap), off, (uint32_t)j);
-            cnt[u] = uniform(cnt[u] + __popcll(m));
-          }
-        }
+        const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1);
+        const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + kb * kRowB + vad[bk]));
+        const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + (kb + 8) * kRowB + vad[bk]));
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s2], oacc[bk]);
       }
     }
+    // Selection, part 2, once the PV products are issued (it does not
+    // depend on them): every candidate key whose score reaches the row's
+    // threshold is appended, in ascending key order, to the row's buffer.
+    // Exactly kStores range-checked stores per tile: failing lanes and
+    // positions past the buffer's capacity aim beyond the row and are dropped.
+    if (sel_tile) {
+      const float* ws = sig[wave];
+      const int j = key0 + lane;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const float v = ws[u * 64 + lane] * P.scale;
+        const bool pass = j <= lim[u] && v >= theta[u];
+        const uint64_t m = ballot(pass);
+        const uint32_t off = pass ? 4u * ((uint32_t)cnt[u] + lane_prefix(m)) : kDropOffset;
+        const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap;  // wave-uniform row base
+        buf_st4(make_rsrc_sized(P.buf_sigma + rb, 4u * (uint32_t)P.cap), off, __float_as_uint(v));
+        buf_st4(make_rsrc_sized(P.buf_j + rb, 4u * (uint32_t)P.cap), off, (uint32_t)j);
+        cnt[u] = uniform(cnt[u] + __popcll(m));
+      }
+    }
+  };
+
+  // two tiles per trip, so that every LDS address is a constant offset
+  fetch(0, std::integral_constant<int, 0>{});
+  int kt = 0;
+#pragma unroll 1
+  for (; kt + 1 < ntiles; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>{});
+    tile(kt + 1, std::integral_constant<int, 1>{});
   }
+  if (kt < ntiles) tile(kt, std::integral_constant<int, 0>{});
 
   const float l_tot = xor32_sum(l_run);
   if (tok_ok) {
