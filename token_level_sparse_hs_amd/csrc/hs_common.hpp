@@ -28,6 +28,7 @@ constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
 constexpr float kRescaleLog2 = 8.f;  // deferred-rescale slack of the online softmax (log2 units)
 
 // ---------------------------------------------------------------- bf16 data

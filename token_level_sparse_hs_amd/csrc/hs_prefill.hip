@@ -201,18 +201,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   load_q<G>(P.q, b, P.n_q, P.Hq, g, tok, qb);
 
   // Selection state of the wave's tokens, all wave-uniform (scalar
-  // registers): threshold, last selectable key (-1: none) and count.
-  // Row (b, wt0 + u, g) is row0 + u * Hkv.
+  // registers): threshold (+inf past the chunk: nothing passes) and count.
+  // Row (b, wt0 + u, g) is row0 + u * Hkv; its last selectable key is
+  // off + wt0 + u - W.
   const int64_t row0 = uniform64(((int64_t)b * P.n_q + wt0) * P.Hkv + g);
   float theta[TPW];
-  int lim[TPW], cnt[TPW];
+  int cnt[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    const int tk = wt0 + u;
-    const bool ok = P.select && tk < P.n_q;
+    const bool ok = P.select && wt0 + u < P.n_q;
     theta[u] = ok ? __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, P.theta[row0 + (int64_t)u * P.Hkv])))
-                  : kNegInf;
-    lim[u] = ok ? off + tk - P.window : -1;
+                  : kPosInf;
     cnt[u] = 0;
   }
 
@@ -370,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const float v = ws[u * 64 + lane] * P.scale;
-        const bool pass = j <= lim[u] && v >= theta[u];
+        const bool pass = j <= off + wt0 + u - P.window && v >= theta[u];
         const uint64_t m = ballot(pass);
         const uint32_t off = pass ? 4u * ((uint32_t)cnt[u] + lane_prefix(m)) : kDropOffset;
         const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap;  // wave-uniform row base
