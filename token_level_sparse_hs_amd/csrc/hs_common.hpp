@@ -163,7 +163,28 @@ __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
 }
-constexpr uint32_t kDropOffset = 0x80000000u;  // past every buffer range: the store is dropped
+constexpr uint32_t kDropOffset = 0x80000000u;
+
+// Raw buffer descriptor (base, range in bytes, no stride) as four scalar
+// words, for inline assembly.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)uniform((int)(uint32_t)a), (uint32_t)uniform((int)(uint32_t)(a >> 32)) & 0xffffu,
+               (uint32_t)uniform((int)bytes), 0x00020000u};
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Direct global->LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane l's bytes land at LDS address lds + 16 l. The compiler does not see an
+// LDS write here: callers order it with s_waitcnt vmcnt and barriers.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, u32x4 rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"((uint32_t)uniform((int)lds)), "v"(voff), "s"(rsrc), "s"(soff)
+               : "m0");
+}  // past every buffer range: the store is dropped
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {  // set bits below this lane
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }

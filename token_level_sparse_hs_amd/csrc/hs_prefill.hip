@@ -173,7 +173,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   // so that both operand read patterns hit distinct banks: chunk c of K row r
   // sits at c ^ (r % 16) (16 rows read the same chunk), chunk c of V row r at
   // c ^ 4(r % 4) (the transpose reads take 4 rows x 64 bytes at a time).
-  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2][2][kTileB];
+  // (one array per stage: distinct objects, so that reads of one stage are
+  // not made to wait for loads in flight into the other)
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_st0[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_st1[2][kTileB];
   __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -230,8 +233,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   const uint16_t* slab = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<int64_t>(P.kv.slab(b, g))));
   const uint32_t rowb = 2u * (uint32_t)P.kv.st;
   const uint32_t span = (uint32_t)(P.n_kv - 1) * rowb + 2u * kHeadDim;  // bytes up to the last valid row's end
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc_sized(slab, span);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc_sized(slab + P.kv.voff, span);
+  // Buffer descriptors (raw, range-checked) in scalar registers.
+  const u32x4 krs = rsrc_words(slab, span);
+  const u32x4 vrs = rsrc_words(slab + P.kv.voff, span);
   uint32_t dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -239,16 +243,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     dk[i] = r * rowb + 16u * ((lane & 15) ^ (r & 15));
     dv[i] = r * rowb + 16u * ((lane & 15) ^ (4u * (r & 3)));
   }
-  typedef __attribute__((address_space(3))) void lds_void;
+  // The loads are issued from inline assembly, so the compiler does not
+  // treat them as LDS writes in flight (it would otherwise wait for all of
+  // them before every LDS access, the next tile's included); the tile wait
+  // and the barrier below order them explicitly.
   auto fetch = [&](int kt, auto stage_c) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
     const uint32_t soff = (uint32_t)uniform(kt * 64) * rowb;
+    const uint32_t base = lds_addr(S ? kv_st1 : kv_st0) + (uint32_t)(16 * wave) * kRowB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kv_lds[S][0][(16 * wave + 4 * i) * kRowB], 16, dk[i],
-                                               soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&kv_lds[S][1][(16 * wave + 4 * i) * kRowB], 16, dv[i],
-                                               soff, 0, 0);
+      lds_dma16(base + 4u * i * kRowB, dk[i], krs, soff);
+      lds_dma16(base + kTileB + 4u * i * kRowB, dv[i], vrs, soff);
     }
   };
   // Operand read offsets within a tile. K (S^T = K Q^T, A operand): lane
@@ -283,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     const bool sel_tile = P.select && wave_live && key0 <= p_whi - P.window;
     stores_pending = sel_tile;
     if (!(wave_live && key0 <= p_whi)) return;
-    const uint8_t* Kb = kv_lds[S][0];
-    const uint8_t* Vb = kv_lds[S][1];
+    const uint8_t* Kb = S ? kv_st1[0] : kv_st0[0];
+    const uint8_t* Vb = S ? kv_st1[1] : kv_st0[1];
     f32x16 acc[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
