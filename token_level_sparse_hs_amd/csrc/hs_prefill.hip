@@ -291,14 +291,13 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     if (!(wave_live && key0 <= p_whi)) return;
     const uint8_t* Kb = S ? kv_st1[0] : kv_st0[0];
     const uint8_t* Vb = S ? kv_st1[1] : kv_st0[1];
-    f32x16 acc[2];
+    // the two key blocks' products interleaved: independent accumulators
+    // keep the matrix pipe fed without waiting on the previous result
+    f32x16 acc[2] = {};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f32x16 a = {};
+    for (int s2 = 0; s2 < 8; ++s2)
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) a = mfma32x32x16(as_bf16x8(ld16(Kb + c * 32 * kRowB + kad[s2])), qb[s2], a);
-      acc[c] = a;
-    }
+      for (int c = 0; c < 2; ++c) acc[c] = mfma32x32x16(as_bf16x8(ld16(Kb + c * 32 * kRowB + kad[s2])), qb[s2], acc[c]);
     if (key0 + 63 > p_wlo) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -354,9 +353,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     // O^T += V^T P^T: the A operand (dims 32bk + l%32, keys kb + 0..3 and
     // kb + 8 + 0..3 of the permuted k order) from two transpose reads.
 #pragma unroll
-    for (int bk = 0; bk < 4; ++bk) {
+    for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
+      for (int bk = 0; bk < 4; ++bk) {  // four independent accumulators in turn
         const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1);
         const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + kb * kRowB + vad[bk]));
         const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + (kb + 8) * kRowB + vad[bk]));
