@@ -294,10 +294,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     // the two key blocks' products interleaved: independent accumulators
     // keep the matrix pipe fed without waiting on the previous result
     f32x16 acc[2] = {};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2)
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[c] = mfma32x32x16(as_bf16x8(ld16(Kb + c * 32 * kRowB + kad[s2])), qb[s2], acc[c]);
+    __builtin_amdgcn_s_setprio(0);
     if (key0 + 63 > p_wlo) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
