@@ -59,6 +59,31 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 // v_mfma_f32_16x16x16_bf16: A: m = l%16, k = 4*(l/16)+e; B: n = l%16,
 // k = 4*(l/16)+e (e = 0..3); C as for 16x16x32.
+// Pause before VALU code reads matrix results. On gfx950 the results of
+// v_mfma_f32_{32x32x16,16x16x32}_bf16 arrive later than the wait states the
+// compiler inserts before a dependent VALU read: a read a few instructions
+// after the last MFMA returned partly written accumulators (measured: the
+// row maximum of a freshly computed score tile varied from run to run while
+// the scores read later did not). Tying the accumulators to an explicit
+// 32-wait-state pause orders every later read after the matrix pipe is done.
+template <typename A>
+__device__ __forceinline__ void mfma_settle(A& a) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(a));
+}
+template <typename A, typename B>
+__device__ __forceinline__ void mfma_settle(A& a, B& b) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(a), "+v"(b));
+}
+template <typename A>
+__device__ __forceinline__ void mfma_settle4(A* a) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+}
+template <typename A>
+__device__ __forceinline__ void mfma_settle8(A* a) {
+  asm volatile("s_nop 15\n\ts_nop 15"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]));
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
                                                     0, 0, 0);
