@@ -62,26 +62,44 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 // Pause before VALU code reads matrix results. On gfx950 the results of
 // v_mfma_f32_{32x32x16,16x16x32}_bf16 arrive later than the wait states the
 // compiler inserts before a dependent VALU read: a read a few instructions
-// after the last MFMA returned partly written accumulators (measured: the
-// row maximum of a freshly computed score tile varied from run to run while
-// the scores read later did not). Tying the accumulators to an explicit
-// 32-wait-state pause orders every later read after the matrix pipe is done.
-template <typename A>
+// after the last MFMA of a chain (across a branch) returned partly written
+// accumulators. Measured on the decode sparse layer: the row maximum read
+// right after its score tile varied from run to run while the scores read
+// later did not (repeated calls then differed by one bf16 ulp); 8 extra wait
+// states removed it. The accumulators are tied to an explicit pause of
+// kSettle16 (16x16 tiles) or kSettle32 (32x32 tiles) wait states, so every
+// later read is ordered after it.
+constexpr int kSettle16 = 12;
+constexpr int kSettle32 = 20;
+#define HS_NOPS_12 "s_nop 11"
+#define HS_NOPS_20 "s_nop 15\n\ts_nop 3"
+template <int N, typename A>
 __device__ __forceinline__ void mfma_settle(A& a) {
-  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(a));
+  static_assert(N == 12 || N == 20, "settle length");
+  if constexpr (N == 12) asm volatile(HS_NOPS_12 : "+v"(a));
+  else asm volatile(HS_NOPS_20 : "+v"(a));
 }
-template <typename A, typename B>
+template <int N, typename A, typename B>
 __device__ __forceinline__ void mfma_settle(A& a, B& b) {
-  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(a), "+v"(b));
+  static_assert(N == 12 || N == 20, "settle length");
+  if constexpr (N == 12) asm volatile(HS_NOPS_12 : "+v"(a), "+v"(b));
+  else asm volatile(HS_NOPS_20 : "+v"(a), "+v"(b));
 }
-template <typename A>
+template <int N, typename A>
 __device__ __forceinline__ void mfma_settle4(A* a) {
-  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  static_assert(N == 12 || N == 20, "settle length");
+  if constexpr (N == 12) asm volatile(HS_NOPS_12 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  else asm volatile(HS_NOPS_20 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
-template <typename A>
+template <int N, typename A>
 __device__ __forceinline__ void mfma_settle8(A* a) {
-  asm volatile("s_nop 15\n\ts_nop 15"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]));
+  static_assert(N == 12 || N == 20, "settle length");
+  if constexpr (N == 12)
+    asm volatile(HS_NOPS_12 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                 "+v"(a[7]));
+  else
+    asm volatile(HS_NOPS_20 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                 "+v"(a[7]));
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {

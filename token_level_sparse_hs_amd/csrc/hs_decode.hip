@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     f32x4 acc = {};
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(ld16(&Kt[n * kKS16 + 32 * s + 8 * gq])), qb[s], acc);
-    mfma_settle(acc);
+    mfma_settle<kSettle16>(acc);
     // lane holds query column n, chunk keys 4*gq + i: the keys it gathered
     if (ch.nv < 16) {
 #pragma unroll
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2)
               acc = mfma16x16x32(as_bf16x8(ld16(krow + 16 * ((4 * s2 + gq) ^ n))), qb[s2], acc);
-            mfma_settle(acc);
+            mfma_settle<kSettle16>(acc);
             if (kb < w0 || kb + 15 > p) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     }
   }
 
-  mfma_settle8(oacc);
+  mfma_settle8<kSettle16>(oacc);
   const float l_tot = xor32_sum(xor16_sum(l_part));
   if (decode && P.combine_in_block) {
     // The block's waves are splits 0..3 of one (b, g) row. Each wave leaves

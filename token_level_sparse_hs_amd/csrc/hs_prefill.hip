@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     for (int s2 = 0; s2 < 8; ++s2)
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[c] = mfma32x32x16(as_bf16x8(ld16(Kb + c * 32 * kRowB + kad[s2])), qb[s2], acc[c]);
-    mfma_settle(acc[0], acc[1]);
+    mfma_settle<kSettle32>(acc[0], acc[1]);
     __builtin_amdgcn_s_setprio(0);
     if (key0 + 63 > p_wlo) {
 #pragma unroll
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   }
   if (kt < ntiles) tile(kt, std::integral_constant<int, 0>{});
 
-  mfma_settle4(oacc);
+  mfma_settle4<kSettle32>(oacc);
   const float l_tot = xor32_sum(l_run);
   if (tok_ok) {
     const float inv = 1.f / l_tot;
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
     if (s0 < ns_whi) {
       f32x16 acc[2];
       qk_tile(Ks, qb, acc);
-      mfma_settle(acc[0], acc[1]);
+      mfma_settle<kSettle32>(acc[0], acc[1]);
       float* ws = sig[wave];
       stage_group_max<G>(acc, ws, fmaxf(acc[0][15], acc[1][15]));
       lds_wait();
