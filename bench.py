@@ -34,7 +34,7 @@ L1_FILL_GBS = 256 * 64 * 2.4  # 256 CUs x 64 B/clk x 2.4 GHz: vector-memory fill
 # Bytes per launch past L2 from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
 # a calibration copy's reading (bench.py --traffic-probe); taken for the
 # current kernels and refreshed by hand whenever they change.
-TRAFFIC = {"sparse_prefill": 1.162e10, "prefill_attn": 6.405e9, "decode_full": 2.064e10, "sparse_decode": 3.39e8}
+TRAFFIC = {"sparse_prefill": 1.031e10, "prefill_attn": 6.394e9, "decode_full": 2.064e10, "sparse_decode": 3.391e8}
 
 
 def log(*a):
@@ -191,6 +191,37 @@ def run_decode(args, hs, synth, _lib, torch):
     return dec
 
 
+def copy_ceiling(torch):
+    """Bytes moved per second (read + written) by a plain elementwise copy of
+    2 GiB on this GPU (torch's y = x * 1, one streaming kernel): the measured
+    ceiling that the decode rooflines are also given against."""
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(5):
+        e0.record()
+        torch.mul(x, 1.0, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x, y
+    torch.cuda.empty_cache()
+    return best
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, w, case, torch):
     """The oracle on a bounded sample of prefill rows of the same workload
     (the very inputs the GPU step used, copied to the host)."""
@@ -225,6 +256,7 @@ def cpu_baseline(args, w, case, torch):
     rows = sorted(set(int(x) for x in np.linspace(0, w.n_q - 1, R)))
     t = rows_time(rows)
     return {"value": round(len(rows) / t, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{len(rows)} query rows evenly spaced over the {w.n_q}-row {w.name} chunk "
                       f"(full layer + selection + {len(qs)} sparse layers), {t:.1f} s of CPU time"}
 
@@ -282,16 +314,20 @@ def main():
         achieved = fl / (us * 1e-6) / 1e12
         byts = counts["sparse_bytes_per_layer"]
         gb = byts / (us * 1e-6) / 1e9
+        G = w.Hq // w.Hkv
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": TRAFFIC.get(dom), "kernel": dom,
                 "flops_per_launch": fl, "avg_us": round(us, 1),
+                # the G heads of a group fill G of the 16 columns of each matrix tile
+                "executed_flops_per_launch": fl * 16 // G if G < 16 else fl,
                 "gather": {"achieved_GBs": round(gb, 1), "bytes_per_launch": byts,
                            "l1_fill_peak_GBs": L1_FILL_GBS, "frac": round(gb / L1_FILL_GBS, 4)}}
     kernels = {k: {"launches_per_step": n / args.steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()}
     full_ach = counts["full_flops"] / (pa_us * 1e-6) / 1e12
     roof_full = {"bound": "mfma", "achieved": round(full_ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(full_ach / PEAK_BF16_TFLOPS, 4), "kernel": "prefill_attn",
-                 "flops_per_launch": counts["full_flops"], "avg_us": round(pa_us, 1)}
+                 "flops_per_launch": counts["full_flops"], "executed_flops_per_launch": counts["full_flops"],
+                 "avg_us": round(pa_us, 1)}
     n_sp, t_sp = kt.get("sparse_prefill", (0, 0.0))
     sp_us = t_sp / max(1, n_sp) * 1e3
     sparse_prefill = {"avg_us": round(sp_us, 1),
@@ -308,6 +344,11 @@ def main():
     decode = None
     if not args.no_decode:
         decode = run_decode(args, hs, synth, _lib, torch)
+        ceil = copy_ceiling(torch)
+        log(f"[bench] plain copy: {ceil:.0f} GB/s moved")
+        decode["copy_ceiling_GBs"] = round(ceil, 1)
+        for key in ("sparse_decode_roofline", "decode_full_roofline"):
+            decode[key]["frac_of_copy_ceiling"] = round(decode[key]["achieved"] / ceil, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
