@@ -9,8 +9,10 @@ before timing starts. `value` is prefill tokens/s of that block.
 
 Beside it: the batched decode workload (64 sequences, contexts drawn from
 [65536, 262144], 32 steps of append + full attention + select once + three
-sparse layers), reported as microseconds per step, and the CPU oracle timed
-on a bounded sample of prefill rows.
+sparse layers) and the single-sequence decode at a 1M-token context (16
+steps), each reported as microseconds per step with eager calls and with the
+step replayed as one HIP graph; and the CPU oracle timed on a bounded sample
+of prefill rows.
 
 Per-kernel durations come from the library's HIP-event timing on the stream
 the kernels run on; the roofline object describes the kernel that takes the
@@ -34,7 +36,7 @@ L1_FILL_GBS = 256 * 64 * 2.4  # 256 CUs x 64 B/clk x 2.4 GHz: vector-memory fill
 # Bytes per launch past L2 from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
 # a calibration copy's reading (bench.py --traffic-probe); taken for the
 # current kernels and refreshed by hand whenever they change.
-TRAFFIC = {"sparse_prefill": 1.031e10, "prefill_attn": 6.394e9, "decode_full": 2.064e10, "sparse_decode": 3.391e8}
+TRAFFIC = {"sparse_prefill": 1.031e10, "prefill_attn": None, "decode_full": None, "sparse_decode": 3.391e8}
 
 
 def log(*a):
@@ -131,16 +133,17 @@ def traffic_probe(args, hs, synth, _lib, torch):
     del y
 
 
-def run_decode(args, hs, synth, _lib, torch):
-    w = synth.WORKLOADS["decode64"]
+def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
+    """Decode steps of one workload: append + full layer + select once + the
+    sparse layers, `steps` steps with fresh inputs (eager calls); then step 0
+    captured as one HIP graph and replayed `steps` times."""
+    w = synth.WORKLOADS[wname]
     dev = "cuda:0"
-    lengths = synth.decode_lengths(w)
-    steps = args.decode_steps
-    log(f"[bench] generating decode64 cache (sum of lengths {sum(lengths)})")
+    log(f"[bench] generating {wname} decode cache (sum of lengths {sum(lengths)})")
     case = synth.make_decode_case(w, dev, lengths, steps)
     kv = case["kv"]
     cap = case["cap"]
-    shape = hs.make_shape(batch=w.B, n_q=1, n_kv=0, kv_capacity=cap, q_heads=w.Hq, kv_heads=w.Hkv,
+    shape = hs.make_shape(batch=len(lengths), n_q=1, n_kv=0, kv_capacity=cap, q_heads=w.Hq, kv_heads=w.Hkv,
                           top_k=w.top_k, window=w.window)
     ws_full = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
     ws_sp = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, shape, 1), dev)
@@ -160,33 +163,53 @@ def run_decode(args, hs, synth, _lib, torch):
     _lib.timing_enable(False)
     kt = _lib.timing_read()
     us_step = (t1 - t0) * 1e6 / steps
-    log(f"[bench] decode64: {us_step:.1f} us/step")
+    log(f"[bench] {wname}: {us_step:.1f} us/step")
     for k, (n, tot) in sorted(kt.items(), key=lambda x: -x[1][1]):
         log(f"[bench]   {k:16s} launches={n:5d} avg={tot / n * 1e3:10.1f} us")
+    # the same step as one graph launch (inputs of step 0, replayed)
+    g = hs.DecodeStepGraph(kv, batch=len(lengths), q_heads=w.Hq, sparse_layers=w.sparse_layers, top_k=w.top_k,
+                           window=w.window)
+    st = case["steps"][0]
+    g.q.copy_(st["q_full"])
+    g.kv_new.copy_(st["kv_new"])
+    for d, x in zip(g.q_sparse, st["q_sparse"]):
+        d.copy_(x)
+    g.seq_lens.copy_(seqs[0])
+    g.step(max(lengths) + 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        g.step(max(lengths) + 1)
+    torch.cuda.synchronize()
+    us_graph = (time.perf_counter() - t0) * 1e6 / steps
+    log(f"[bench] {wname}: {us_graph:.1f} us/step as one graph launch")
     # algorithmic bytes
     full_bytes = sum(512.0 * w.Hkv * (L + s + 1) for L in lengths for s in range(steps)) / steps
     sp_rows = sum(min(w.top_k, max(0, L + s + 1 - w.window)) + min(w.window, L + s + 1)
                   for L in lengths for s in range(steps)) / steps
-    sp_bytes = 512.0 * w.Hkv * sp_rows + 4.0 * w.B * w.Hkv * w.top_k + 2 * 2.0 * w.B * w.Hq * 128
+    sp_bytes = 512.0 * w.Hkv * sp_rows + 4.0 * len(lengths) * w.Hkv * w.top_k + 2 * 2.0 * len(lengths) * w.Hq * 128
     n_sp, t_sp = kt.get("sparse_decode", (0, 0.0))
-    n_cb, t_cb = kt.get("lse_combine", (0, 0.0))
     n_df, t_df = kt.get("decode_full", (0, 0.0))
     sp_us = t_sp / max(1, n_sp) * 1e3
     df_us = t_df / max(1, n_df) * 1e3
     dec = {
-        "workload": "decode64", "batch": w.B, "context": [w.ctx_lo, w.ctx_hi], "steps": steps,
+        "workload": wname, "batch": len(lengths), "context": [min(lengths), max(lengths)], "steps": steps,
         "us_per_step": round(us_step, 2),
+        "us_per_step_graph": round(us_graph, 2),
         "sparse_layer_kernel_us": round(sp_us, 2),
+        "kernels": {k: {"launches_per_step": n / steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()},
         "sparse_decode_roofline": {"bound": "hbm", "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": round(sp_bytes / (sp_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                                   "bytes_per_launch": sp_bytes, "traffic": TRAFFIC.get("sparse_decode")},
+                                   "bytes_per_launch": sp_bytes,
+                                   "traffic": TRAFFIC.get("sparse_decode") if wname == "decode64" else None},
         "decode_full_roofline": {"bound": "hbm", "achieved": round(full_bytes / (df_us * 1e-6) / 1e9, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(full_bytes / (df_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                                 "bytes_per_launch": full_bytes, "traffic": TRAFFIC.get("decode_full")},
+                                 "bytes_per_launch": full_bytes,
+                                 "traffic": TRAFFIC.get("decode_full") if wname == "decode64" else None},
     }
-    del case, kv
+    del case, kv, g
     torch.cuda.empty_cache()
     return dec
 
@@ -341,14 +364,18 @@ def main():
     del case
     torch.cuda.empty_cache()
 
-    decode = None
+    decode = decode_1m = None
     if not args.no_decode:
-        decode = run_decode(args, hs, synth, _lib, torch)
+        wd = synth.WORKLOADS["decode64"]
+        decode = run_decode(args, hs, synth, _lib, torch, "decode64", synth.decode_lengths(wd), args.decode_steps)
+        w5 = synth.WORKLOADS["ctx1m"]
+        decode_1m = run_decode(args, hs, synth, _lib, torch, "ctx1m", [w5.n_kv], w5.decode_steps)
         ceil = copy_ceiling(torch)
         log(f"[bench] plain copy: {ceil:.0f} GB/s moved")
-        decode["copy_ceiling_GBs"] = round(ceil, 1)
-        for key in ("sparse_decode_roofline", "decode_full_roofline"):
-            decode[key]["frac_of_copy_ceiling"] = round(decode[key]["achieved"] / ceil, 4)
+        for d in (decode, decode_1m):
+            d["copy_ceiling_GBs"] = round(ceil, 1)
+            for key in ("sparse_decode_roofline", "decode_full_roofline"):
+                d[key]["frac_of_copy_ceiling"] = round(d[key]["achieved"] / ceil, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -378,6 +405,7 @@ def main():
         "sparse_prefill_layer": sparse_prefill,
         "kernels": kernels,
         "decode": decode,
+        "decode_ctx1m": decode_1m,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

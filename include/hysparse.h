@@ -55,6 +55,14 @@
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *    stream). All work is enqueued asynchronously on it; buffers must stay
  *    valid until the stream reaches them. No call synchronises the host.
+ *  - Graph capture: with timing off, a call enqueues kernel launches only
+ *    (no allocation, copy, memset, event or host wait), so calls may be
+ *    captured into a HIP graph and replayed ([SSA-3.6] "End-to-end decode
+ *    overhead": per-step launches dominate once kernels take microseconds).
+ *    Host arguments (shape, max_seq_len, workspace) are fixed at capture;
+ *    device data (q, kv, seq_lens, ...) is read at replay, so a captured
+ *    decode step serves any lengths up to the max_seq_len it was captured
+ *    with.
  *  - Errors: arguments are validated on the host before anything is
  *    enqueued, so a non-OK status means no work was queued (except
  *    HS_ERR_HIP, reported when a launch fails). A detail message for the

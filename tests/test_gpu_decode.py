@@ -85,6 +85,34 @@ def test_decode_long_rows_filtered_select():
     run_decode([20000, 70000], 2, 8, 1, 512, 64, seed=13, n_sparse=1)
 
 
+def test_decode_sampled_threshold_overshoot():
+    """Long rows are filtered by the m-th largest of 8192 evenly spaced
+    samples. Keys placed exactly at the sampled positions and aimed at the
+    queries push that threshold above the row's k-th score, so fewer than k
+    keys survive the filter: the selection must fall back to the whole row
+    and still return the exact top k (most of them those planted keys)."""
+    L, Hq, Hkv, k, W = 40000, 4, 1, 512, 16
+    print(f"[case] decode sampled-threshold overshoot L={L} k={k}", flush=True)
+    kv = torch.zeros((1, Hkv, L + 1, 2, 128), dtype=torch.bfloat16, device=DEV)
+    kv[0, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 81, DEV)
+    q = synth.randn_bf16((1, Hq, 128), 82, DEV)
+    u = q[0].float().sum(0)
+    u = u / u.norm() * (128 ** 0.5)
+    ncand = L - W + 1  # candidates of the row after the append (p = L)
+    pos = torch.tensor(sorted({(s * ncand) // 8192 for s in range(8192)}), device=DEV)
+    noise = synth.randn_bf16((len(pos), 128), 83, DEV).float()
+    kv[0, 0, pos, 0] = (0.8 * u[None] + 0.6 * noise).to(torch.bfloat16)
+    kv_new = synth.randn_bf16((1, Hkv, 2, 128), 84, DEV)
+    seq_lens = torch.tensor([L + 1], dtype=torch.int32, device=DEV)
+    o, lse, idx = hs.decode_step(q, kv_new, kv, seq_lens, L + 1, top_k=k, window=W)
+    torch.cuda.synchronize()
+    Ks, Vs = kv[0, :, :, 0].float().cpu().numpy(), kv[0, :, :, 1].float().cpu().numpy()
+    ref = orc.decode_step(f32(q[0]), [], f32(kv_new[0]), Ks, Vs, L + 1, k, W, orc.default_scale(128))
+    check_idx_row(idx.cpu().numpy()[0, 0], ref["idx"][0], ref["sigma"][0], ref["tau"][0], L, W, k, where="overshoot")
+    planted = set(pos.tolist())
+    assert sum(int(j) in planted for j in ref["idx"][0]) > k // 2
+
+
 def test_decode_streaming_select():
     """k close to the row length defeats the sample filter: streaming select."""
     run_decode([9000], 1, 4, 1, 8000, 16, seed=14, n_sparse=1)

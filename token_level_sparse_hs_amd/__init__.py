@@ -147,3 +147,8 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
                                   _lib.ptr(idx) if top_k > 0 else None, _lib.ptr(ws),
                                   0 if ws is None else ws.numel(), _lib.stream_handle(dev)))
     return o, lse, idx
+
+
+from .graph import DecodeStepGraph, length_bucket  # noqa: E402  (uses the calls above)
+
+__all__ += ["DecodeStepGraph", "length_bucket"]

@@ -156,7 +156,8 @@ struct DecodePlan {
   int splits = 1, split_len = 32;
   bool in_block = false;  // sparse decode: splits merged inside the block
   int64_t sigma_stride = 0;
-  size_t off_sigma = 0, off_part = 0, total = 0;
+  int sel_slices = 0;     // sliced selection (0: one block per row)
+  size_t off_sigma = 0, off_part = 0, off_theta = 0, off_segcnt = 0, off_segkey = 0, off_segidx = 0, total = 0;
 };
 
 // Splits a per-(b, g) key stream of up to `nkeys` keys so that the grid holds
@@ -170,27 +171,58 @@ void plan_splits(int64_t bg, int64_t nkeys, int* splits, int* split_len, int64_t
   *splits = (int)std::max<int64_t>(1, (nkeys + len - 1) / len);
 }
 
+// SIMDs of the chip (256 CUs x 4): decode grids are sized in these.
+constexpr int64_t kChipSimds = 1024;
+
 DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   DecodePlan p;
   const int G = s->q_heads / s->kv_heads;
   const int64_t bg = (int64_t)s->batch * s->kv_heads;
-  plan_splits(bg, max_seq_len, &p.splits, &p.split_len, 32768);
-  if (p.splits > 4096) {  // bound of the combine kernel's weight table
-    p.split_len = (int)round_up((max_seq_len + 4095) / 4096, 32);
-    p.splits = (int)((max_seq_len + p.split_len - 1) / p.split_len);
-  }
+  // Splits of about kFullSplitKeys keys (measured best both for 64 sequences
+  // of 64K-256K tokens and for one sequence of 1M), but at least two waves
+  // per SIMD over the batch, and no more splits than the merge takes.
+  constexpr int64_t kFullSplitKeys = 2048, kMinWaves = 2 * kChipSimds, kMaxSplits = 4096;
+  int64_t splits = std::max((max_seq_len + kFullSplitKeys - 1) / kFullSplitKeys, (kMinWaves + bg - 1) / bg);
+  splits = std::min(splits, kMaxSplits);
+  int64_t len = std::max<int64_t>(32, round_up((max_seq_len + splits - 1) / splits, 32));
+  // an odd multiple of 32 keys: split starts a power-of-two stride apart
+  // (1 MiB at 2048 keys) cost ~12% of the single-sequence 1M-context stream
+  if ((len / 32) % 2 == 0) len += 32;
+  p.split_len = (int)len;
+  p.splits = (int)((max_seq_len + len - 1) / len);
   p.sigma_stride = round_up(max_seq_len, 64);
   size_t o = 0;
   p.off_sigma = o;
   o = align_up(o + (s->top_k > 0 ? (size_t)bg * p.sigma_stride * 4 : 0));
   p.off_part = o;
   o = align_up(o + (size_t)bg * p.splits * G * (128 + 2) * 4);
+  // Rows longer than one block's registers hold are selected in slices spread
+  // over the chip; survivors get room for a whole slice each (no overflow).
+  // One block per row filters with 2048 samples into 8192 register slots,
+  // expecting about k + 6 sqrt(k n / 2048) survivors; rows whose survivors
+  // would not fit, or a batch too small to occupy the chip with one block per
+  // row, are selected in slices instead.
+  const int64_t max_cand = (int64_t)max_seq_len - s->window;
+  const double expect = s->top_k + 6.0 * std::sqrt((double)s->top_k * (double)max_cand / 2048.0);
+  if (s->top_k > 0 && max_cand > hs::kSelRegKeys && (bg < kChipSimds / 4 || expect > 0.75 * hs::kSelRegKeys)) {
+    const int64_t ns = (max_cand + hs::kDecSlice - 1) / hs::kDecSlice;
+    if (ns <= hs::kMaxDecSlices) p.sel_slices = (int)ns;
+  }
+  if (p.sel_slices > 0) {
+    const size_t seg = (size_t)bg * p.sel_slices;
+    p.off_theta = o;
+    o = align_up(o + (size_t)bg * 4);
+    p.off_segcnt = o;
+    o = align_up(o + seg * 4);
+    p.off_segkey = o;
+    o = align_up(o + seg * hs::kDecSlice * 4);
+    p.off_segidx = o;
+    o = align_up(o + seg * hs::kDecSlice * 4);
+  }
   p.total = o;
   return p;
 }
 
-// SIMDs of the chip (256 CUs x 4): the sparse decode grid is sized in these.
-constexpr int64_t kChipSimds = 1024;
 
 // Sparse decode: each (b, g) row gathers top_k + W keys. When the batch has
 // at least a quarter as many rows as the chip has SIMDs, every row is split
@@ -536,6 +568,13 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     hs::SelectDecodeParams sp{};
     sp.B = s->batch; sp.Hkv = s->kv_heads; sp.top_k = s->top_k; sp.window = s->window;
     sp.seq_lens = seq_lens; sp.sigma = dp.sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = idx;
+    sp.nslices = plan.sel_slices;
+    if (plan.sel_slices > 0) {
+      sp.theta_key = reinterpret_cast<uint32_t*>(w + plan.off_theta);
+      sp.seg_count = reinterpret_cast<uint32_t*>(w + plan.off_segcnt);
+      sp.seg_key = reinterpret_cast<uint32_t*>(w + plan.off_segkey);
+      sp.seg_idx = reinterpret_cast<int32_t*>(w + plan.off_segidx);
+    }
     HIP_TRY(timed("select_decode", hst, [&] { return hs::launch_select_decode(sp, s->batch * s->kv_heads, hst); }));
   }
   return ok();

@@ -70,6 +70,11 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 // kSettle16 (16x16 tiles) or kSettle32 (32x32 tiles) wait states, so every
 // later read is ordered after it.
 constexpr int kSettle16 = 12;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x2;
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
 constexpr int kSettle32 = 20;
 #define HS_NOPS_12 "s_nop 11"
 #define HS_NOPS_20 "s_nop 15\n\ts_nop 3"

@@ -72,7 +72,20 @@ struct SelectDecodeParams {
   const float* sigma;  // [B*Hkv][sigma_stride]
   int64_t sigma_stride;
   int32_t* idx;        // [B][Hkv][top_k]
+  // Sliced path (nslices > 0) for rows longer than one block holds in
+  // registers: per-row threshold, a filter over row slices of kDecSlice keys
+  // by separate blocks, then one block per row on the survivors.
+  int nslices;         // slices per row (covers the longest row)
+  uint32_t* theta_key; // [rows] filter threshold (score key; 0 = no filter)
+  uint32_t* seg_count; // [rows][nslices] survivors per slice
+  uint32_t* seg_key;   // [rows][nslices][kDecSlice] survivors' score keys, index order
+  int32_t* seg_idx;    // [rows][nslices][kDecSlice] survivors' token indices
 };
+// Sliced decode selection: keys per filter block; rows of up to kSelRegKeys
+// candidates are selected directly from registers by one block.
+constexpr int kDecSlice = 16384;
+constexpr int kSelRegKeys = 8192;
+constexpr int kMaxDecSlices = 1024;
 
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s);
 hipError_t launch_threshold(const ThresholdParams& p, int64_t rows, hipStream_t s);

@@ -13,15 +13,19 @@
 //    tokens. Each wave owns 32 MFMA rows = 32/G tokens x the G query heads of
 //    group g, so the group's heads share every K/V tile staged in LDS and the
 //    group maximum over heads (the selection score) is a reduction across
-//    lanes: heads sit 32/G lanes apart, so its first step swaps lane rows
-//    (v_permlane16_swap) and halves the values each lane carries.
+//    lanes: a token's heads sit 16/G lanes apart inside one 16-lane row, and
+//    masked DPP steps halve the values each lane carries.
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: with the key
 //    axis on MFMA rows and the query rows on lanes, every per-row softmax
 //    quantity (running max, sum, rescale) is lane-local apart from one
 //    lane^32 exchange, and the S^T accumulator is already laid out as the B
-//    operand of the PV product. K and V tiles live row-major in LDS; V is
-//    read back with LDS transpose reads (ds_read_b64_tr_b16) as the A
-//    operand of O^T = V^T P^T.
+//    operand of the PV product. K and V tiles go from global memory straight
+//    into LDS (buffer loads with the lds modifier, two stages, the next tile
+//    in flight during the current one), 256-byte rows with their 16-byte
+//    chunks XOR-permuted by row so operand reads hit distinct banks; K
+//    operands are read two steps ahead of their products, and V is read back
+//    with LDS transpose reads (ds_read_b64_tr_b16) as the A operand of
+//    O^T = V^T P^T.
 //  * Online softmax in fp32 on exp2 with the scale folded into one FMA.
 //  * Selection: the per-lane scaled logits are maxed over the G head lanes
 //    (DPP), staged per wave in LDS, and every candidate (j <= p - W) whose
@@ -295,10 +299,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     // keep the matrix pipe fed without waiting on the previous result
     f32x16 acc[2] = {};
     __builtin_amdgcn_s_setprio(1);
+    // K operands read two steps ahead of their products (a three-slot
+    // ring), so the LDS latency hides behind the matrix pipe
+    u32x4 kf[3][2];
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2)
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) acc[c] = mfma32x32x16(as_bf16x8(ld16(Kb + c * 32 * kRowB + kad[s2])), qb[s2], acc[c]);
+      for (int c = 0; c < 2; ++c) kf[s2][c] = ld16(Kb + c * 32 * kRowB + kad[s2]);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      if (s2 + 2 < 8)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) kf[(s2 + 2) % 3][c] = ld16(Kb + c * 32 * kRowB + kad[s2 + 2]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[c] = mfma32x32x16(as_bf16x8(kf[s2 % 3][c]), qb[s2], acc[c]);
+    }
+    // keep that order: the scheduler would otherwise pull each read down
+    // to its product to save registers
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      if (s2 + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
     mfma_settle<kSettle32>(acc[0], acc[1]);
     __builtin_amdgcn_s_setprio(0);
     if (key0 + 63 > p_wlo) {

@@ -233,6 +233,7 @@ __device__ void topk_stream(SelShared& sh, const Src& src, int n, int k, int32_t
 
 constexpr int kE = 32;                    // elements per thread in registers
 constexpr int kRegCap = kSelThreads * kE; // 8192
+static_assert(kRegCap == kSelRegKeys, "host and device agree on the register path's capacity");
 constexpr int kSamples = 2048;
 
 struct RadixResult {
@@ -733,6 +734,185 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecode
   topk_any<true>(sh, lds.key, lds.idx, src, ncand, P.top_k, out);
 }
 
+// ---------------------------------------------------------------- decode, long rows
+//
+// A decode score row of a long sequence (a million keys at the 1M-token
+// context) is too long for one block to scan at memory speed, and a batch of
+// one sequence has only Hkv such rows. Three launches spread it over the chip:
+//  1. threshold: one block per row takes kDecSamples evenly spaced keys and
+//     their m-th largest, m = mu + 6 sqrt(mu) + 1 with mu = k S / n the
+//     expected number of samples among the row's top k, so that the k-th
+//     largest key of the row lies at or above it with overwhelming
+//     probability;
+//  2. filter: one block per (slice of kDecSlice keys, row) keeps the keys at
+//     or above the threshold, in index order, with their indices;
+//  3. final: one block per row concatenates the slices' survivors in slice
+//     order (so still in index order) and selects exactly from them. When
+//     the survivors are fewer than k (the threshold overshot) or more than
+//     the block holds, it selects from the whole dense row instead, so the
+//     result never depends on the sampling.
+
+constexpr int kDecSamples = 8192;
+constexpr int kDecCandCap = 16384;  // survivors the final block holds in LDS
+
+// Exclusive block-wide scan that also returns the block total.
+__device__ __forceinline__ uint32_t block_scan_total(SelShared& sh, uint32_t v, uint32_t* total) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t incl = (uint32_t)wave_incl_scan((int)v);
+  if (lane == 63) sh.wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint32_t t = sh.wave_tot[w];
+    base += w < wave ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+struct DecRow {
+  int ncand;       // |C(p)|
+  const float* s;  // dense score row
+};
+__device__ __forceinline__ DecRow dec_row(const SelectDecodeParams& P, int row) {
+  const int b = row / P.Hkv;
+  const int p = P.seq_lens[b] - 1;
+  return DecRow{imax(0, p - P.window + 1), P.sigma + (int64_t)row * P.sigma_stride};
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_decode_threshold_kernel(SelectDecodeParams P) {
+  __shared__ SelShared sh;
+  const int row = blockIdx.x;
+  const DecRow r = dec_row(P, row);
+  if (r.ncand <= kRegCap) return;  // selected directly by the final kernel
+  const double mu = (double)P.top_k * kDecSamples / (double)r.ncand;
+  const int m = (int)ceil(mu + 6.0 * sqrt(mu)) + 1;
+  if (m >= kDecSamples) {  // the samples cannot bound the k-th key: no filter
+    if (threadIdx.x == 0) P.theta_key[row] = 0u;
+    return;
+  }
+  constexpr int ES = kDecSamples / kSelThreads;
+  const DenseSrc src{r.s};
+  uint32_t skey[ES];
+#pragma unroll
+  for (int e = 0; e < ES; ++e) {
+    const int s = threadIdx.x * ES + e;
+    skey[e] = src.key((int)(((int64_t)s * r.ncand) / kDecSamples));
+  }
+  const RadixResult rr = radix_regs<ES>(sh, skey, (uint32_t)m);
+  // keys >= prefix include the m largest samples (take_all leaves the low
+  // bits of prefix zero: still a lower bound)
+  if (threadIdx.x == 0) P.theta_key[row] = rr.prefix;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_decode_filter_kernel(SelectDecodeParams P) {
+  __shared__ SelShared sh;
+  const int slice = blockIdx.x, row = blockIdx.y;
+  const DecRow r = dec_row(P, row);
+  if (r.ncand <= kRegCap) return;
+  const int i0 = slice * kDecSlice;
+  const int n = imin(r.ncand, i0 + kDecSlice) - i0;
+  const int64_t seg = (int64_t)row * P.nslices + slice;
+  if (n <= 0) {
+    if (threadIdx.x == 0) P.seg_count[seg] = 0u;
+    return;
+  }
+  const uint32_t theta = P.theta_key[row];
+  // thread t owns keys [64t, 64t + 64) of the slice: one scan keeps index order
+  constexpr int kPer = kDecSlice / kSelThreads;
+  static_assert(kPer == 64, "16 vector loads per thread");
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(r.s + i0, 4u * (uint32_t)n);  // reads past n return 0
+  u32x4 w[kPer / 4];
+#pragma unroll
+  for (int j = 0; j < kPer / 4; ++j) w[j] = buf_ld16(rs, 4u * (uint32_t)(kPer * threadIdx.x + 4 * j));
+  const int e0 = kPer * threadIdx.x;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer / 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += (e0 + 4 * j + q < n && score_key(__uint_as_float(w[j][q])) >= theta) ? 1u : 0u;
+  uint32_t total;
+  uint32_t pos = block_scan_total(sh, cnt, &total);
+  uint32_t* okey = P.seg_key + seg * kDecSlice;
+  int32_t* oidx = P.seg_idx + seg * kDecSlice;
+#pragma unroll
+  for (int j = 0; j < kPer / 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t key = score_key(__uint_as_float(w[j][q]));
+      if (e0 + 4 * j + q < n && key >= theta) {
+        okey[pos] = key;
+        oidx[pos] = i0 + e0 + 4 * j + q;
+        ++pos;
+      }
+    }
+  if (threadIdx.x == 0) P.seg_count[seg] = total;
+}
+
+struct DecLds {
+  uint32_t key[kDecCandCap];
+  int32_t idx[kDecCandCap];
+  uint32_t off[kMaxDecSlices + 1];
+};
+
+__global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(SelectDecodeParams P) {
+  __shared__ SelShared sh;
+  __shared__ DecLds lds;
+  const int row = blockIdx.x;
+  const DecRow r = dec_row(P, row);
+  const int k = P.top_k;
+  int32_t* out = P.idx + (int64_t)row * k;
+  if (r.ncand <= k) {
+    for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = i < r.ncand ? i : -1;
+    return;
+  }
+  const DenseSrc dense{r.s};
+  if (r.ncand <= kRegCap) {
+    topk_regs(sh, dense, r.ncand, k, out);
+    return;
+  }
+  const int ns = (r.ncand + kDecSlice - 1) / kDecSlice;  // <= nslices <= kMaxDecSlices
+  const uint32_t* cnt = P.seg_count + (int64_t)row * P.nslices;
+  const int per = (ns + kSelThreads - 1) / kSelThreads;
+  const int s0 = imin(ns, threadIdx.x * per), s1 = imin(ns, s0 + per);
+  uint32_t local = 0;
+  for (int i = s0; i < s1; ++i) local += cnt[i];
+  uint32_t total;
+  uint32_t base = block_scan_total(sh, local, &total);
+  for (int i = s0; i < s1; ++i) {
+    lds.off[i] = base;
+    base += cnt[i];
+  }
+  if (threadIdx.x == 0) lds.off[ns] = total;
+  __syncthreads();
+  if (total < (uint32_t)k || total > (uint32_t)kDecCandCap) {
+    topk_stream(sh, dense, r.ncand, k, out);
+    return;
+  }
+  for (uint32_t i = threadIdx.x; i < total; i += kSelThreads) {
+    int lo = 0, hi = ns;  // the last slice whose offset is <= i
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (lds.off[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    const int64_t src = ((int64_t)row * P.nslices + lo) * kDecSlice + (i - lds.off[lo]);
+    lds.key[i] = P.seg_key[src];
+    lds.idx[i] = P.seg_idx[src];
+  }
+  __syncthreads();
+  const LdsSrc ls{lds.key, lds.idx};
+  if (total == (uint32_t)k) {
+    for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = lds.idx[i];
+  } else if (total <= (uint32_t)kRegCap) {
+    topk_regs(sh, ls, (int)total, k, out);
+  } else {
+    topk_stream(sh, ls, (int)total, k, out);
+  }
+}
+
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s) {
   select_prefill_wave_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
   hipError_t e = hipGetLastError();
@@ -752,7 +932,17 @@ hipError_t launch_threshold(const ThresholdParams& p, int64_t rows, hipStream_t 
   return hipGetLastError();
 }
 hipError_t launch_select_decode(const SelectDecodeParams& p, int rows, hipStream_t s) {
-  select_decode_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+  if (p.nslices <= 0) {
+    select_decode_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+    return hipGetLastError();
+  }
+  select_decode_threshold_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_decode_filter_kernel<<<dim3((unsigned)p.nslices, (unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_decode_final_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 
