@@ -534,14 +534,19 @@ __global__ void append_kernel(AppendParams P) {
   st16(dst, w);
 }
 
-// Log-sum-exp merge of split partials; one 128-thread block per (b, head).
-// Pass 1 (threads over splits): M = max m_s, then weights w_s = 2^(m_s - M)
-// into LDS and l = sum w_s l_s. Pass 2 (threads over dims): o = sum w_s acc_s / l
-// with independent loads.
+// Log-sum-exp merge of split partials; one block per (b, head) of
+// kCombGroups groups of 128 threads. Pass 1 (threads over splits): M = max
+// m_s, then weights w_s = 2^(m_s - M) into LDS and l = sum w_s l_s. Pass 2:
+// group i takes the i-th quarter of the splits, thread d of a group sums
+// w_s acc_s[d] over them with independent loads; the groups' sums add in LDS
+// and o = sum / l.
 constexpr int kMaxCombineSplits = 4096;
-__global__ __launch_bounds__(128) void combine_kernel(CombineParams P) {
+constexpr int kCombGroups = 4;
+constexpr int kCombThreads = 128 * kCombGroups;
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams P) {
   __shared__ float wsh[kMaxCombineSplits];
-  __shared__ float red[2][4];
+  __shared__ float red[2][kCombThreads / 64];
+  __shared__ float part[kCombGroups][kHeadDim];
   const int bh = blockIdx.x;
   const int head = bh % P.Hq, b = bh / P.Hq;
   const int G = P.Hq / P.Hkv;
@@ -554,15 +559,17 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams P) {
   const int64_t sstride = (int64_t)G * (kHeadDim + 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float M = kNegInf;
-  for (int s = tid; s < ns; s += 128) M = fmaxf(M, base[s * sstride + kHeadDim]);
+  for (int s = tid; s < ns; s += kCombThreads) M = fmaxf(M, base[s * sstride + kHeadDim]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   if (lane == 0) red[0][wave] = M;
   __syncthreads();
-  M = fmaxf(red[0][0], red[0][1]);
+  M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kCombThreads / 64; ++w) M = fmaxf(M, red[0][w]);
   const float Mu = M == kNegInf ? 0.f : M;
   float l = 0.f;
-  for (int s = tid; s < ns; s += 128) {
+  for (int s = tid; s < ns; s += kCombThreads) {
     const float w = __builtin_amdgcn_exp2f(base[s * sstride + kHeadDim] - Mu);
     wsh[s] = w;
     l += w * base[s * sstride + kHeadDim + 1];
@@ -571,19 +578,30 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams P) {
   for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
   if (lane == 0) red[1][wave] = l;
   __syncthreads();
-  l = red[1][0] + red[1][1];
+  l = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombThreads / 64; ++w) l += red[1][w];
+  const int grp = tid >> 7, d = tid & 127;
+  const int s0 = (ns * grp) / kCombGroups, s1 = (ns * (grp + 1)) / kCombGroups;
   float acc = 0.f;
-  const float* pd = base + tid;
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
+  const float* pd = base + d;
+  int s = s0;
+  for (; s + 8 <= s1; s += 8) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = pd[(s + u) * sstride];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc += wsh[s + u] * v[u];
   }
-  for (; s < ns; ++s) acc += wsh[s] * pd[s * sstride];
-  P.o[((int64_t)b * P.Hq + head) * kHeadDim + tid] = (uint16_t)f32_to_bf16_bits(acc / l);
+  for (; s < s1; ++s) acc += wsh[s] * pd[s * sstride];
+  part[grp][d] = acc;
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float o = part[0][tid];
+#pragma unroll
+    for (int q = 1; q < kCombGroups; ++q) o += part[q][tid];
+    P.o[((int64_t)b * P.Hq + head) * kHeadDim + tid] = (uint16_t)f32_to_bf16_bits(o / l);
+  }
   if (P.lse && tid == 0) P.lse[(int64_t)b * P.Hq + head] = M * kLn2 + __logf(l);
 }
 
@@ -621,7 +639,7 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
-  combine_kernel<<<dim3((unsigned)(p.B * p.Hq)), dim3(128), 0, s>>>(p);
+  combine_kernel<<<dim3((unsigned)(p.B * p.Hq)), dim3(kCombThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -273,19 +273,20 @@ __device__ RadixResult radix_regs(SelShared& sh, const uint32_t (&key)[E], uint3
   return r;
 }
 
-// Exact top-k (k < n <= kRegCap) of an index-ordered source; writes the k
-// selected indices ascending to out.
-template <class Src>
-__device__ void topk_regs(SelShared& sh, const Src& src, int n, int k, int32_t* out) {
-  const int E = (n + kSelThreads - 1) / kSelThreads;
-  const int beg = threadIdx.x * E;
-  uint32_t key[kE];
+// Exact top-k (k < n <= E * kSelThreads) of an index-ordered source; writes
+// the k selected indices ascending to out. Each thread holds a contiguous run
+// of the source in E registers.
+template <int E, class Src>
+__device__ void topk_regs_e(SelShared& sh, const Src& src, int n, int k, int32_t* out) {
+  const int run = (n + kSelThreads - 1) / kSelThreads;
+  const int beg = threadIdx.x * run;
+  uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < kE; ++e) key[e] = (e < E && beg + e < n) ? src.key(beg + e) : 0u;
-  const RadixResult r = radix_regs<kE>(sh, key, (uint32_t)k);
+  for (int e = 0; e < E; ++e) key[e] = (e < run && beg + e < n) ? src.key(beg + e) : 0u;
+  const RadixResult r = radix_regs<E>(sh, key, (uint32_t)k);
   uint32_t ngt = 0, neq = 0;
 #pragma unroll
-  for (int e = 0; e < kE; ++e) {
+  for (int e = 0; e < E; ++e) {
     if (!key[e]) continue;
     const uint32_t km = key[e] & r.mask;
     ngt += km > r.prefix;
@@ -296,7 +297,7 @@ __device__ void topk_regs(SelShared& sh, const Src& src, int n, int k, int32_t* 
   uint32_t pos = (excl & 0xffffu) + (r.take_all ? eq_before : (eq_before < r.need ? eq_before : r.need));
   uint32_t eq_rank = eq_before;
 #pragma unroll
-  for (int e = 0; e < kE; ++e) {
+  for (int e = 0; e < E; ++e) {
     if (!key[e]) continue;
     const uint32_t km = key[e] & r.mask;
     bool sel = km > r.prefix;
@@ -306,6 +307,11 @@ __device__ void topk_regs(SelShared& sh, const Src& src, int n, int k, int32_t* 
     }
     if (sel) out[pos++] = src.index(beg + e);
   }
+}
+
+template <class Src>
+__device__ void topk_regs(SelShared& sh, const Src& src, int n, int k, int32_t* out) {
+  topk_regs_e<kE>(sh, src, n, k, out);
 }
 
 struct LdsSrc {
@@ -909,7 +915,7 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
   } else if (total <= (uint32_t)kRegCap) {
     topk_regs(sh, ls, (int)total, k, out);
   } else {
-    topk_stream(sh, ls, (int)total, k, out);
+    topk_regs_e<kDecCandCap / kSelThreads>(sh, ls, (int)total, k, out);
   }
 }
 
