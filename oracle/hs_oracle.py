@@ -45,6 +45,10 @@ design notes of the repository):
   R7 GQA: query head h reads KV head h // G, G = Hq / Hkv.
   R8 the selection decision is taken on float32 scores (float64 evaluation
      rounded once to float32), the precision the kernels decide in.
+  R1' (optional score, score="prob"): the softmax-normalised group score
+     max over h of (scale * <q_h(t), k_g(j)> - lse_h(t)), lse_h(t) the log
+     of the softmax denominator of head h over keys 0..p, i.e. the log of the
+     largest attention probability any head of the group gives token j.
 """
 
 from __future__ import annotations
@@ -146,16 +150,21 @@ def full_attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
 
 
 def selection_scores(q_group: np.ndarray, Kg: np.ndarray, p: int, window: int,
-                     scale: float) -> np.ndarray:
+                     scale: float, lse_group=None) -> np.ndarray:
     """sigma_j for j in C(p), for one query row and one KV group (readings R1, R3).
 
     q_group: [G][d] (the group's query heads); Kg: [n][d]. Returns float64
-    scores of length |C(p)|; position j of the result is token j.
+    scores of length |C(p)|; position j of the result is token j. With
+    lse_group ([G], each head's log-sum-exp over keys 0..p) the score is the
+    softmax-normalised one of reading R1': each head's logit minus its
+    log-sum-exp, then the maximum over the group.
     """
     c = candidate_count(p, window)
     if c == 0:
         return np.zeros(0, dtype=np.float64)
     s = scale * (np.asarray(q_group, np.float64) @ np.asarray(Kg[:c], np.float64).T)
+    if lse_group is not None:
+        s = s - np.asarray(lse_group, np.float64)[:, None]
     return s.max(axis=0)
 
 
@@ -184,14 +193,18 @@ def topk_select(sigma: np.ndarray, k: int):
 
 
 def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
-                          positions, k: int, window: int, scale: float):
+                          positions, k: int, window: int, scale: float, score: str = "logit"):
     """The full-attention layer of a hybrid block for the given query rows.
 
     It computes causal GQA attention and, per (row, KV group), the top-k token
     indices that the following sparse layers reuse [HS2-cs], [DAIR].
-    Returns dict with o [rows][Hq][d], lse [rows][Hq], idx [rows][Hkv][k]
-    (int64), tau [rows][Hkv], sigma (list of per-(row, group) float64 arrays).
+    score: "logit" (reading R1) or "prob" (reading R1', which needs this
+    layer's lse first). Returns dict with o [rows][Hq][d], lse [rows][Hq],
+    idx [rows][Hkv][k] (int64), tau [rows][Hkv], sigma (list of per-(row,
+    group) float64 arrays).
     """
+    if score not in ("logit", "prob"):
+        raise ValueError("score must be 'logit' or 'prob'")
     rows, Hq, d = q.shape
     Hkv = K.shape[0]
     G = _check_gqa(Hq, Hkv)
@@ -203,7 +216,8 @@ def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
         p = int(positions[r])
         row_sig = []
         for g in range(Hkv):
-            s = selection_scores(q[r, g * G:(g + 1) * G], K[g], p, window, scale)
+            lg = lse[r, g * G:(g + 1) * G] if score == "prob" else None
+            s = selection_scores(q[r, g * G:(g + 1) * G], K[g], p, window, scale, lg)
             idx[r, g], tau[r, g] = topk_select(s, k)
             row_sig.append(s)
         sig.append(row_sig)
@@ -237,7 +251,7 @@ def sparse_attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
 
 def decode_step(q_full: np.ndarray, q_sparse: list, kv_new: np.ndarray,
                 K: np.ndarray, V: np.ndarray, length: int, k: int,
-                window: int, scale: float):
+                window: int, scale: float, score: str = "logit"):
     """One decode step of one sequence through a hybrid block.
 
     The new token's key/value row is written at slot length-1 of the cache
@@ -251,7 +265,7 @@ def decode_step(q_full: np.ndarray, q_sparse: list, kv_new: np.ndarray,
     K[:, p] = kv_new[:, 0]
     V[:, p] = kv_new[:, 1]
     pos = np.array([p])
-    res = full_attn_select_rows(q_full[None], K, V, pos, k, window, scale)
+    res = full_attn_select_rows(q_full[None], K, V, pos, k, window, scale, score)
     outs = []
     for qs in q_sparse:
         o, _ = sparse_attention_rows(qs[None], K, V, res["idx"], pos, window, scale)

@@ -377,3 +377,68 @@ def test_lse_combine_of_split_partials():
     o, lse = orc.lse_combine(parts)
     np.testing.assert_allclose(o, whole[0], atol=1e-13)
     np.testing.assert_allclose(lse, whole[1], atol=1e-13)
+
+
+# ---------------------------------------------------------------- normalised score (reading R1')
+
+def test_prob_score_is_log_of_largest_attention_probability():
+    """Pinned on torch.softmax (float64): exp(sigma'_j) equals the largest
+    attention probability that the group's heads give key j, computed by
+    softmax over the causal row independently of the oracle's lse."""
+    rng = np.random.default_rng(41)
+    G, n, d, W = 4, 90, 128, 8
+    q = bf16_exact((1, G, d), rng)
+    K = bf16_exact((1, n, d), rng)
+    V = bf16_exact((1, n, d), rng)
+    scale = orc.default_scale(d)
+    p = n - 1
+    res = orc.full_attn_select_rows(q, K, V, [p], 10, W, scale, score="prob")
+    s = torch.from_numpy(q[0].astype(np.float64)) @ torch.from_numpy(K[0].astype(np.float64)).T * scale
+    prob = torch.softmax(s, dim=1)                      # [G][n], causal row covers 0..p = all keys
+    want = torch.log(prob.max(dim=0).values[:p - W + 1]).numpy()
+    np.testing.assert_allclose(res["sigma"][0][0], want, rtol=0, atol=1e-12)
+
+
+def test_prob_score_with_one_head_ranks_like_the_logit():
+    """G = 1: the normalised score is the logit minus a per-row constant, so
+    the selection equals the logit selection."""
+    rng = np.random.default_rng(42)
+    n, d, W, k = 300, 128, 16, 40
+    q = bf16_exact((3, 2, d), rng)
+    K = bf16_exact((2, n, d), rng)
+    V = bf16_exact((2, n, d), rng)
+    pos = [150, 220, 299]
+    a = orc.full_attn_select_rows(q, K, V, pos, k, W, orc.default_scale(d), score="logit")
+    b = orc.full_attn_select_rows(q, K, V, pos, k, W, orc.default_scale(d), score="prob")
+    assert np.array_equal(a["idx"], b["idx"])
+    for r in range(3):
+        for g in range(2):
+            np.testing.assert_allclose(a["sigma"][r][g] - b["sigma"][r][g], b["lse"][r, g], rtol=0, atol=1e-12)
+
+
+def test_prob_score_prefers_the_sharper_head():
+    """Constructed G = 2 case where the two scores disagree: head A is flat
+    (many equal logits, large lse), head B is peaked. Key x: A gives 3, B
+    gives 0; key y: A gives 0, B gives 2.5. The logit score ranks x first;
+    the normalised score ranks y first because head B concentrates its
+    probability on y (brute force below)."""
+    d, n, W = 128, 40, 1
+    K = np.zeros((1, n, d), np.float32)
+    K[0, :, 2] = 1.0                    # background keys: logit 3 for head A (flat), 0 for B
+    K[0, 0, 2], K[0, 0, 0] = 1.0, 0.0   # key x: A 3, B 0
+    K[0, 1, 2], K[0, 1, 1] = 0.0, 1.0   # key y: A 0, B 2.5
+    q = np.zeros((1, 2, d), np.float32)
+    q[0, 0, 2] = 3.0                    # head A
+    q[0, 1, 1] = 2.5                    # head B
+    V = np.zeros((1, n, d), np.float32)
+    p = n - 1
+    lg = orc.full_attn_select_rows(q, K, V, [p], 1, W, 1.0, score="logit")
+    pr = orc.full_attn_select_rows(q, K, V, [p], 1, W, 1.0, score="prob")
+    # brute force of R1': per head logits over keys 0..p, log-softmax, max over heads
+    Kd = K.astype(np.float64)
+    logits = np.array([[3.0 * Kd[0, j, 2] for j in range(n)], [2.5 * Kd[0, j, 1] for j in range(n)]])
+    lsm = logits - np.log(np.exp(logits).sum(axis=1, keepdims=True))
+    best = lsm[:, :p - W + 1].max(axis=0)
+    assert int(np.argmax(best)) == 1
+    assert lg["idx"][0, 0, 0] != 1 and pr["idx"][0, 0, 0] == 1
+    np.testing.assert_allclose(pr["sigma"][0][0], best, rtol=0, atol=1e-12)
