@@ -105,6 +105,21 @@ typedef enum {
                                    rescan path instead of the sampled
                                    threshold filter (testing hook; same
                                    results, slower) */
+#define HS_FLAG_PROB_SCORE 2u   /* selection score sigma'(j) = max over the
+                                   group's heads h of s_h(j) - lse_h, lse_h
+                                   the natural-log softmax denominator of
+                                   head h over keys 0..p: the log of the
+                                   largest attention probability the group
+                                   gives token j (the pages leave the score
+                                   open; this is the softmax-normalised
+                                   alternative to the logit default). Needs
+                                   the layer's lse first, so the selection
+                                   runs as its own pass after attention
+                                   (prefill: a QK-only pass; decode: a
+                                   second read of the K rows). Affects
+                                   hs_full_attn_select and hs_decode_step;
+                                   lse may still be NULL (kept in the
+                                   workspace). */
 
 typedef struct {
   int32_t batch;       /* B >= 1                                            */

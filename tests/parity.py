@@ -92,8 +92,10 @@ def sample_rows(n_q: int, n_kv: int, top_k: int, window: int, spans=(), evenly=8
     return sorted(r for r in rows if 0 <= r < n_q)
 
 
-def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_sparse=(), o_sparse=(), scale=None):
-    """Checks one prefill call (and its sparse layers) on the given query rows."""
+def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_sparse=(), o_sparse=(), scale=None,
+                  score="logit"):
+    """Checks one prefill call (and its sparse layers) on the given query rows;
+    score names the oracle's selection score ("logit" or "prob")."""
     B, n_q, Hq, d = q_full.shape
     scale = orc.default_scale(d) if scale is None else scale
     rows = list(range(n_q)) if rows is None else list(rows)
@@ -107,7 +109,7 @@ def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_spa
     for b in range(B):
         K, V = cache_np(kv, b, n_kv)
         qb = f32(q_full[b])[rows]
-        res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale)
+        res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale, score)
         full_stats.add(o_np[b, rows], res["o"])
         if lse_np is not None:
             lse_stats.add(lse_np[b][:, rows].T, res["lse"])

@@ -17,10 +17,10 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import HS_FLAG_EXACT_RESCAN, HsError, HsShape  # noqa: F401
+from ._lib import HS_FLAG_EXACT_RESCAN, HS_FLAG_PROB_SCORE, HsError, HsShape  # noqa: F401
 
 __all__ = ["full_attn_select", "sparse_attn_reuse", "decode_step", "make_shape", "HsError",
-           "HS_FLAG_EXACT_RESCAN", "version"]
+           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "version"]
 
 
 def version() -> int:
@@ -118,7 +118,7 @@ def sparse_attn_reuse(q, kv, idx, *, top_k, window, n_kv=None, seq_lens=None, sc
     return o
 
 
-def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.0, with_lse=True,
+def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.0, with_lse=True, flags=0,
                 kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None):
     """Decode full-attention layer: append kv_new at seq_lens[b]-1, attend, select once.
 
@@ -134,7 +134,7 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
     if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda:
         raise TypeError("seq_lens must be an int32 device tensor")
     shape = make_shape(batch=B, n_q=1, n_kv=0, kv_capacity=kv_capacity, q_heads=Hq, kv_heads=kv_heads,
-                       top_k=top_k, window=window, scale=scale, kv_strides=kv_strides, head_dim=d)
+                       top_k=top_k, window=window, scale=scale, kv_strides=kv_strides, flags=flags, head_dim=d)
     dev = q.device
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if with_lse else None

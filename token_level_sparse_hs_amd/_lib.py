@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libhysparse.so")
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE, HS_ERR_HIP, HS_ERR_INTERNAL = range(6)
 HS_OP_FULL_ATTN_SELECT, HS_OP_SPARSE_ATTN_REUSE, HS_OP_DECODE_STEP = range(3)
 HS_FLAG_EXACT_RESCAN = 1
+HS_FLAG_PROB_SCORE = 2
 
 EXPORTED = ("hs_workspace_size", "hs_full_attn_select", "hs_sparse_attn_reuse", "hs_decode_step",
             "hs_timing_enable", "hs_timing_read", "hs_status_string", "hs_last_error", "hs_version")

@@ -82,7 +82,8 @@ hs_status validate_common(const hs_shape* s, Layout* lay) {
   if (s->window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", s->window);
   if (s->kv_capacity < 1) return fail(HS_ERR_INVALID_ARG, "kv_capacity must be >= 1");
   if (!(s->scale >= 0.f) || std::isinf(s->scale)) return fail(HS_ERR_INVALID_ARG, "scale must be finite and >= 0");
-  if ((s->flags & ~HS_FLAG_EXACT_RESCAN) != 0) return fail(HS_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  if ((s->flags & ~(HS_FLAG_EXACT_RESCAN | HS_FLAG_PROB_SCORE)) != 0)
+    return fail(HS_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
   Layout l;
   if (s->kv_stride_b == 0 && s->kv_stride_h == 0 && s->kv_stride_t == 0 && s->kv_v_offset == 0) {
     l.st = 2 * 128;
@@ -121,7 +122,8 @@ struct PrefillPlan {
   int max_samples = 0;
   bool sample = false;
   size_t off_theta = 0, off_counts = 0, off_bs = 0, off_bj = 0, off_samples = 0, off_stat = 0, off_defer = 0,
-         total = 0;
+         off_lse = 0, total = 0;
+  bool prob = false;  // probability score: selection pass after attention, lse kept here
 };
 
 PrefillPlan plan_prefill(const hs_shape* s) {
@@ -148,6 +150,11 @@ PrefillPlan plan_prefill(const hs_shape* s) {
   o = align_up(o + 4);
   p.off_defer = o;  // queued rows of the selection, then their count
   o = align_up(o + (size_t)p.rows * 4 + 4);
+  p.prob = (s->flags & HS_FLAG_PROB_SCORE) != 0;
+  if (p.prob) {
+    p.off_lse = o;
+    o = align_up(o + (size_t)s->batch * s->q_heads * s->n_q * 4);
+  }
   p.total = o;
   return p;
 }
@@ -157,7 +164,9 @@ struct DecodePlan {
   bool in_block = false;  // sparse decode: splits merged inside the block
   int64_t sigma_stride = 0;
   int sel_slices = 0;     // sliced selection (0: one block per row)
-  size_t off_sigma = 0, off_part = 0, off_theta = 0, off_segcnt = 0, off_segkey = 0, off_segidx = 0, total = 0;
+  bool prob = false;      // probability score: score pass after the full layer
+  size_t off_sigma = 0, off_part = 0, off_theta = 0, off_segcnt = 0, off_segkey = 0, off_segidx = 0, off_lse = 0,
+         total = 0;
 };
 
 // Splits a per-(b, g) key stream of up to `nkeys` keys so that the grid holds
@@ -218,6 +227,11 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
     o = align_up(o + seg * hs::kDecSlice * 4);
     p.off_segidx = o;
     o = align_up(o + seg * hs::kDecSlice * 4);
+  }
+  p.prob = s->top_k > 0 && (s->flags & HS_FLAG_PROB_SCORE) != 0;
+  if (p.prob) {
+    p.off_lse = o;
+    o = align_up(o + (size_t)s->batch * s->q_heads * 4);
   }
   p.total = o;
   return p;
@@ -409,6 +423,25 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
   const hs::KvView kvv = kv_view(kv, lay);
   const bool select = s->top_k > 0;
   float* theta = select ? reinterpret_cast<float*>(w + plan.off_theta) : nullptr;
+  // probability score: attention first (its lse feeds the score), then the
+  // sampled threshold and a QK-only candidate pass
+  const bool prob = select && plan.prob;
+  float* lse_buf = prob && !lse ? reinterpret_cast<float*>(w + plan.off_lse) : lse;
+
+  hs::PrefillParams pp{};
+  pp.q = static_cast<const uint16_t*>(q);
+  pp.kv = kvv;
+  pp.o = static_cast<uint16_t*>(o);
+  pp.lse = lse_buf;
+  pp.B = s->batch; pp.n_q = s->n_q; pp.n_kv = s->n_kv; pp.Hq = s->q_heads; pp.Hkv = s->kv_heads; pp.window = s->window;
+  pp.scale = scale;
+  pp.select = select && !prob ? 1 : 0;
+  pp.theta = theta;
+  pp.buf_sigma = select ? reinterpret_cast<float*>(w + plan.off_bs) : nullptr;
+  pp.buf_j = select ? reinterpret_cast<int32_t*>(w + plan.off_bj) : nullptr;
+  pp.counts = select ? reinterpret_cast<int32_t*>(w + plan.off_counts) : nullptr;
+  pp.cap = plan.cap;
+  if (prob) HIP_TRY(timed("prefill_attn", hst, [&] { return hs::launch_prefill_attn(pp, hst); }));
 
   if (select) {
     if (plan.sample) {
@@ -418,6 +451,7 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
       sp.B = s->batch; sp.n_q = s->n_q; sp.n_kv = s->n_kv; sp.Hq = s->q_heads; sp.Hkv = s->kv_heads;
       sp.window = s->window; sp.scale = scale; sp.stride = plan.stride; sp.max_samples = plan.max_samples;
       sp.samples = reinterpret_cast<float*>(w + plan.off_samples);
+      sp.lse = prob ? lse_buf : nullptr;
       HIP_TRY(timed("sample_scores", hst, [&] { return hs::launch_sample_scores(sp, hst); }));
     }
     hs::ThresholdParams tp{};
@@ -429,20 +463,13 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
     HIP_TRY(timed("threshold", hst, [&] { return hs::launch_threshold(tp, plan.rows, hst); }));
   }
 
-  hs::PrefillParams pp{};
-  pp.q = static_cast<const uint16_t*>(q);
-  pp.kv = kvv;
-  pp.o = static_cast<uint16_t*>(o);
-  pp.lse = lse;
-  pp.B = s->batch; pp.n_q = s->n_q; pp.n_kv = s->n_kv; pp.Hq = s->q_heads; pp.Hkv = s->kv_heads; pp.window = s->window;
-  pp.scale = scale;
-  pp.select = select ? 1 : 0;
-  pp.theta = theta;
-  pp.buf_sigma = select ? reinterpret_cast<float*>(w + plan.off_bs) : nullptr;
-  pp.buf_j = select ? reinterpret_cast<int32_t*>(w + plan.off_bj) : nullptr;
-  pp.counts = select ? reinterpret_cast<int32_t*>(w + plan.off_counts) : nullptr;
-  pp.cap = plan.cap;
-  HIP_TRY(timed("prefill_attn", hst, [&] { return hs::launch_prefill_attn(pp, hst); }));
+  if (prob) {
+    hs::PrefillParams cp = pp;
+    cp.select = 1;
+    HIP_TRY(timed("score_pass", hst, [&] { return hs::launch_score_pass(cp, hst); }));
+  } else {
+    HIP_TRY(timed("prefill_attn", hst, [&] { return hs::launch_prefill_attn(pp, hst); }));
+  }
 
   if (select) {
     hs::SelectParams sp{};
@@ -456,6 +483,7 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
     sp.rescan_count = nullptr;
     sp.defer_rows = reinterpret_cast<int32_t*>(w + plan.off_defer);
     sp.defer_count = reinterpret_cast<uint32_t*>(w + plan.off_defer + (size_t)plan.rows * 4);
+    sp.lse = prob ? lse_buf : nullptr;
     HIP_TRY(timed("select_prefill", hst, [&] { return hs::launch_select_prefill(sp, plan.rows, hst); }));
   }
   return ok();
@@ -552,22 +580,31 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   dp.seq_lens = seq_lens;
   dp.splits = plan.splits; dp.split_len = plan.split_len;
   dp.o = static_cast<uint16_t*>(o);
-  dp.lse = lse;
+  float* lse_buf = plan.prob && !lse ? reinterpret_cast<float*>(w + plan.off_lse) : lse;
+  dp.lse = lse_buf;
   dp.part = reinterpret_cast<float*>(w + plan.off_part);
-  dp.sigma = s->top_k > 0 ? reinterpret_cast<float*>(w + plan.off_sigma) : nullptr;
+  float* sigma = s->top_k > 0 ? reinterpret_cast<float*>(w + plan.off_sigma) : nullptr;
+  dp.sigma = plan.prob ? nullptr : sigma;  // the probability score is written by its own pass
   dp.sigma_stride = plan.sigma_stride;
   HIP_TRY(timed("decode_full", hst, [&] { return hs::launch_decode_full(dp, hst); }));
   if (plan.splits > 1) {
     hs::CombineParams cp{};
-    cp.part = dp.part; cp.o = dp.o; cp.lse = lse; cp.seq_lens = seq_lens;
+    cp.part = dp.part; cp.o = dp.o; cp.lse = lse_buf; cp.seq_lens = seq_lens;
     cp.B = s->batch; cp.Hq = s->q_heads; cp.Hkv = s->kv_heads; cp.splits = plan.splits; cp.split_len = plan.split_len;
     cp.sparse_k = -1; cp.window = s->window; cp.max_len = max_seq_len;
     HIP_TRY(timed("lse_combine", hst, [&] { return hs::launch_combine(cp, hst); }));
   }
+  if (plan.prob) {
+    hs::DecodeScoreParams zp{};
+    zp.q = dp.q; zp.kv = dp.kv; zp.seq_lens = seq_lens; zp.lse = lse_buf;
+    zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
+    zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window;
+    HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
+  }
   if (s->top_k > 0) {
     hs::SelectDecodeParams sp{};
     sp.B = s->batch; sp.Hkv = s->kv_heads; sp.top_k = s->top_k; sp.window = s->window;
-    sp.seq_lens = seq_lens; sp.sigma = dp.sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = idx;
+    sp.seq_lens = seq_lens; sp.sigma = sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = idx;
     sp.nslices = plan.sel_slices;
     if (plan.sel_slices > 0) {
       sp.theta_key = reinterpret_cast<uint32_t*>(w + plan.off_theta);

@@ -37,10 +37,15 @@ struct SampleParams {
   int stride;       // sampled keys j = s * stride
   int max_samples;  // row stride of `samples`
   float* samples;   // [rows][max_samples]
+  const float* lse; // probability score: [B][Hq][n_q] log-sum-exp; null for the logit score
 };
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_sample_scores(const SampleParams& p, hipStream_t s);
+// Probability-score candidate pass: the selection part of the prefill
+// attention kernel alone (QK, group maximum of scale*s - lse, threshold
+// compaction into buf_sigma / buf_j / counts), reading lse from p.lse.
+hipError_t launch_score_pass(const PrefillParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ selection
 struct SelectParams {
@@ -57,6 +62,7 @@ struct SelectParams {
   uint32_t* rescan_count;  // optional counter of rows that took the rescan
   int32_t* defer_rows;     // [rows] rows left to the block-wide path
   uint32_t* defer_count;   // zeroed by the threshold kernel of the same call
+  const float* lse;        // probability score: [B][Hq][n_q] for the exact rescan; null: logit score
 };
 
 struct ThresholdParams {
@@ -86,6 +92,22 @@ struct SelectDecodeParams {
 constexpr int kDecSlice = 16384;
 constexpr int kSelRegKeys = 8192;
 constexpr int kMaxDecSlices = 1024;
+
+// Decode probability-score row: sigma[(b,g)][j] = max over the group's heads
+// of fl(scale * <q_h, k_j>) - lse_h for j in C(p), fp32 dot products in
+// dimension order.
+struct DecodeScoreParams {
+  const uint16_t* q;  // [B][Hq][128]
+  KvView kv;
+  const int32_t* seq_lens;
+  const float* lse;   // [B][Hq]
+  int B, Hq, Hkv, window;
+  float scale;
+  float* sigma;       // [B*Hkv][sigma_stride]
+  int64_t sigma_stride;
+  int max_cand;       // bound on |C(p)| over the batch (grid size)
+};
+hipError_t launch_decode_prob_score(const DecodeScoreParams& p, hipStream_t s);
 
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s);
 hipError_t launch_threshold(const ThresholdParams& p, int64_t rows, hipStream_t s);

@@ -113,6 +113,12 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int b, int n_q, int Hq
   asm volatile("v_max_f32_dpp %0, %1, %1 row_ror:" #ROR " row_mask:0xf bank_mask:" #BANKS : "+v"(dst) \
                : "v"(src), "v"(dep))
 
+// The group maximum reads the scores through DPP from inline assembly, so
+// the compiler does not insert the two wait states a DPP read needs after a
+// vector write of its source: callers that have just rewritten the scores
+// with vector code pause here first.
+__device__ __forceinline__ void dpp_read_pause(f32x16& a, f32x16& b) { asm volatile("s_nop 1" : "+v"(a), "+v"(b)); }
+
 // Writes the group-max scores of the wave's tile into sig[TPW][64] (raw,
 // unscaled). acc[c][i] holds key 32c + 8(i/4) + 4h + i%4 of MFMA row n.
 // Transposing steps halve the values each lane carries instead of
@@ -469,6 +475,10 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
 
   bf16x8 qb[8];
   load_q<G>(P.q, b, P.n_q, P.Hq, g, tok, qb);
+  // probability score: each lane's column subtracts its head's log-sum-exp
+  const bool prob = P.lse != nullptr;
+  const float lse_col =
+      prob && tok < P.n_q ? P.lse[((int64_t)b * P.Hq + g * G + head_of<G>(n)) * P.n_q + tok] : 0.f;
 
   const int p_bhi = off + imin(t0 + TPB, P.n_q) - 1;
   const int ncand_hi = imax(0, p_bhi - P.window + 1);
@@ -496,6 +506,13 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
       f32x16 acc[2];
       qk_tile(Ks, qb, acc);
       mfma_settle<kSettle32>(acc[0], acc[1]);
+      if (prob) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(acc[c][i], P.scale, -lse_col);
+        dpp_read_pause(acc[0], acc[1]);
+      }
       float* ws = sig[wave];
       stage_group_max<G>(acc, ws, fmaxf(acc[0][15], acc[1][15]));
       lds_wait();
@@ -508,11 +525,119 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
         const int ns = (ncand + P.stride - 1) / P.stride;
         if (s < ns) {
           const int64_t row = ((int64_t)b * P.n_q + tk) * P.Hkv + g;
-          P.samples[row * P.max_samples + s] = ws[u * 64 + lane] * P.scale;
+          P.samples[row * P.max_samples + s] = prob ? ws[u * 64 + lane] : ws[u * 64 + lane] * P.scale;
         }
       }
     }
     __syncthreads();
+  }
+}
+
+// Probability-score candidates, after the attention pass has produced lse:
+// the selection of the prefill attention kernel on its own. Per 64-key tile,
+// S^T = K Q^T, each lane's column turned into scale * s - lse of its head
+// (one rounding), the group maximum over the G heads staged in LDS, and every
+// candidate j <= p - W at or above its row's threshold appended in ascending
+// key order (same buffers and counts as the fused path). K tiles go through
+// registers into padded LDS tiles, the next tile's rows in flight while the
+// current one is scored.
+template <int G>
+__global__ __launch_bounds__(256, 2) void score_pass_kernel(PrefillParams P) {
+  constexpr int TPW = 32 / G;
+  constexpr int TPB = 4 * TPW;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
+  __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int ntq = (P.n_q + TPB - 1) / TPB;
+  int L = blockIdx.x;
+  const int g = L % P.Hkv;
+  L /= P.Hkv;
+  const int b = L % P.B;
+  L /= P.B;
+  const int t0 = (ntq - 1 - L) * TPB;
+  const int off = P.n_kv - P.n_q;
+  const int wt0 = t0 + wave * TPW;
+  const int tok = wt0 + tok_of<G>(n);
+  const bool wave_live = wt0 < P.n_q;
+
+  bf16x8 qb[8];
+  load_q<G>(P.q, b, P.n_q, P.Hq, g, tok, qb);
+  const float lse_col = tok < P.n_q ? P.lse[((int64_t)b * P.Hq + g * G + head_of<G>(n)) * P.n_q + tok] : 0.f;
+
+  const int64_t row0 = uniform64(((int64_t)b * P.n_q + wt0) * P.Hkv + g);
+  float theta[TPW];
+  int cnt[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const bool ok = wt0 + u < P.n_q;
+    theta[u] = ok ? __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, P.theta[row0 + (int64_t)u * P.Hkv])))
+                  : kPosInf;
+    cnt[u] = 0;
+  }
+  // last candidate key of the block and of this wave (< 0: none)
+  const int jb = off + imin(t0 + TPB, P.n_q) - 1 - P.window;
+  const int jw = wave_live ? off + imin(wt0 + TPW, P.n_q) - 1 - P.window : -1;
+  const int ntiles = jb >= 0 ? jb / 64 + 1 : 0;
+
+  // tile loader: thread (kq, dq) moves rows 4kq .. 4kq+3, 16-byte chunk dq
+  const int dq = tid & 15, kq = tid >> 4;
+  const uint16_t* slab = P.kv.slab(b, g);
+  u32x4 kw[4];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = imin(kt * 64 + 4 * kq + r, jb);  // rows past the last candidate: any valid row
+      kw[r] = ld16(slab + (uint32_t)(j * P.kv.st) + 8 * dq);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st16(&Ks[buf][(4 * kq + r) * kKS + 8 * dq], kw[r]);
+  };
+  if (ntiles > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) load(kt + 1);
+    const int key0 = kt * 64;
+    if (key0 <= jw) {
+      f32x16 acc[2];
+      qk_tile(Ks[buf], qb, acc);
+      mfma_settle<kSettle32>(acc[0], acc[1]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(acc[c][i], P.scale, -lse_col);
+      dpp_read_pause(acc[0], acc[1]);
+      float* ws = sig[wave];
+      stage_group_max<G>(acc, ws, fmaxf(acc[0][15], acc[1][15]));
+      lds_wait();
+      const int j = key0 + lane;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const float v = ws[u * 64 + lane];
+        const bool pass = j <= off + wt0 + u - P.window && v >= theta[u];
+        const uint64_t m = ballot(pass);
+        const uint32_t o = pass ? 4u * ((uint32_t)cnt[u] + lane_prefix(m)) : kDropOffset;
+        const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap;  // wave-uniform row base
+        buf_st4(make_rsrc_sized(P.buf_sigma + rb, 4u * (uint32_t)P.cap), o, __float_as_uint(v));
+        buf_st4(make_rsrc_sized(P.buf_j + rb, 4u * (uint32_t)P.cap), o, (uint32_t)j);
+        cnt[u] = uniform(cnt[u] + __popcll(m));
+      }
+    }
+    if (kt + 1 < ntiles) store(buf ^ 1);
+    __syncthreads();
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+      if (wt0 + u < P.n_q) P.counts[row0 + (int64_t)u * P.Hkv] = cnt[u];
   }
 }
 
@@ -532,7 +657,25 @@ hipError_t launch_sample_g(const SampleParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int G>
+hipError_t launch_score_pass_g(const PrefillParams& p, hipStream_t s) {
+  constexpr int TPB = 4 * (32 / G);
+  const int64_t blocks = (int64_t)((p.n_q + TPB - 1) / TPB) * p.B * p.Hkv;
+  score_pass_kernel<G><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_score_pass(const PrefillParams& p, hipStream_t s) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_score_pass_g<1>(p, s);
+    case 2: return launch_score_pass_g<2>(p, s);
+    case 4: return launch_score_pass_g<4>(p, s);
+    case 8: return launch_score_pass_g<8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   switch (p.Hq / p.Hkv) {

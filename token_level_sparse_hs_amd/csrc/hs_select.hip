@@ -131,13 +131,15 @@ struct BufSrc {
 
 // Scores recomputed from the group's query heads (fp32 copy in LDS) and the
 // cache: sigma_j = max_h fl(scale * <q_h, k_j>), dot products in fp32, in
-// dimension order.
+// dimension order; with per-head log-sum-exps ls, the probability score
+// max_h fl(scale * <q_h, k_j> - ls_h).
 struct RescanSrc {
   const float* qs;  // LDS [G][128]
   const uint16_t* krow0;
   int64_t kstride;
   int G;
   float scale;
+  const float* ls;  // LDS [G] or null
   __device__ uint32_t key(int i) const {
     const uint16_t* kr = krow0 + (int64_t)i * kstride;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -155,7 +157,7 @@ struct RescanSrc {
     float best = kNegInf;
 #pragma unroll
     for (int h = 0; h < 8; ++h)
-      if (h < G) best = fmaxf(best, acc[h] * scale);
+      if (h < G) best = fmaxf(best, ls ? fmaf(acc[h], scale, -ls[h]) : acc[h] * scale);
     return score_key(best);
   }
   __device__ __forceinline__ int32_t index(int i) const { return i; }
@@ -627,7 +629,10 @@ __device__ void select_prefill_row(const SelectParams& P, int64_t row, SelShared
     qs[i] = __uint_as_float((uint32_t)v << 16);
   }
   __syncthreads();
-  RescanSrc src{qs, P.kv.slab(b, g), P.kv.st, G, P.scale};
+  float* ls = qs + G * kHeadDim;  // the group's log-sum-exps (probability score)
+  if (P.lse && threadIdx.x < G) ls[threadIdx.x] = P.lse[((int64_t)b * P.Hq + g * G + threadIdx.x) * P.n_q + t];
+  __syncthreads();
+  RescanSrc src{qs, P.kv.slab(b, g), P.kv.st, G, P.scale, P.lse ? ls : nullptr};
   topk_any<BIG>(sh, lds.key, lds.idx, src, ncand, P.top_k, out);
   if (threadIdx.x == 0 && P.rescan_count) atomicAdd(P.rescan_count, 1u);
 }
@@ -637,7 +642,7 @@ template <bool BIG>
 __global__ __launch_bounds__(kSelThreads) void select_prefill_deferred_kernel(SelectParams P) {
   __shared__ SelShared sh;
   __shared__ SelLds<BIG> lds;
-  __shared__ float qs[8 * kHeadDim];
+  __shared__ float qs[8 * kHeadDim + 8];
   const uint32_t n = *reinterpret_cast<volatile const uint32_t*>(P.defer_count);
   for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
     select_prefill_row<BIG>(P, P.defer_rows[li], sh, lds, qs);
@@ -917,6 +922,81 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
   } else {
     topk_regs_e<kDecCandCap / kSelThreads>(sh, ls, (int)total, k, out);
   }
+}
+
+// Decode probability-score row (after the full layer has produced lse):
+// tiles of 16 keys x 16 columns (the group's G heads, zero columns beyond)
+// on v_mfma_f32_16x16x32_bf16, each head's column turned into
+// scale * s - lse_h (one rounding), the maximum across the G head lanes,
+// one store per 4 keys. Each wave walks kDecScoreWaveKeys keys of one (b, g)
+// row with four 16-key chunks (16 loads per lane) in flight.
+constexpr int kDecScoreWaveKeys = 256;
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_prob_score_kernel(DecodeScoreParams P) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.y;  // b * Hkv + g
+  const int b = row / P.Hkv, g = row % P.Hkv;
+  const int ncand = imax(0, P.seq_lens[b] - P.window);  // p - W + 1 with p = seq_len - 1
+  const int j0 = ((int)blockIdx.x * 4 + wave) * kDecScoreWaveKeys;
+  if (j0 >= ncand) return;
+  const int col = lane & 15, kg = lane >> 4;
+  // B operand: head `col` of the group, dims 32s + 8kg .. +8 (zero past G)
+  bf16x8 qb[4];
+  const uint16_t* qrow = P.q + ((int64_t)b * P.Hq + g * G + (col < G ? col : 0)) * kHeadDim;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qb[s] = as_bf16x8(col < G ? ld16(qrow + 32 * s + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
+  const float lse_col = col < G ? P.lse[(int64_t)b * P.Hq + g * G + col] : 0.f;
+  const uint16_t* slab = P.kv.slab(b, g);
+  float* srow = P.sigma + (int64_t)row * P.sigma_stride;
+  const int jend = imin(ncand, j0 + kDecScoreWaveKeys);
+  for (int c0 = j0; c0 < jend; c0 += 64) {
+    // A operand: key c0 + 16ch + col, dims 32s + 8kg .. +8 (rows past the
+    // last candidate read the last one; their scores are not stored)
+    u32x4 kw[4][4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int j = imin(c0 + 16 * ch + col, ncand - 1);
+      const uint16_t* kr = slab + (uint32_t)(j * P.kv.st);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kw[ch][s] = ld16(kr + 32 * s + 8 * kg);
+    }
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(kw[ch][s]), qb[s], acc);
+      mfma_settle<kSettle16>(acc);
+      // lane (kg, col) holds keys 4kg + i of the chunk for head col
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = group_max<G>(col < G ? fmaf(acc[i], P.scale, -lse_col) : kNegInf);
+      const int jk = c0 + 16 * ch + 4 * kg;
+      if (col == 0) {
+        if (jk + 3 < ncand) {
+          *reinterpret_cast<f32x4*>(srow + jk) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (jk + i < ncand) srow[jk + i] = v[i];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_decode_prob_score(const DecodeScoreParams& p, hipStream_t s) {
+  const unsigned gx = (unsigned)((std::max(p.max_cand, 1) + 4 * kDecScoreWaveKeys - 1) / (4 * kDecScoreWaveKeys));
+  const dim3 grid(gx, (unsigned)(p.B * p.Hkv));
+  switch (p.Hq / p.Hkv) {
+    case 1: decode_prob_score_kernel<1><<<grid, dim3(256), 0, s>>>(p); break;
+    case 2: decode_prob_score_kernel<2><<<grid, dim3(256), 0, s>>>(p); break;
+    case 4: decode_prob_score_kernel<4><<<grid, dim3(256), 0, s>>>(p); break;
+    case 8: decode_prob_score_kernel<8><<<grid, dim3(256), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s) {
