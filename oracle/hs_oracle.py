@@ -70,6 +70,8 @@ __all__ = [
     "sparse_attention_rows",
     "decode_step",
     "lse_combine",
+    "fp8_scale_exponent",
+    "quantize_fp8",
 ]
 
 
@@ -287,3 +289,34 @@ def lse_combine(parts):
     tot = w.sum(axis=0)
     o = sum(w[i][:, None] * np.asarray(parts[i][0], np.float64) for i in range(len(parts)))
     return o / tot[:, None], m + np.log(tot)
+
+
+# ---------------------------------------------------------------- FP8 cache
+
+E4M3_MAX = 448.0
+
+
+def fp8_scale_exponent(amax: float) -> int:
+    """Smallest e with amax <= 448 * 2^e (e = 0 for an all-zero head): the
+    power-of-two scale of one KV head's K (or V) rows in the FP8 cache, so
+    that every value divided by 2^e lies within the e4m3 range and the
+    dequantised values (e4m3 times 2^e) are exactly representable in bf16."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = math.frexp(amax)[1] - 9
+    while amax > E4M3_MAX * 2.0 ** e:
+        e += 1
+    while amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return e
+
+
+def quantize_fp8(x: np.ndarray, e: int):
+    """e4m3 codes of x / 2^e, clamped to +-448, rounded to nearest (ties to
+    even) by torch's float8_e4m3fn conversion; returns (codes as uint8,
+    dequantised float64 values codes * 2^e)."""
+    import torch
+    y = torch.from_numpy(np.asarray(x, np.float64) * 2.0 ** (-e)).clamp(-E4M3_MAX, E4M3_MAX)
+    q = y.to(torch.float32).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), q.to(torch.float64).numpy() * 2.0 ** e

@@ -442,3 +442,66 @@ def test_prob_score_prefers_the_sharper_head():
     assert int(np.argmax(best)) == 1
     assert lg["idx"][0, 0, 0] != 1 and pr["idx"][0, 0, 0] == 1
     np.testing.assert_allclose(pr["sigma"][0][0], best, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- FP8 cache quantiser
+
+def _e4m3_values():
+    """All finite e4m3 values with their codes, from the format's definition
+    (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+    subnormal; code 0x7f / 0xff is NaN, so 448 is the largest value)."""
+    vals = {}
+    for code in range(256):
+        s, ex, m = code >> 7, (code >> 3) & 15, code & 7
+        if ex == 15 and m == 7:
+            continue
+        mag = (m / 8.0) * 2.0 ** -6 if ex == 0 else (1 + m / 8.0) * 2.0 ** (ex - 7)
+        vals[code] = -mag if s else mag
+    return vals
+
+
+def test_fp8_conversion_is_round_to_nearest_even_by_brute_force():
+    """Pins the quantiser's rounding on the e4m3 definition: every in-range
+    input maps to the nearest e4m3 value, ties to the even code."""
+    vals = _e4m3_values()
+    pos = sorted((v, c) for c, v in vals.items() if v >= 0 and not (v == 0 and c == 0x80))
+    rng = np.random.default_rng(51)
+    xs = list(rng.uniform(-448, 448, 3000)) + list(rng.standard_normal(2000) * 2.0 ** rng.uniform(-10, 8, 2000))
+    mids = [(a[0] + b[0]) / 2 for a, b in zip(pos[:-1], pos[1:])]
+    xs += mids + [-m for m in mids]
+    xs = np.array(xs, np.float32).astype(np.float64)  # float32-exact inputs
+    codes, deq = orc.quantize_fp8(xs, 0)
+    for x, c, d in zip(xs, codes, deq):
+        mag = abs(x)
+        best = min(pos, key=lambda vc: (abs(vc[0] - mag), vc[1] & 1))  # nearest, then even code
+        assert abs(d) == best[0], (x, d, best)
+        if d != 0:
+            assert (d < 0) == (x < 0)
+
+
+def test_fp8_scale_exponent_bounds():
+    for amax in [1e-30, 0.013, 1.0, 3.7, 447.99, 448.0, 448.01, 896.0, 1e6]:
+        e = orc.fp8_scale_exponent(amax)
+        assert amax <= 448.0 * 2.0 ** e
+        assert amax > 448.0 * 2.0 ** (e - 1)
+    assert orc.fp8_scale_exponent(0.0) == 0
+
+
+def test_fp8_quantiser_error_bound_and_exact_values():
+    """Dequantised values: within 2^-4 relative of the input in the normal
+    range (3 mantissa bits, round to nearest); values that are e4m3 numbers
+    times 2^e round-trip exactly; the head maximum lands at or below 448."""
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((64, 128)) * 3.0
+    e = orc.fp8_scale_exponent(np.abs(x).max())
+    codes, deq = orc.quantize_fp8(x, e)
+    normal = np.abs(x) >= 2.0 ** (e - 6)
+    rel = np.abs(deq - x)[normal] / np.abs(x)[normal]
+    assert rel.max() <= 2.0 ** -4
+    assert np.abs(deq).max() <= 448.0 * 2.0 ** e
+    exact = np.array([v for v in _e4m3_values().values()]) * 2.0 ** e
+    _, back = orc.quantize_fp8(exact, e)
+    assert np.array_equal(back, exact)
+    # values past the range saturate instead of becoming NaN
+    _, sat = orc.quantize_fp8(np.array([1e9, -1e9]), 0)
+    assert list(sat) == [448.0, -448.0]
