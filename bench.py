@@ -96,7 +96,39 @@ def run_prefill(args, hs, synth, _lib, torch):
     log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step")
     for k, (n, tot) in sorted(kt.items(), key=lambda x: -x[1][1]):
         log(f"[bench]   {k:16s} launches={n:5d} avg={tot / n * 1e3:10.1f} us  share/step={tot / args.steps:8.3f} ms")
-    return w, ms_per_step, kt, case
+    variants = prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch)
+    return w, ms_per_step, kt, case, variants
+
+
+def prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch):
+    """Options beside the default path, timed on the same inputs (not part
+    of `value`): the probability selection score (full layer) and the
+    sparse layers gathering from the FP8 copy of the cache."""
+    _, _, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, workspace=ws)
+    copy = hs.kv_to_fp8(kv, n_kv=w.n_kv)
+    runs = {
+        "prob_score_full_layer": lambda: hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window,
+                                                             flags=hs.HS_FLAG_PROB_SCORE, workspace=ws),
+        "fp8_cache_conversion": lambda: hs.kv_to_fp8(kv, n_kv=w.n_kv, out=copy),
+        "fp8_sparse_layer": lambda: hs.sparse_attn_reuse(qs[0], kv, idx, top_k=w.top_k, window=w.window,
+                                                         n_kv=w.n_kv, kv_fp8=copy),
+    }
+    out = {}
+    for name, fn in runs.items():
+        fn()
+        torch.cuda.synchronize()
+        _lib.timing_read()
+        _lib.timing_enable(True)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        _lib.timing_enable(False)
+        kt = _lib.timing_read()
+        out[name] = {"ms": round(sum(t for n, t in kt.values()) / 3, 3),
+                     "kernels_us": {k: round(t / n * 1e3, 1) for k, (n, t) in kt.items()}}
+        log(f"[bench] {w.name} {name}: {out[name]}")
+    del copy
+    return out
 
 
 def traffic_probe(args, hs, synth, _lib, torch):
@@ -183,6 +215,28 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
     torch.cuda.synchronize()
     us_graph = (time.perf_counter() - t0) * 1e6 / steps
     log(f"[bench] {wname}: {us_graph:.1f} us/step as one graph launch")
+    # option: the sparse layers gathering from the FP8 copy of the cache
+    copy = hs.kv_to_fp8(kv, n_kv=cap)
+    st = case["steps"][0]
+    _, _, idx0 = hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
+                                window=w.window, workspace=ws_full)
+    hs.kv_to_fp8(kv, seq_lens=seqs[0], out=copy)
+    hs.sparse_attn_reuse(st["q_sparse"][0], kv, idx0, top_k=w.top_k, window=w.window, seq_lens=seqs[0],
+                         workspace=ws_sp, kv_fp8=copy)
+    torch.cuda.synchronize()
+    _lib.timing_read()
+    _lib.timing_enable(True)
+    for x in st["q_sparse"]:
+        hs.sparse_attn_reuse(x, kv, idx0, top_k=w.top_k, window=w.window, seq_lens=seqs[0], workspace=ws_sp,
+                             kv_fp8=copy)
+    hs.kv_to_fp8(kv, seq_lens=seqs[0], out=copy)
+    torch.cuda.synchronize()
+    _lib.timing_enable(False)
+    kf = _lib.timing_read()
+    fp8_sparse_us = kf["sparse_decode"][1] / kf["sparse_decode"][0] * 1e3
+    fp8_append_us = kf["kv_fp8_convert"][1] / kf["kv_fp8_convert"][0] * 1e3
+    log(f"[bench] {wname}: fp8 sparse layer {fp8_sparse_us:.1f} us, appended-row conversion {fp8_append_us:.1f} us")
+    del copy
     # algorithmic bytes
     full_bytes = sum(512.0 * w.Hkv * (L + s + 1) for L in lengths for s in range(steps)) / steps
     sp_rows = sum(min(w.top_k, max(0, L + s + 1 - w.window)) + min(w.window, L + s + 1)
@@ -197,6 +251,8 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
         "us_per_step": round(us_step, 2),
         "us_per_step_graph": round(us_graph, 2),
         "sparse_layer_kernel_us": round(sp_us, 2),
+        "fp8_sparse_layer_kernel_us": round(fp8_sparse_us, 2),
+        "fp8_append_conversion_us": round(fp8_append_us, 2),
         "kernels": {k: {"launches_per_step": n / steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()},
         "sparse_decode_roofline": {"bound": "hbm", "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -310,7 +366,7 @@ def main():
         traffic_probe(args, hs, synth, _lib, torch)
         return
 
-    w, ms_step, kt, case = run_prefill(args, hs, synth, _lib, torch)
+    w, ms_step, kt, case, variants = run_prefill(args, hs, synth, _lib, torch)
     counts = prefill_counts(w)
     tokens = w.B * w.n_q
     value = tokens / (ms_step * 1e-3)
@@ -403,6 +459,7 @@ def main():
         "roofline_full_layer": roof_full,
         "full_layer_ms": round(full_layer_ms, 3),
         "sparse_prefill_layer": sparse_prefill,
+        "prefill_options": variants,
         "kernels": kernels,
         "decode": decode,
         "decode_ctx1m": decode_1m,

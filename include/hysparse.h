@@ -120,6 +120,15 @@ typedef enum {
                                    hs_full_attn_select and hs_decode_step;
                                    lse may still be NULL (kept in the
                                    workspace). */
+#define HS_FLAG_FP8_KV 4u       /* hs_sparse_attn_reuse reads its keys and
+                                   values from the FP8 copy of the cache
+                                   made by hs_kv_fp8_convert (kv then points
+                                   to that copy; strides must be 0). The
+                                   pages leave the cache precision open
+                                   ([DAIR] "Cheaper at 1M tokens" gives
+                                   the cache size only): this halves the
+                                   gathered bytes.
+                                   Rejected by the other calls. */
 
 typedef struct {
   int32_t batch;       /* B >= 1                                            */
@@ -212,6 +221,31 @@ hs_status hs_timing_enable(int32_t on);
 hs_status hs_timing_read(hs_kernel_time* out, int32_t max, int32_t* count);
 
 /* Static English name of a status code. */
+/* FP8 (e4m3) copy of a bf16 cache for the sparse layers (HS_FLAG_FP8_KV).
+ *
+ * Layout of the copy (caller-owned device buffer of hs_kv_fp8_size bytes,
+ * 16-byte aligned): codes [batch][kv_heads][kv_capacity][2][128] bytes (K row
+ * then V row of each token), then [batch][kv_heads][2] uint32 (scratch of
+ * the conversion), then [batch][kv_heads][2] float scales 2^e_K, 2^e_V.
+ * A stored value x of KV head (b, g) is e4m3(clamp(x / 2^e, -448, 448)),
+ * rounded to nearest even, and reads back as code * 2^e: every such value is
+ * a bf16 value, so the sparse kernels compute on it exactly.
+ *
+ * hs_kv_fp8_size: bytes of the copy for s->batch, kv_heads, kv_capacity.
+ * hs_kv_fp8_convert:
+ *   seq_lens == NULL (prefill form): per (b, g), e_K and e_V are the smallest
+ *     exponents with max |x| <= 448 * 2^e over rows [0, n_kv) (0 for an
+ *     all-zero head), stored, and rows [0, n_kv) are converted; needs
+ *     1 <= n_kv <= kv_capacity.
+ *   seq_lens != NULL (decode form, device int32 [batch]): row seq_lens[b]-1
+ *     of every (b, g) is converted with the stored scales (values beyond the
+ *     range saturate at +-448 * 2^e); call it after hs_decode_step appended
+ *     the row.
+ *   kv: the bf16 cache in the layout of hs_shape (strides allowed). Runs on
+ *   `stream`; errors as for the other calls. */
+hs_status hs_kv_fp8_size(const hs_shape* s, size_t* bytes);
+hs_status hs_kv_fp8_convert(const hs_shape* s, const void* kv, void* kv8, const int32_t* seq_lens, void* stream);
+
 const char* hs_status_string(hs_status st);
 
 /* Detail message of the calling thread's most recent failed call ("" if

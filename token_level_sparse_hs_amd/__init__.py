@@ -6,6 +6,7 @@ Thin Python front-end over the C ABI of libhysparse (include/hysparse.h):
                        per-KV-group top-k token indices (forced window implicit)
     sparse_attn_reuse  sparse layer reusing the full layer's cache and indices
     decode_step        decode full layer: append, attend, select once
+    kv_to_fp8          FP8 (e4m3) copy of the cache for the sparse layers
 
 All tensors live on the GPU; the cache layout is [B][Hkv][capacity][2][128]
 bf16 (K row then V row per token) unless explicit strides are given.
@@ -17,10 +18,10 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import HS_FLAG_EXACT_RESCAN, HS_FLAG_PROB_SCORE, HsError, HsShape  # noqa: F401
+from ._lib import HS_FLAG_EXACT_RESCAN, HS_FLAG_FP8_KV, HS_FLAG_PROB_SCORE, HsError, HsShape  # noqa: F401
 
 __all__ = ["full_attn_select", "sparse_attn_reuse", "decode_step", "make_shape", "HsError",
-           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "version"]
+           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "kv_to_fp8", "version"]
 
 
 def version() -> int:
@@ -84,12 +85,13 @@ def full_attn_select(q, kv, n_kv, *, top_k, window, scale=0.0, with_lse=True, fl
 
 
 def sparse_attn_reuse(q, kv, idx, *, top_k, window, n_kv=None, seq_lens=None, scale=0.0,
-                      kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None):
+                      kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None, kv_fp8=None):
     """Sparse layer reusing the full layer's cache and selection.
 
     Prefill: q bf16 [B][n_q][Hq][128], idx [B][n_q][Hkv][k], n_kv given.
     Decode:  q bf16 [B][Hq][128], idx [B][Hkv][k], seq_lens int32 [B] on device.
-    Returns o with q's shape.
+    kv_fp8: the cache's FP8 copy from kv_to_fp8 to gather from instead of kv
+    (kv then only gives the shape). Returns o with q's shape.
     """
     decode = seq_lens is not None
     _check_bf16("q", q, 3 if decode else 4)
@@ -106,13 +108,13 @@ def sparse_attn_reuse(q, kv, idx, *, top_k, window, n_kv=None, seq_lens=None, sc
         raise TypeError("seq_lens must be an int32 device tensor")
     shape = make_shape(batch=B, n_q=n_q, n_kv=0 if decode else n_kv, kv_capacity=kv_capacity, q_heads=Hq,
                        kv_heads=kv_heads, top_k=top_k, window=window, scale=scale, kv_strides=kv_strides,
-                       head_dim=d)
+                       flags=_lib.HS_FLAG_FP8_KV if kv_fp8 is not None else 0, head_dim=d)
     dev = q.device
     o = torch.empty_like(q)
     nbytes = _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, shape, 1 if decode else 0)
     ws = workspace if workspace is not None else _lib.alloc_workspace(nbytes, dev)
     lib = _lib.load()
-    _lib.check(lib.hs_sparse_attn_reuse(ctypes.byref(shape), _lib.ptr(q), _lib.ptr(kv),
+    _lib.check(lib.hs_sparse_attn_reuse(ctypes.byref(shape), _lib.ptr(q), _lib.ptr(kv if kv_fp8 is None else kv_fp8),
                                         _lib.ptr(idx) if top_k > 0 else None, _lib.ptr(seq_lens), _lib.ptr(o),
                                         _lib.ptr(ws), 0 if ws is None else ws.numel(), _lib.stream_handle(dev)))
     return o
@@ -147,6 +149,31 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
                                   _lib.ptr(idx) if top_k > 0 else None, _lib.ptr(ws),
                                   0 if ws is None else ws.numel(), _lib.stream_handle(dev)))
     return o, lse, idx
+
+
+def kv_to_fp8(kv, *, n_kv=None, seq_lens=None, out=None):
+    """FP8 (e4m3) copy of the bf16 cache kv [B][Hkv][capacity][2][128] for
+    the sparse layers (include/hysparse.h, hs_kv_fp8_convert).
+
+    Prefill form (n_kv given): per-KV-head power-of-two scales from rows
+    [0, n_kv), those rows converted into a new (or the given) copy. Decode
+    form (seq_lens given, int32 [B] on the device): row seq_lens[b]-1 of
+    `out` refreshed with its stored scales. Returns the copy (uint8 tensor).
+    """
+    B, Hkv, cap = kv.shape[0], kv.shape[1], kv.shape[2]
+    _kv_dims(kv, None)
+    shape = make_shape(batch=B, n_q=1, n_kv=n_kv or 0, kv_capacity=cap, q_heads=Hkv, kv_heads=Hkv, top_k=0,
+                       window=1)
+    lib = _lib.load()
+    if out is None:
+        if seq_lens is not None:
+            raise ValueError("the decode form refreshes an existing copy: pass out")
+        n = ctypes.c_size_t(0)
+        _lib.check(lib.hs_kv_fp8_size(ctypes.byref(shape), ctypes.byref(n)))
+        out = torch.empty(n.value, dtype=torch.uint8, device=kv.device)
+    _lib.check(lib.hs_kv_fp8_convert(ctypes.byref(shape), _lib.ptr(kv), _lib.ptr(out), _lib.ptr(seq_lens),
+                                     _lib.stream_handle(kv.device)))
+    return out
 
 
 from .graph import DecodeStepGraph, length_bucket  # noqa: E402  (uses the calls above)

@@ -20,8 +20,10 @@ HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE, HS_ERR_HIP, HS_
 HS_OP_FULL_ATTN_SELECT, HS_OP_SPARSE_ATTN_REUSE, HS_OP_DECODE_STEP = range(3)
 HS_FLAG_EXACT_RESCAN = 1
 HS_FLAG_PROB_SCORE = 2
+HS_FLAG_FP8_KV = 4
 
 EXPORTED = ("hs_workspace_size", "hs_full_attn_select", "hs_sparse_attn_reuse", "hs_decode_step",
+            "hs_kv_fp8_size", "hs_kv_fp8_convert",
             "hs_timing_enable", "hs_timing_read", "hs_status_string", "hs_last_error", "hs_version")
 
 
@@ -67,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.hs_decode_step.argtypes = [POINTER(HsShape), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.hs_decode_step.restype = c_int32
+    lib.hs_kv_fp8_size.argtypes = [POINTER(HsShape), POINTER(c_size_t)]
+    lib.hs_kv_fp8_size.restype = c_int32
+    lib.hs_kv_fp8_convert.argtypes = [POINTER(HsShape), c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.hs_kv_fp8_convert.restype = c_int32
     lib.hs_status_string.argtypes = [c_int32]
     lib.hs_status_string.restype = ctypes.c_char_p
     lib.hs_last_error.argtypes = []

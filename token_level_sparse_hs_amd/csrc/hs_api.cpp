@@ -82,8 +82,10 @@ hs_status validate_common(const hs_shape* s, Layout* lay) {
   if (s->window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", s->window);
   if (s->kv_capacity < 1) return fail(HS_ERR_INVALID_ARG, "kv_capacity must be >= 1");
   if (!(s->scale >= 0.f) || std::isinf(s->scale)) return fail(HS_ERR_INVALID_ARG, "scale must be finite and >= 0");
-  if ((s->flags & ~(HS_FLAG_EXACT_RESCAN | HS_FLAG_PROB_SCORE)) != 0)
+  if ((s->flags & ~(HS_FLAG_EXACT_RESCAN | HS_FLAG_PROB_SCORE | HS_FLAG_FP8_KV)) != 0)
     return fail(HS_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  if ((s->flags & HS_FLAG_FP8_KV) && (s->kv_stride_b || s->kv_stride_h || s->kv_stride_t || s->kv_v_offset))
+    return fail(HS_ERR_INVALID_ARG, "the FP8 cache copy has a fixed layout: strides must be 0");
   Layout l;
   if (s->kv_stride_b == 0 && s->kv_stride_h == 0 && s->kv_stride_t == 0 && s->kv_v_offset == 0) {
     l.st = 2 * 128;
@@ -404,6 +406,7 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
   if (st != HS_OK) return st;
   if (s->n_q < 1 || s->n_kv < s->n_q || s->n_kv > s->kv_capacity)
     return fail(HS_ERR_INVALID_ARG, "need 1 <= n_q (%d) <= n_kv (%d) <= kv_capacity (%d)", s->n_q, s->n_kv, s->kv_capacity);
+  if (s->flags & HS_FLAG_FP8_KV) return fail(HS_ERR_UNSUPPORTED, "the FP8 cache copy serves hs_sparse_attn_reuse only");
   if (!q || !kv || !o) return fail(HS_ERR_INVALID_ARG, "q, kv and o must be non-NULL");
   if (s->top_k > 0 && !idx) return fail(HS_ERR_INVALID_ARG, "idx must be non-NULL when top_k > 0");
   if (!aligned16(q) || !aligned16(kv) || !aligned16(o)) return fail(HS_ERR_INVALID_ARG, "q, kv and o must be 16-byte aligned");
@@ -517,6 +520,12 @@ hs_status hs_sparse_attn_reuse(const hs_shape* s, const void* q, const void* kv,
   hs::DecodeParams dp{};
   dp.q = static_cast<const uint16_t*>(q);
   dp.kv = kv_view(kv, lay);
+  if (s->flags & HS_FLAG_FP8_KV) {  // kv is the FP8 copy made by hs_kv_fp8_convert
+    dp.kv8 = static_cast<const uint8_t*>(kv);
+    dp.kv8_scale = reinterpret_cast<const float*>(dp.kv8 + hs::kv8_codes_bytes(s->batch, s->kv_heads, s->kv_capacity) +
+                                                  (size_t)s->batch * s->kv_heads * 8);
+    dp.kv8_cap = s->kv_capacity;
+  }
   dp.B = s->batch; dp.n_q = decode ? 1 : s->n_q; dp.n_kv = decode ? s->kv_capacity : s->n_kv; dp.Hq = s->q_heads; dp.Hkv = s->kv_heads;
   dp.top_k = s->top_k; dp.window = s->window; dp.scale = eff_scale(s);
   dp.seq_lens = seq_lens;
@@ -553,6 +562,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   if (s->n_q != 1) return fail(HS_ERR_INVALID_ARG, "decode calls need n_q == 1 (got %d)", s->n_q);
   if (max_seq_len < 1 || max_seq_len > s->kv_capacity)
     return fail(HS_ERR_INVALID_ARG, "need 1 <= max_seq_len (%d) <= kv_capacity (%d)", max_seq_len, s->kv_capacity);
+  if (s->flags & HS_FLAG_FP8_KV) return fail(HS_ERR_UNSUPPORTED, "the FP8 cache copy serves hs_sparse_attn_reuse only");
   if (!q || !kv_new || !kv || !seq_lens || !o) return fail(HS_ERR_INVALID_ARG, "q, kv_new, kv, seq_lens and o must be non-NULL");
   if (s->top_k > 0 && !idx) return fail(HS_ERR_INVALID_ARG, "idx must be non-NULL when top_k > 0");
   if (!aligned16(q) || !aligned16(kv_new) || !aligned16(kv) || !aligned16(o))
@@ -614,6 +624,34 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     }
     HIP_TRY(timed("select_decode", hst, [&] { return hs::launch_select_decode(sp, s->batch * s->kv_heads, hst); }));
   }
+  return ok();
+}
+
+hs_status hs_kv_fp8_size(const hs_shape* s, size_t* bytes) {
+  if (!s || !bytes) return fail(HS_ERR_INVALID_ARG, "shape and bytes must be non-NULL");
+  if (s->batch < 1 || s->kv_heads < 1 || s->kv_capacity < 1)
+    return fail(HS_ERR_INVALID_ARG, "need batch, kv_heads and kv_capacity >= 1");
+  *bytes = (size_t)hs::kv8_total_bytes(s->batch, s->kv_heads, s->kv_capacity);
+  return ok();
+}
+
+hs_status hs_kv_fp8_convert(const hs_shape* s, const void* kv, void* kv8, const int32_t* seq_lens, void* stream) {
+  Layout lay;
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  if (!kv || !kv8) return fail(HS_ERR_INVALID_ARG, "kv and kv8 must be non-NULL");
+  if (!aligned16(kv) || !aligned16(kv8)) return fail(HS_ERR_INVALID_ARG, "kv and kv8 must be 16-byte aligned");
+  if (!seq_lens && (s->n_kv < 1 || s->n_kv > s->kv_capacity))
+    return fail(HS_ERR_INVALID_ARG, "need 1 <= n_kv (%d) <= kv_capacity (%d)", s->n_kv, s->kv_capacity);
+  st = check_device();
+  if (st != HS_OK) return st;
+  hipStream_t hst = static_cast<hipStream_t>(stream);
+  hs::Fp8ConvertParams cp{};
+  cp.kv = kv_view(kv, lay);
+  cp.kv8 = static_cast<uint8_t*>(kv8);
+  cp.B = s->batch; cp.Hkv = s->kv_heads; cp.n_kv = s->n_kv; cp.cap = s->kv_capacity;
+  cp.seq_lens = seq_lens;
+  HIP_TRY(timed("kv_fp8_convert", hst, [&] { return hs::launch_kv_convert_fp8(cp, hst); }));
   return ok();
 }
 

@@ -53,15 +53,26 @@ __device__ __forceinline__ void lds_wait() {
 // 4gq..4gq+3 of the chunk, dims 8n..8n+7 of each K and V row (consecutive
 // lanes read consecutive bytes of a row: full cache lines, one address quad
 // per row segment).
-struct Chunk {
+template <bool FP8>
+struct ChunkT {
   u32x4 kw[4];  // K rows 4gq + r
   u32x4 vw[4];  // V rows 4gq + r
   int nv;       // wave-uniform: keys 0..nv-1 of the chunk are real, the rest masked
 };
+// FP8 cache: the same eight dims per row as e4m3 codes (8 bytes), widened to
+// bf16 when consumed.
+template <>
+struct ChunkT<true> {
+  u32x2 kw[4];
+  u32x2 vw[4];
+  int nv;
+};
 
 // SIGMA (full rows only): also write the group score row of the candidates.
-template <int G, bool SPARSE, bool SIGMA>
+template <int G, bool SPARSE, bool SIGMA, bool FP8 = false>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
+  static_assert(!FP8 || (SPARSE && !SIGMA), "the FP8 cache serves the sparse layers");
+  using Chunk = ChunkT<FP8>;
   // Per-wave K tiles and key lists; in prefill SPARSE mode the block's
   // shared window tiles alias this region before the lists are built.
   constexpr int kKtBytes = 16 * kKS16 * 2;
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     const int64_t bt0 = (int64_t)(blockIdx.x / P.Hkv) * 4;
     b0 = (int)(bt0 / P.n_q);
     t0 = (int)(bt0 % P.n_q);
-    win_shared = SPARSE && row_ok && b == b0;
+    win_shared = SPARSE && !FP8 && row_ok && b == b0;  // FP8: window keys gathered per wave
   }
   const int64_t qrow = (int64_t)b * P.n_q + t;  // decode: n_q == 1
 
@@ -137,13 +148,27 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
 
   b = uniform(b);
   g = uniform(g);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(P.kv.slab(b, g));
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(P.kv.slab(b, g) + P.kv.voff);
-  const uint32_t rowb = 2u * (uint32_t)P.kv.st;  // bytes per token
-  const uint32_t colb = 16u * (uint32_t)n;       // this lane's 16 bytes of a row
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  uint32_t rowb, colb;  // bytes per token; this lane's bytes of a row (dims 8n .. 8n+7)
+  float kscale = 1.f, vscale = 1.f;
+  if constexpr (FP8) {
+    const uint8_t* slab8 = P.kv8 + ((int64_t)b * P.Hkv + g) * P.kv8_cap * kFp8RowBytes;
+    krs = make_rsrc(slab8);
+    vrs = make_rsrc(slab8 + kHeadDim);
+    rowb = kFp8RowBytes;
+    colb = 8u * (uint32_t)n;
+    // power-of-two scales: K's folds into the logit scale, V's into P (exact)
+    kscale = P.kv8_scale[((int64_t)b * P.Hkv + g) * 2];
+    vscale = P.kv8_scale[((int64_t)b * P.Hkv + g) * 2 + 1];
+  } else {
+    krs = make_rsrc(P.kv.slab(b, g));
+    vrs = make_rsrc(P.kv.slab(b, g) + P.kv.voff);
+    rowb = 2u * (uint32_t)P.kv.st;
+    colb = 16u * (uint32_t)n;
+  }
   f32x4 oacc[8] = {};
   float m_run = kNegInf, l_part = 0.f;
-  const float cexp = P.scale * kLog2e;
+  const float cexp = P.scale * kscale * kLog2e;
   const int cand_end = lim;  // last candidate position (FULL score row)
   // Score row: the group maxima of each chunk are staged in the wave's LDS
   // segment buffer and written out once the segment's gathers are done: a
@@ -220,8 +245,13 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     ch.nv = uniform(imin(imax(vend - v, 0), 16));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      ch.kw[r] = buf_ld16(krs, off[r]);
-      ch.vw[r] = buf_ld16(vrs, off[r]);
+      if constexpr (FP8) {
+        ch.kw[r] = buf_ld8(krs, off[r]);
+        ch.vw[r] = buf_ld8(vrs, off[r]);
+      } else {
+        ch.kw[r] = buf_ld16(krs, off[r]);
+        ch.vw[r] = buf_ld16(vrs, off[r]);
+      }
     }
   };
 
@@ -264,6 +294,10 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
       psum += pv;
     }
     l_part += psum;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= vscale;  // exact: a power of two
+    }
     u32x2 pb;
     pb[0] = pack_bf16x2(acc[0], acc[1]);
     pb[1] = pack_bf16x2(acc[2], acc[3]);
@@ -282,7 +316,12 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   auto compute = [&](const Chunk& ch, int v) __attribute__((always_inline)) {
     // K rows into the per-wave LDS tile (row-major, key 4gq + r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (FP8)
+        st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], fp8x8_to_bf16x8(ch.kw[r]));
+      else
+        st16(&Kt[(4 * gq + r) * kKS16 + 8 * n], ch.kw[r]);
+    }
     lds_wait();
     // S^T = K Q^T: A operand lane (n, gq) = K[key n][32s + 8gq .. +8]
     f32x4 acc = {};
@@ -301,7 +340,14 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
       for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
       if (n == 0) *reinterpret_cast<f32x4*>(&sig_stage[v - sig_v0 + 4 * gq]) = mxh;
     }
-    finish(acc, ch.vw);
+    if constexpr (FP8) {
+      u32x4 vw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vw[r] = fp8x8_to_bf16x8(ch.vw[r]);
+      finish(acc, vw);
+    } else {
+      finish(acc, ch.vw);
+    }
   };
 
   // Prefill: the forced windows of the block's rows (consecutive tokens of
@@ -313,7 +359,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   // permuted (chunk c of row r at c ^ (r % 16)) so that the score operand
   // reads of 16 rows hit distinct banks.
   if constexpr (SPARSE) {
-    if (!decode) {
+    if (!decode && !FP8) {
       constexpr int kWinKeys = 32;
       constexpr int kWinTile = 2 * kWinKeys * 256;  // K then V, 256-byte rows
       static_assert(3 * kWinTile <= 4 * (kKtBytes + kListBytes), "window tiles exceed the aliased LDS");
@@ -534,6 +580,106 @@ __global__ void append_kernel(AppendParams P) {
   st16(dst, w);
 }
 
+// ---------------------------------------------------------------- FP8 cache copy
+// A token row is 32 pieces of 8 dims: piece c < 16 holds K dims 8c .. 8c+7,
+// piece c >= 16 V dims 8(c-16) ...; thread t takes piece t % 32 of rows
+// t / 32, t / 32 + 8, ... of its block's rows.
+constexpr int kFp8RowsPerBlock = 256;
+
+// Smallest e with amax <= 448 * 2^e (0 for an all-zero head).
+__device__ __forceinline__ int fp8_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  (void)frexpf(amax, &e);
+  e -= 9;
+  while (amax > ldexpf(448.f, e)) ++e;
+  while (amax <= ldexpf(448.f, e - 1)) --e;
+  return e;
+}
+
+// Eight bf16 values times inv (a power of two), clamped to +-448, to e4m3
+// codes rounded to nearest even (byte i = element i).
+__device__ __forceinline__ u32x2 bf16x8_to_fp8x8(u32x4 w, float inv) {
+  float x[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    x[2 * q] = fminf(fmaxf(bf16lo(w[q]) * inv, -448.f), 448.f);
+    x[2 * q + 1] = fminf(fmaxf(bf16hi(w[q]) * inv, -448.f), 448.f);
+  }
+  uint32_t a = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
+  a = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], a, true);
+  uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0u, false);
+  c = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], c, true);
+  return u32x2{a, c};
+}
+
+__global__ void fp8_zero_kernel(uint32_t* amax, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) amax[i] = 0u;
+}
+
+// Per-(b, g) maxima of |K| and |V| over rows [0, n_kv): per block, then one
+// atomic max per block (non-negative floats order like their bit patterns).
+__global__ __launch_bounds__(256) void fp8_amax_kernel(Fp8ConvertParams P) {
+  __shared__ float red[2][4];
+  const int bg = blockIdx.y, b = bg / P.Hkv, g = bg % P.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid & 31, vsel = c >> 4, d0 = 8 * (c & 15);
+  const int r0 = blockIdx.x * kFp8RowsPerBlock;
+  const int r1 = imin(P.n_kv, r0 + kFp8RowsPerBlock);
+  float m = 0.f;
+  for (int r = r0 + (tid >> 5); r < r1; r += 8) {
+    const u32x4 w = ld16((vsel ? P.kv.v_row(b, g, r) : P.kv.k_row(b, g, r)) + d0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(fabsf(bf16lo(w[q])), fabsf(bf16hi(w[q]))));
+  }
+  // lanes with bit 4 clear hold K pieces, the others V pieces
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  if (lane == 0) red[0][wave] = m;
+  if (lane == 16) red[1][wave] = m;
+  __syncthreads();
+  if (tid < 2) {
+    const float mm = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
+    uint32_t* amax = reinterpret_cast<uint32_t*>(P.kv8 + kv8_codes_bytes(P.B, P.Hkv, P.cap));
+    atomicMax(&amax[bg * 2 + tid], __float_as_uint(mm));
+  }
+}
+
+__global__ __launch_bounds__(256) void fp8_convert_kernel(Fp8ConvertParams P) {
+  const int bg = blockIdx.y, b = bg / P.Hkv, g = bg % P.Hkv;
+  const int tid = threadIdx.x;
+  const int c = tid & 31, vsel = c >> 4, d0 = 8 * (c & 15);
+  const uint32_t* amax = reinterpret_cast<const uint32_t*>(P.kv8 + kv8_codes_bytes(P.B, P.Hkv, P.cap));
+  float* scale = reinterpret_cast<float*>(P.kv8 + kv8_codes_bytes(P.B, P.Hkv, P.cap) + (int64_t)P.B * P.Hkv * 8);
+  const int e = fp8_exponent(__uint_as_float(amax[bg * 2 + vsel]));
+  const float inv = ldexpf(1.f, -e);
+  if (blockIdx.x == 0 && (tid == 0 || tid == 16)) scale[bg * 2 + vsel] = ldexpf(1.f, e);
+  const int r0 = blockIdx.x * kFp8RowsPerBlock;
+  const int r1 = imin(P.n_kv, r0 + kFp8RowsPerBlock);
+  uint8_t* dst = P.kv8 + (int64_t)bg * P.cap * kFp8RowBytes + vsel * kHeadDim + d0;
+  for (int r = r0 + (tid >> 5); r < r1; r += 8) {
+    const u32x4 w = ld16((vsel ? P.kv.v_row(b, g, r) : P.kv.k_row(b, g, r)) + d0);
+    *reinterpret_cast<u32x2*>(dst + (int64_t)r * kFp8RowBytes) = bf16x8_to_fp8x8(w, inv);
+  }
+}
+
+// Decode: the row appended at slot seq_lens[b] - 1, with the stored scales.
+__global__ __launch_bounds__(256) void fp8_append_kernel(Fp8ConvertParams P) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P.B * P.Hkv * 32) return;
+  const int bg = i >> 5, c = i & 31, vsel = c >> 4, d0 = 8 * (c & 15);
+  const int b = bg / P.Hkv, g = bg % P.Hkv;
+  const int r = P.seq_lens[b] - 1;
+  if (r < 0 || r >= P.cap) return;
+  const float* scale = reinterpret_cast<const float*>(P.kv8 + kv8_codes_bytes(P.B, P.Hkv, P.cap) + (int64_t)P.B * P.Hkv * 8);
+  const float inv = 1.f / scale[bg * 2 + vsel];  // exact: a power of two
+  const u32x4 w = ld16((vsel ? P.kv.v_row(b, g, r) : P.kv.k_row(b, g, r)) + d0);
+  *reinterpret_cast<u32x2*>(P.kv8 + ((int64_t)bg * P.cap + r) * kFp8RowBytes + vsel * kHeadDim + d0) =
+      bf16x8_to_fp8x8(w, inv);
+}
+
 // Log-sum-exp merge of split partials; one block per (b, head) of
 // kCombGroups groups of 128 threads. Pass 1 (threads over splits): M = max
 // m_s, then weights w_s = 2^(m_s - M) into LDS and l = sum w_s l_s. Pass 2:
@@ -611,6 +757,8 @@ hipError_t launch_gather_g(const DecodeParams& p, hipStream_t s) {
                                     : (((int64_t)p.B * p.n_q + 3) / 4) * p.Hkv;
   if (!SPARSE && p.sigma)
     flash_gather_kernel<G, false, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  else if (SPARSE && p.kv8)
+    flash_gather_kernel<G, true, false, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
   else
     flash_gather_kernel<G, SPARSE, false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
   return hipGetLastError();
@@ -635,6 +783,24 @@ hipError_t launch_sparse(const DecodeParams& p, hipStream_t s) { return launch_g
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.B * p.Hkv * 32;
   append_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_convert_fp8(const Fp8ConvertParams& p, hipStream_t s) {
+  const int bg = p.B * p.Hkv;
+  if (p.seq_lens) {
+    fp8_append_kernel<<<dim3((unsigned)((bg * 32 + 255) / 256)), dim3(256), 0, s>>>(p);
+    return hipGetLastError();
+  }
+  uint32_t* amax = reinterpret_cast<uint32_t*>(p.kv8 + kv8_codes_bytes(p.B, p.Hkv, p.cap));
+  fp8_zero_kernel<<<dim3((unsigned)((2 * bg + 255) / 256)), dim3(256), 0, s>>>(amax, 2 * bg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((p.n_kv + kFp8RowsPerBlock - 1) / kFp8RowsPerBlock), (unsigned)bg);
+  fp8_amax_kernel<<<grid, dim3(256), 0, s>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  fp8_convert_kernel<<<grid, dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -133,7 +133,36 @@ struct DecodeParams {
                             // splits of one (b, g) row and merge in LDS (part unused)
   float* sigma;             // FULL: [B*Hkv][sigma_stride]
   int64_t sigma_stride;
+  // SPARSE from the FP8 cache copy (kv8 != null; kv unused): rows of
+  // [B][Hkv][kv8_cap] tokens, K then V codes, and per-(b, g) scales.
+  const uint8_t* kv8;
+  const float* kv8_scale;   // [B][Hkv][2]: 2^e of K and of V
+  int64_t kv8_cap;
 };
+
+// FP8 (e4m3) copy of a bf16 cache for the sparse gathers. Buffer layout:
+// codes [B][Hkv][cap][2][128] (256 bytes per token: K then V), then amax bits
+// [B][Hkv][2] (uint32, scratch of the conversion), then scales [B][Hkv][2]
+// (float, 2^e of K and of V). Prefill form: per (b, g), e = the smallest
+// exponent with max|x| over rows [0, n_kv) <= 448 * 2^e, separately for K
+// and V, then every row converted as e4m3(clamp(x / 2^e, +-448)) rounded to
+// nearest even. Decode form (seq_lens given): row seq_lens[b] - 1 converted
+// with the stored scales.
+constexpr int kFp8RowBytes = 256;
+struct Fp8ConvertParams {
+  KvView kv;
+  uint8_t* kv8;
+  int B, Hkv, n_kv;
+  int64_t cap;
+  const int32_t* seq_lens;
+};
+__host__ __device__ inline int64_t kv8_codes_bytes(int B, int Hkv, int64_t cap) {
+  return (int64_t)B * Hkv * cap * kFp8RowBytes;
+}
+__host__ __device__ inline int64_t kv8_total_bytes(int B, int Hkv, int64_t cap) {
+  return kv8_codes_bytes(B, Hkv, cap) + (int64_t)B * Hkv * 16;
+}
+hipError_t launch_kv_convert_fp8(const Fp8ConvertParams& p, hipStream_t s);
 
 struct AppendParams {
   const uint16_t* kv_new;  // [B][Hkv][2][128]
