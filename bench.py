@@ -106,9 +106,12 @@ def prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch):
     sparse layers gathering from the FP8 copy of the cache."""
     _, _, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, workspace=ws)
     copy = hs.kv_to_fp8(kv, n_kv=w.n_kv)
+    shape = hs.make_shape(batch=w.B, n_q=w.n_q, n_kv=w.n_kv, kv_capacity=kv.shape[2], q_heads=w.Hq,
+                          kv_heads=w.Hkv, top_k=w.top_k, window=w.window, flags=hs.HS_FLAG_PROB_SCORE)
+    ws_prob = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), "cuda:0")
     runs = {
         "prob_score_full_layer": lambda: hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window,
-                                                             flags=hs.HS_FLAG_PROB_SCORE, workspace=ws),
+                                                             flags=hs.HS_FLAG_PROB_SCORE, workspace=ws_prob),
         "fp8_cache_conversion": lambda: hs.kv_to_fp8(kv, n_kv=w.n_kv, out=copy),
         "fp8_sparse_layer": lambda: hs.sparse_attn_reuse(qs[0], kv, idx, top_k=w.top_k, window=w.window,
                                                          n_kv=w.n_kv, kv_fp8=copy),
@@ -127,7 +130,7 @@ def prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch):
         out[name] = {"ms": round(sum(t for n, t in kt.values()) / 3, 3),
                      "kernels_us": {k: round(t / n * 1e3, 1) for k, (n, t) in kt.items()}}
         log(f"[bench] {w.name} {name}: {out[name]}")
-    del copy
+    del copy, ws_prob
     return out
 
 
