@@ -12,16 +12,21 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def test_decode_graph_matches_eager():
+@pytest.mark.parametrize("option", ["default", "prob_score", "fp8_cache"])
+def test_decode_graph_matches_eager(option):
     lengths = [4093, 700, 64, 2500, 1, 3000]  # the longest crosses 4096 -> a second bucket
     B, Hq, Hkv, k, W, nsl, steps = len(lengths), 32, 4, 256, 64, 2, 6
-    print(f"[case] decode graph B={B} steps={steps}", flush=True)
+    print(f"[case] decode graph B={B} steps={steps} option={option}", flush=True)
     cap = max(lengths) + steps
     kv_a = torch.zeros((B, Hkv, cap, 2, 128), dtype=torch.bfloat16, device=DEV)
     for b, L in enumerate(lengths):
         kv_a[b, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 700 + b, DEV)
     kv_b = kv_a.clone()
-    g = hs.DecodeStepGraph(kv_b, batch=B, q_heads=Hq, sparse_layers=nsl, top_k=k, window=W)
+    flags = hs.HS_FLAG_PROB_SCORE if option == "prob_score" else 0
+    f8_a = hs.kv_to_fp8(kv_a, n_kv=cap) if option == "fp8_cache" else None
+    f8_b = f8_a.clone() if f8_a is not None else None
+    g = hs.DecodeStepGraph(kv_b, batch=B, q_heads=Hq, sparse_layers=nsl, top_k=k, window=W, flags=flags,
+                           kv_fp8=f8_b)
     for s in range(steps):
         q = synth.randn_bf16((B, Hq, 128), 710 + s, DEV)
         kv_new = synth.randn_bf16((B, Hkv, 2, 128), 720 + s, DEV)
@@ -36,8 +41,10 @@ def test_decode_graph_matches_eager():
         o_g, lse_g, idx_g, osp_g = g.step(max(cur))
         torch.cuda.synchronize()
         # eager calls with the bound the graph was captured with (same plan)
-        o, lse, idx = hs.decode_step(q, kv_new, kv_a, seq, g.bound, top_k=k, window=W)
-        osp = [hs.sparse_attn_reuse(x, kv_a, idx, top_k=k, window=W, seq_lens=seq) for x in qs]
+        o, lse, idx = hs.decode_step(q, kv_new, kv_a, seq, g.bound, top_k=k, window=W, flags=flags)
+        if f8_a is not None:
+            hs.kv_to_fp8(kv_a, seq_lens=seq, out=f8_a)
+        osp = [hs.sparse_attn_reuse(x, kv_a, idx, top_k=k, window=W, seq_lens=seq, kv_fp8=f8_a) for x in qs]
         torch.cuda.synchronize()
         assert torch.equal(idx_g, idx), s
         assert torch.equal(o_g, o), s
@@ -46,4 +53,6 @@ def test_decode_graph_matches_eager():
             assert torch.equal(a, b), s
         print(f"[case] step {s} bound {g.bound} captures {g.captures}: identical", flush=True)
     assert torch.equal(kv_a, kv_b)
+    if f8_a is not None:
+        assert torch.equal(f8_a, f8_b)
     assert g.captures == 2

@@ -24,7 +24,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from . import decode_step, make_shape, sparse_attn_reuse
+from . import decode_step, kv_to_fp8, make_shape, sparse_attn_reuse
 
 __all__ = ["DecodeStepGraph", "length_bucket"]
 
@@ -48,7 +48,8 @@ class DecodeStepGraph:
     slot seq_lens[b]-1 by every replay.
     """
 
-    def __init__(self, kv, *, batch, q_heads, sparse_layers, top_k, window, scale=0.0, with_lse=True):
+    def __init__(self, kv, *, batch, q_heads, sparse_layers, top_k, window, scale=0.0, with_lse=True, flags=0,
+                 kv_fp8=None):
         if not isinstance(kv, torch.Tensor) or kv.dim() != 5:
             raise ValueError("kv must be the [B][Hkv][capacity][2][128] cache tensor")
         self.kv = kv
@@ -58,12 +59,16 @@ class DecodeStepGraph:
             raise ValueError("kv batch does not match")
         self.B, self.Hq, self.Hkv, self.cap = B, q_heads, Hkv, cap
         self.top_k, self.window, self.scale, self.with_lse = top_k, window, scale, with_lse
+        # options: selection flags of the full layer; an FP8 copy of the cache
+        # (from kv_to_fp8) that the step refreshes at the appended row and the
+        # sparse layers gather from
+        self.flags, self.kv_fp8 = flags, kv_fp8
         self.q = torch.zeros((B, q_heads, 128), dtype=torch.bfloat16, device=dev)
         self.kv_new = torch.zeros((B, Hkv, 2, 128), dtype=torch.bfloat16, device=dev)
         self.q_sparse = [torch.zeros_like(self.q) for _ in range(sparse_layers)]
         self.seq_lens = torch.ones((B,), dtype=torch.int32, device=dev)
         shape = make_shape(batch=B, n_q=1, n_kv=0, kv_capacity=cap, q_heads=q_heads, kv_heads=Hkv,
-                           top_k=top_k, window=window, scale=scale)
+                           top_k=top_k, window=window, scale=scale, flags=flags)
         self.ws_sparse = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, shape, 1), dev)
         self._shape = shape
         self.graph = None
@@ -78,9 +83,12 @@ class DecodeStepGraph:
         with torch.cuda.graph(g):
             o, lse, idx = decode_step(self.q, self.kv_new, self.kv, self.seq_lens, bound, top_k=self.top_k,
                                       window=self.window, scale=self.scale, with_lse=self.with_lse,
-                                      workspace=ws_full)
+                                      flags=self.flags, workspace=ws_full)
+            if self.kv_fp8 is not None:
+                kv_to_fp8(self.kv, seq_lens=self.seq_lens, out=self.kv_fp8)
             o_sp = [sparse_attn_reuse(x, self.kv, idx, top_k=self.top_k, window=self.window, scale=self.scale,
-                                      seq_lens=self.seq_lens, workspace=self.ws_sparse) for x in self.q_sparse]
+                                      seq_lens=self.seq_lens, workspace=self.ws_sparse, kv_fp8=self.kv_fp8)
+                    for x in self.q_sparse]
         self.graph, self.ws_full, self.bound = g, ws_full, bound
         self.o, self.lse, self.idx, self.o_sparse = o, lse, idx, o_sp
         self.captures += 1
