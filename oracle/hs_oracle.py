@@ -45,6 +45,11 @@ design notes of the repository):
   R7 GQA: query head h reads KV head h // G, G = Hq / Hkv.
   R8 the selection decision is taken on float32 scores (float64 evaluation
      rounded once to float32), the precision the kernels decide in.
+  R9 (optional, block-level selection, the ablation the pages compare
+     token-level selection against): C(p) is cut into aligned blocks of 64
+     tokens, a block scores the maximum sigma of its candidates, the top
+     k / 64 blocks (ties: lower block first) are taken whole (the last block
+     of C(p) may be partial), emitted ascending and padded with -1.
   R1' (optional score, score="prob"): the softmax-normalised group score
      max over h of (scale * <q_h(t), k_g(j)> - lse_h(t)), lse_h(t) the log
      of the softmax denominator of head h over keys 0..p, i.e. the log of the
@@ -72,6 +77,7 @@ __all__ = [
     "lse_combine",
     "fp8_scale_exponent",
     "quantize_fp8",
+    "block_select",
 ]
 
 
@@ -194,14 +200,43 @@ def topk_select(sigma: np.ndarray, k: int):
     return out, float(sigma[chosen[-1]])
 
 
+def block_select(sigma: np.ndarray, k: int, block: int = 64):
+    """Block-level selection (reading R9) over the candidate scores of one
+    (row, group): blocks [block*b, block*b + block) of C(p), block score =
+    the largest member score, the top k // block blocks by (score desc, block
+    index asc) decided on float32 scores (R8), expanded to their tokens.
+    Returns (idx of length k, ascending, -1 padded; tau = the float64 score of
+    the last block taken, or -inf when every block is taken)."""
+    n = sigma.shape[0]
+    out = np.full(k, -1, dtype=np.int64)
+    nb = k // block
+    if nb == 0 or n == 0:
+        return out, -math.inf
+    nblk = (n + block - 1) // block
+    bs = np.array([sigma[b * block:(b + 1) * block].max() for b in range(nblk)])
+    if nblk <= nb:
+        chosen, tau = np.arange(nblk), -math.inf
+    else:
+        b32 = bs.astype(np.float32).astype(np.float64)
+        b32 = np.where(b32 == 0.0, 0.0, b32)
+        order = np.lexsort((np.arange(nblk), -b32))
+        chosen = np.sort(order[:nb])
+        tau = float(bs[order[nb - 1]])
+    toks = np.concatenate([np.arange(b * block, min((b + 1) * block, n)) for b in chosen])
+    out[:len(toks)] = toks
+    return out, tau
+
+
 def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
-                          positions, k: int, window: int, scale: float, score: str = "logit"):
+                          positions, k: int, window: int, scale: float, score: str = "logit",
+                          blocks: bool = False):
     """The full-attention layer of a hybrid block for the given query rows.
 
     It computes causal GQA attention and, per (row, KV group), the top-k token
     indices that the following sparse layers reuse [HS2-cs], [DAIR].
     score: "logit" (reading R1) or "prob" (reading R1', which needs this
-    layer's lse first). Returns dict with o [rows][Hq][d], lse [rows][Hq],
+    layer's lse first); blocks: block-level selection (reading R9) instead of
+    token-level. Returns dict with o [rows][Hq][d], lse [rows][Hq],
     idx [rows][Hkv][k] (int64), tau [rows][Hkv], sigma (list of per-(row,
     group) float64 arrays).
     """
@@ -220,7 +255,7 @@ def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
         for g in range(Hkv):
             lg = lse[r, g * G:(g + 1) * G] if score == "prob" else None
             s = selection_scores(q[r, g * G:(g + 1) * G], K[g], p, window, scale, lg)
-            idx[r, g], tau[r, g] = topk_select(s, k)
+            idx[r, g], tau[r, g] = block_select(s, k) if blocks else topk_select(s, k)
             row_sig.append(s)
         sig.append(row_sig)
     return {"o": o, "lse": lse, "idx": idx, "tau": tau, "sigma": sig}
@@ -253,7 +288,7 @@ def sparse_attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
 
 def decode_step(q_full: np.ndarray, q_sparse: list, kv_new: np.ndarray,
                 K: np.ndarray, V: np.ndarray, length: int, k: int,
-                window: int, scale: float, score: str = "logit"):
+                window: int, scale: float, score: str = "logit", blocks: bool = False):
     """One decode step of one sequence through a hybrid block.
 
     The new token's key/value row is written at slot length-1 of the cache
@@ -267,7 +302,7 @@ def decode_step(q_full: np.ndarray, q_sparse: list, kv_new: np.ndarray,
     K[:, p] = kv_new[:, 0]
     V[:, p] = kv_new[:, 1]
     pos = np.array([p])
-    res = full_attn_select_rows(q_full[None], K, V, pos, k, window, scale, score)
+    res = full_attn_select_rows(q_full[None], K, V, pos, k, window, scale, score, blocks)
     outs = []
     for qs in q_sparse:
         o, _ = sparse_attention_rows(qs[None], K, V, res["idx"], pos, window, scale)

@@ -505,3 +505,42 @@ def test_fp8_quantiser_error_bound_and_exact_values():
     # values past the range saturate instead of becoming NaN
     _, sat = orc.quantize_fp8(np.array([1e9, -1e9]), 0)
     assert list(sat) == [448.0, -448.0]
+
+
+# ---------------------------------------------------------------- block-level selection (reading R9)
+
+def test_block_select_with_unit_blocks_is_token_select():
+    rng = np.random.default_rng(61)
+    for n, k in [(500, 40), (70, 64), (3, 8), (129, 128)]:
+        sig = rng.standard_normal(n)
+        a, ta = orc.topk_select(sig, k)
+        b, tb = orc.block_select(sig, k, block=1)
+        assert np.array_equal(a, b) and ta == tb
+
+
+def test_block_select_brute_force():
+    """Brute force with plain Python on small rows: every block's maximum,
+    ranked by (score desc, index asc), the first k/B blocks expanded."""
+    rng = np.random.default_rng(62)
+    for n, k, B in [(300, 64, 16), (257, 128, 64), (64, 64, 64), (1000, 192, 64)]:
+        sig = np.round(rng.standard_normal(n), 2)  # rounding creates ties
+        got, _ = orc.block_select(sig, k, block=B)
+        blocks = [(max(sig[i:i + B]), i // B) for i in range(0, n, B)]
+        ranked = sorted(blocks, key=lambda t: (-float(np.float32(t[0])), t[1]))[:k // B]
+        want = sorted(j for _, b in ranked for j in range(b * B, min(b * B + B, n)))
+        assert list(got[:len(want)]) == want and np.all(got[len(want):] == -1)
+
+
+def test_block_selection_rows_keep_whole_blocks():
+    rng = np.random.default_rng(63)
+    q = bf16_exact((2, 4, 128), rng)
+    K = bf16_exact((1, 900, 128), rng)
+    V = bf16_exact((1, 900, 128), rng)
+    res = orc.full_attn_select_rows(q, K, V, [600, 899], 128, 32, orc.default_scale(128), blocks=True)
+    for r, p in enumerate([600, 899]):
+        sel = res["idx"][r, 0]
+        sel = sel[sel >= 0]
+        c = p - 32 + 1
+        for b in set(sel // 64):
+            assert set(sel[sel // 64 == b]) == set(range(64 * b, min(64 * b + 64, c)))
+        assert len(set(sel // 64)) == 2
