@@ -102,16 +102,21 @@ def run_prefill(args, hs, synth, _lib, torch):
 
 def prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch):
     """Options beside the default path, timed on the same inputs (not part
-    of `value`): the probability selection score (full layer) and the
-    sparse layers gathering from the FP8 copy of the cache."""
+    of `value`): the probability selection score and block-level selection
+    (full layer), and the sparse layers gathering from the FP8 copy of the
+    cache."""
     _, _, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, workspace=ws)
     copy = hs.kv_to_fp8(kv, n_kv=w.n_kv)
     shape = hs.make_shape(batch=w.B, n_q=w.n_q, n_kv=w.n_kv, kv_capacity=kv.shape[2], q_heads=w.Hq,
                           kv_heads=w.Hkv, top_k=w.top_k, window=w.window, flags=hs.HS_FLAG_PROB_SCORE)
     ws_prob = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), "cuda:0")
+    shape.flags = hs.HS_FLAG_BLOCK_SELECT
+    ws_blk = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), "cuda:0")
     runs = {
         "prob_score_full_layer": lambda: hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window,
                                                              flags=hs.HS_FLAG_PROB_SCORE, workspace=ws_prob),
+        "block_select_full_layer": lambda: hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window,
+                                                               flags=hs.HS_FLAG_BLOCK_SELECT, workspace=ws_blk),
         "fp8_cache_conversion": lambda: hs.kv_to_fp8(kv, n_kv=w.n_kv, out=copy),
         "fp8_sparse_layer": lambda: hs.sparse_attn_reuse(qs[0], kv, idx, top_k=w.top_k, window=w.window,
                                                          n_kv=w.n_kv, kv_fp8=copy),
@@ -130,7 +135,7 @@ def prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch):
         out[name] = {"ms": round(sum(t for n, t in kt.values()) / 3, 3),
                      "kernels_us": {k: round(t / n * 1e3, 1) for k, (n, t) in kt.items()}}
         log(f"[bench] {w.name} {name}: {out[name]}")
-    del copy, ws_prob
+    del copy, ws_prob, ws_blk
     return out
 
 
@@ -240,6 +245,24 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
     fp8_append_us = kf["kv_fp8_convert"][1] / kf["kv_fp8_convert"][0] * 1e3
     log(f"[bench] {wname}: fp8 sparse layer {fp8_sparse_us:.1f} us, appended-row conversion {fp8_append_us:.1f} us")
     del copy
+    # option: block-level selection (block scores from the score rows, then
+    # the top blocks), against the token-level selection timed above
+    shape.flags = hs.HS_FLAG_BLOCK_SELECT
+    ws_blk = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
+    shape.flags = 0
+    blk_call = lambda: hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
+                                      window=w.window, flags=hs.HS_FLAG_BLOCK_SELECT, workspace=ws_blk)
+    blk_call()
+    torch.cuda.synchronize()
+    _lib.timing_read()
+    _lib.timing_enable(True)
+    blk_call()
+    torch.cuda.synchronize()
+    _lib.timing_enable(False)
+    kb = _lib.timing_read()
+    blk_sel_us = sum(kb[k][1] / kb[k][0] * 1e3 for k in ("block_max", "select_blocks"))
+    log(f"[bench] {wname}: block-level selection {blk_sel_us:.1f} us (block scores + top blocks)")
+    del ws_blk
     # algorithmic bytes
     full_bytes = sum(512.0 * w.Hkv * (L + s + 1) for L in lengths for s in range(steps)) / steps
     sp_rows = sum(min(w.top_k, max(0, L + s + 1 - w.window)) + min(w.window, L + s + 1)
@@ -256,6 +279,7 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
         "sparse_layer_kernel_us": round(sp_us, 2),
         "fp8_sparse_layer_kernel_us": round(fp8_sparse_us, 2),
         "fp8_append_conversion_us": round(fp8_append_us, 2),
+        "block_select_us": round(blk_sel_us, 2),
         "kernels": {k: {"launches_per_step": n / steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()},
         "sparse_decode_roofline": {"bound": "hbm", "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",

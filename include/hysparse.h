@@ -120,6 +120,16 @@ typedef enum {
                                    hs_full_attn_select and hs_decode_step;
                                    lse may still be NULL (kept in the
                                    workspace). */
+/* Block-level selection, the choice that token-level selection replaces
+   ([HS2-cs] section "Proc neni nutne znovu zpracovat cely dlouhy vstup";
+   [DAIR] bullet "Prefill exits early"), kept as an ablation: C(p) is cut into aligned
+   blocks of 64 tokens, a block scores the largest sigma of its candidates,
+   the top top_k/64 blocks (ties: lower block first) are taken whole and
+   written as their tokens, ascending, -1 padded (the last block of C(p) may
+   be partial). Needs top_k % 64 == 0 (else HS_ERR_INVALID_ARG); not
+   combined with HS_FLAG_PROB_SCORE (HS_ERR_UNSUPPORTED). Read by
+   hs_full_attn_select and hs_decode_step. */
+#define HS_FLAG_BLOCK_SELECT 8u
 #define HS_FLAG_FP8_KV 4u       /* hs_sparse_attn_reuse reads its keys and
                                    values from the FP8 copy of the cache
                                    made by hs_kv_fp8_convert (kv then points

@@ -45,7 +45,7 @@ design notes of the repository):
   R7 GQA: query head h reads KV head h // G, G = Hq / Hkv.
   R8 the selection decision is taken on float32 scores (float64 evaluation
      rounded once to float32), the precision the kernels decide in.
-  R9 (optional, block-level selection, the ablation the pages compare
+  R11 (optional, block-level selection, the ablation the pages compare
      token-level selection against): C(p) is cut into aligned blocks of 64
      tokens, a block scores the maximum sigma of its candidates, the top
      k / 64 blocks (ties: lower block first) are taken whole (the last block
@@ -201,7 +201,7 @@ def topk_select(sigma: np.ndarray, k: int):
 
 
 def block_select(sigma: np.ndarray, k: int, block: int = 64):
-    """Block-level selection (reading R9) over the candidate scores of one
+    """Block-level selection (reading R11) over the candidate scores of one
     (row, group): blocks [block*b, block*b + block) of C(p), block score =
     the largest member score, the top k // block blocks by (score desc, block
     index asc) decided on float32 scores (R8), expanded to their tokens.
@@ -235,7 +235,7 @@ def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
     It computes causal GQA attention and, per (row, KV group), the top-k token
     indices that the following sparse layers reuse [HS2-cs], [DAIR].
     score: "logit" (reading R1) or "prob" (reading R1', which needs this
-    layer's lse first); blocks: block-level selection (reading R9) instead of
+    layer's lse first); blocks: block-level selection (reading R11) instead of
     token-level. Returns dict with o [rows][Hq][d], lse [rows][Hq],
     idx [rows][Hkv][k] (int64), tau [rows][Hkv], sigma (list of per-(row,
     group) float64 arrays).

@@ -68,6 +68,32 @@ def check_idx_row(got: np.ndarray, ref: np.ndarray, sigma: np.ndarray, tau: floa
     return len(diff)
 
 
+def check_block_row(got: np.ndarray, ref: np.ndarray, sigma: np.ndarray, tau: float, p: int, window: int, k: int,
+                    where="", block=64):
+    """Block-level selection row: whole aligned blocks of C(p), ascending, the
+    min(k / block, blocks of C(p)) of them expanded to their tokens, then -1
+    padding; the GPU block set may differ from the oracle's only by blocks
+    whose block score lies within 1e-3 of the oracle's last block score."""
+    ncand = max(0, p - window + 1)
+    nblk = -(-ncand // block)
+    nsel = min(k // block, nblk)
+    got = np.asarray(got, np.int64)
+    assert got.shape == (k,), where
+    v = got[got >= 0]
+    gb = sorted(set((v // block).tolist()))
+    assert len(gb) == nsel, f"{where}: {len(gb)} blocks, want {nsel}"
+    want = np.concatenate([np.arange(b * block, min((b + 1) * block, ncand)) for b in gb]) if gb else \
+        np.zeros(0, np.int64)
+    assert np.array_equal(got[:len(want)], want) and np.all(got[len(want):] == -1), \
+        f"{where}: not whole ascending blocks then padding: {got[:8]}..."
+    R = set(int(x) // block for x in ref if x >= 0)
+    diff = set(gb) ^ R
+    for b in diff:
+        bs = float(sigma[b * block:(b + 1) * block].max())
+        assert abs(bs - tau) <= TIE_BAND, f"{where}: block {b} differs (score {bs:.6f}, tau {tau:.6f})"
+    return len(diff)
+
+
 def cache_np(kv: torch.Tensor, b: int, n: int):
     """K, V of sequence b as float64 numpy [Hkv][n][d] (exact widening of bf16;
     float64 so that the oracle takes contiguous ranges as views)."""
@@ -93,9 +119,10 @@ def sample_rows(n_q: int, n_kv: int, top_k: int, window: int, spans=(), evenly=8
 
 
 def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_sparse=(), o_sparse=(), scale=None,
-                  score="logit"):
+                  score="logit", blocks=False):
     """Checks one prefill call (and its sparse layers) on the given query rows;
-    score names the oracle's selection score ("logit" or "prob")."""
+    score names the oracle's selection score ("logit" or "prob"), blocks asks
+    for block-level selection."""
     B, n_q, Hq, d = q_full.shape
     scale = orc.default_scale(d) if scale is None else scale
     rows = list(range(n_q)) if rows is None else list(rows)
@@ -109,13 +136,14 @@ def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_spa
     for b in range(B):
         K, V = cache_np(kv, b, n_kv)
         qb = f32(q_full[b])[rows]
-        res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale, score)
+        res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale, score, blocks=blocks)
+        check_row = check_block_row if blocks else check_idx_row
         full_stats.add(o_np[b, rows], res["o"])
         if lse_np is not None:
             lse_stats.add(lse_np[b][:, rows].T, res["lse"])
         for r, t in enumerate(rows):
             for g in range(K.shape[0]):
-                swaps += check_idx_row(idx_np[b, t, g], res["idx"][r, g], res["sigma"][r][g], res["tau"][r, g],
+                swaps += check_row(idx_np[b, t, g], res["idx"][r, g], res["sigma"][r][g], res["tau"][r, g],
                                        int(pos[r]), window, top_k, where=f"b{b} t{t} g{g}")
         gidx = idx_np[b][rows]
         for qs, osp in zip(qs_np, os_np):

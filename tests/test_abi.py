@@ -70,7 +70,9 @@ def base_shape(**kw):
     (dict(window=0), _lib.HS_ERR_INVALID_ARG),
     (dict(n_q=65), _lib.HS_ERR_INVALID_ARG),
     (dict(n_kv=65), _lib.HS_ERR_INVALID_ARG),
-    (dict(flags=8), _lib.HS_ERR_INVALID_ARG),
+    (dict(flags=16), _lib.HS_ERR_INVALID_ARG),
+    (dict(flags=_lib.HS_FLAG_BLOCK_SELECT), _lib.HS_ERR_INVALID_ARG),  # top_k 16 is not whole blocks
+    (dict(flags=_lib.HS_FLAG_BLOCK_SELECT | _lib.HS_FLAG_PROB_SCORE, top_k=64), _lib.HS_ERR_UNSUPPORTED),
     (dict(kv_strides=(0, 0, 12, 0)), _lib.HS_ERR_INVALID_ARG),
 ])
 def test_invalid_shapes_rejected_before_launch(lib, kw, status):

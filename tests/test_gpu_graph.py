@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("option", ["default", "prob_score", "fp8_cache"])
+@pytest.mark.parametrize("option", ["default", "prob_score", "fp8_cache", "block_select"])
 def test_decode_graph_matches_eager(option):
     lengths = [4093, 700, 64, 2500, 1, 3000]  # the longest crosses 4096 -> a second bucket
     B, Hq, Hkv, k, W, nsl, steps = len(lengths), 32, 4, 256, 64, 2, 6
@@ -22,7 +22,7 @@ def test_decode_graph_matches_eager(option):
     for b, L in enumerate(lengths):
         kv_a[b, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 700 + b, DEV)
     kv_b = kv_a.clone()
-    flags = hs.HS_FLAG_PROB_SCORE if option == "prob_score" else 0
+    flags = {"prob_score": hs.HS_FLAG_PROB_SCORE, "block_select": hs.HS_FLAG_BLOCK_SELECT}.get(option, 0)
     f8_a = hs.kv_to_fp8(kv_a, n_kv=cap) if option == "fp8_cache" else None
     f8_b = f8_a.clone() if f8_a is not None else None
     g = hs.DecodeStepGraph(kv_b, batch=B, q_heads=Hq, sparse_layers=nsl, top_k=k, window=W, flags=flags,

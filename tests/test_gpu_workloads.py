@@ -17,7 +17,8 @@ DEV = "cuda:0"
 def run_prefill_workload(name, evenly=8, flags=0):
     w = synth.WORKLOADS[name]
     score = "prob" if flags & hs.HS_FLAG_PROB_SCORE else "logit"
-    print(f"[case] workload {name}: B={w.B} n_q={w.n_q} n_kv={w.n_kv} k={w.top_k} W={w.window} score={score}",
+    blocks = bool(flags & hs.HS_FLAG_BLOCK_SELECT)
+    print(f"[case] workload {name}: B={w.B} n_q={w.n_q} n_kv={w.n_kv} k={w.top_k} W={w.window} score={score} blocks={blocks}",
           flush=True)
     case = synth.make_prefill_case(w, DEV, kv_capacity=w.n_kv + w.decode_steps)
     q, kv, qs = case["q_full"], case["kv"], case["q_sparse"]
@@ -28,7 +29,7 @@ def run_prefill_workload(name, evenly=8, flags=0):
     rows = sample_rows(w.n_q, w.n_kv, w.top_k, w.window, spans, evenly)
     print(f"[case] checking rows {rows}", flush=True)
     res = check_prefill(q, kv, w.n_kv, w.top_k, w.window, o, lse, idx, rows=rows, q_sparse=qs, o_sparse=osp,
-                        score=score)
+                        score=score, blocks=blocks)
     print(f"[case] {name}: near-tie swaps {res['swaps']}, full max-abs {res['full'].max_abs:.2e} "
           f"mean {res['full'].mean_abs:.2e}, sparse max-abs {res['sparse'].max_abs:.2e}", flush=True)
     # needles: the planted keys should mostly be selected by their span rows
@@ -52,6 +53,12 @@ def test_prefill32k_full_size_prob_score():
     """The probability selection score at full size (attention, then the
     sampled threshold and the QK-only candidate pass on its lse)."""
     run_prefill_workload("prefill32k", evenly=4, flags=hs.HS_FLAG_PROB_SCORE)
+
+
+def test_prefill32k_full_size_block_select():
+    """Block-level selection at full size: block scores from the attention
+    pass, then the top top_k/64 blocks per row."""
+    run_prefill_workload("prefill32k", evenly=4, flags=hs.HS_FLAG_BLOCK_SELECT)
 
 
 def test_chunk128k_full_size():

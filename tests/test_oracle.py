@@ -507,7 +507,7 @@ def test_fp8_quantiser_error_bound_and_exact_values():
     assert list(sat) == [448.0, -448.0]
 
 
-# ---------------------------------------------------------------- block-level selection (reading R9)
+# ---------------------------------------------------------------- block-level selection (reading R11)
 
 def test_block_select_with_unit_blocks_is_token_select():
     rng = np.random.default_rng(61)

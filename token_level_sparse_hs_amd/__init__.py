@@ -18,10 +18,10 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import HS_FLAG_EXACT_RESCAN, HS_FLAG_FP8_KV, HS_FLAG_PROB_SCORE, HsError, HsShape  # noqa: F401
+from ._lib import HS_FLAG_BLOCK_SELECT, HS_FLAG_EXACT_RESCAN, HS_FLAG_FP8_KV, HS_FLAG_PROB_SCORE, HsError, HsShape  # noqa: F401
 
 __all__ = ["full_attn_select", "sparse_attn_reuse", "decode_step", "make_shape", "HsError",
-           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "kv_to_fp8", "version"]
+           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "HS_FLAG_BLOCK_SELECT", "kv_to_fp8", "version"]
 
 
 def version() -> int:

@@ -82,8 +82,12 @@ hs_status validate_common(const hs_shape* s, Layout* lay) {
   if (s->window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", s->window);
   if (s->kv_capacity < 1) return fail(HS_ERR_INVALID_ARG, "kv_capacity must be >= 1");
   if (!(s->scale >= 0.f) || std::isinf(s->scale)) return fail(HS_ERR_INVALID_ARG, "scale must be finite and >= 0");
-  if ((s->flags & ~(HS_FLAG_EXACT_RESCAN | HS_FLAG_PROB_SCORE | HS_FLAG_FP8_KV)) != 0)
+  if ((s->flags & ~(HS_FLAG_EXACT_RESCAN | HS_FLAG_PROB_SCORE | HS_FLAG_FP8_KV | HS_FLAG_BLOCK_SELECT)) != 0)
     return fail(HS_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  if ((s->flags & HS_FLAG_BLOCK_SELECT) && s->top_k % 64 != 0)
+    return fail(HS_ERR_INVALID_ARG, "block-level selection needs top_k %% 64 == 0 (got %d)", s->top_k);
+  if ((s->flags & HS_FLAG_BLOCK_SELECT) && (s->flags & HS_FLAG_PROB_SCORE))
+    return fail(HS_ERR_UNSUPPORTED, "block-level selection uses the logit score");
   if ((s->flags & HS_FLAG_FP8_KV) && (s->kv_stride_b || s->kv_stride_h || s->kv_stride_t || s->kv_v_offset))
     return fail(HS_ERR_INVALID_ARG, "the FP8 cache copy has a fixed layout: strides must be 0");
   Layout l;
@@ -124,8 +128,10 @@ struct PrefillPlan {
   int max_samples = 0;
   bool sample = false;
   size_t off_theta = 0, off_counts = 0, off_bs = 0, off_bj = 0, off_samples = 0, off_stat = 0, off_defer = 0,
-         off_lse = 0, total = 0;
+         off_lse = 0, off_blk = 0, total = 0;
   bool prob = false;  // probability score: selection pass after attention, lse kept here
+  bool block = false; // block-level selection: block scores at off_blk
+  int blk_stride = 0;
 };
 
 PrefillPlan plan_prefill(const hs_shape* s) {
@@ -133,6 +139,13 @@ PrefillPlan plan_prefill(const hs_shape* s) {
   p.rows = (int64_t)s->batch * s->n_q * s->kv_heads;
   if (s->top_k == 0) return p;
   const int64_t max_cand = std::max<int64_t>(0, (int64_t)s->n_kv - s->window + 1);
+  if (s->flags & HS_FLAG_BLOCK_SELECT) {  // block scores only
+    p.block = true;
+    p.blk_stride = (int)std::max<int64_t>(1, (max_cand + 63) / 64);
+    p.off_blk = 0;
+    p.total = align_up((size_t)p.rows * p.blk_stride * 4);
+    return p;
+  }
   p.cap = (int)std::min<int64_t>(round_up(3 * (int64_t)s->top_k + 256, 64), std::max<int64_t>(max_cand, 1));
   p.sample = max_cand > p.cap;
   p.stride = std::max(1, s->top_k / 64);
@@ -167,8 +180,10 @@ struct DecodePlan {
   int64_t sigma_stride = 0;
   int sel_slices = 0;     // sliced selection (0: one block per row)
   bool prob = false;      // probability score: score pass after the full layer
+  bool block = false;     // block-level selection from the score rows
+  int blk_stride = 0;
   size_t off_sigma = 0, off_part = 0, off_theta = 0, off_segcnt = 0, off_segkey = 0, off_segidx = 0, off_lse = 0,
-         total = 0;
+         off_blk = 0, total = 0;
 };
 
 // Splits a per-(b, g) key stream of up to `nkeys` keys so that the grid holds
@@ -215,7 +230,7 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   // row, are selected in slices instead.
   const int64_t max_cand = (int64_t)max_seq_len - s->window;
   const double expect = s->top_k + 6.0 * std::sqrt((double)s->top_k * (double)max_cand / 2048.0);
-  if (s->top_k > 0 && max_cand > hs::kSelRegKeys && (bg < kChipSimds / 4 || expect > 0.75 * hs::kSelRegKeys)) {
+  if (s->top_k > 0 && !(s->flags & HS_FLAG_BLOCK_SELECT) && max_cand > hs::kSelRegKeys && (bg < kChipSimds / 4 || expect > 0.75 * hs::kSelRegKeys)) {
     const int64_t ns = (max_cand + hs::kDecSlice - 1) / hs::kDecSlice;
     if (ns <= hs::kMaxDecSlices) p.sel_slices = (int)ns;
   }
@@ -234,6 +249,12 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   if (p.prob) {
     p.off_lse = o;
     o = align_up(o + (size_t)s->batch * s->q_heads * 4);
+  }
+  p.block = s->top_k > 0 && (s->flags & HS_FLAG_BLOCK_SELECT) != 0;
+  if (p.block) {
+    p.blk_stride = (int)std::max<int64_t>(1, (max_cand + 64) / 64);
+    p.off_blk = o;
+    o = align_up(o + (size_t)bg * p.blk_stride * 4);
   }
   p.total = o;
   return p;
@@ -430,6 +451,24 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
   // sampled threshold and a QK-only candidate pass
   const bool prob = select && plan.prob;
   float* lse_buf = prob && !lse ? reinterpret_cast<float*>(w + plan.off_lse) : lse;
+  if (select && plan.block) {
+    hs::PrefillParams pp{};
+    pp.q = static_cast<const uint16_t*>(q);
+    pp.kv = kvv;
+    pp.o = static_cast<uint16_t*>(o);
+    pp.lse = lse;
+    pp.B = s->batch; pp.n_q = s->n_q; pp.n_kv = s->n_kv; pp.Hq = s->q_heads; pp.Hkv = s->kv_heads; pp.window = s->window;
+    pp.scale = scale;
+    pp.select = 2;
+    pp.blk_score = reinterpret_cast<float*>(w + plan.off_blk);
+    pp.blk_stride = plan.blk_stride;
+    HIP_TRY(timed("prefill_attn", hst, [&] { return hs::launch_prefill_attn(pp, hst); }));
+    hs::BlockSelectParams bp{};
+    bp.B = s->batch; bp.n_q = s->n_q; bp.n_kv = s->n_kv; bp.Hkv = s->kv_heads; bp.top_k = s->top_k; bp.window = s->window;
+    bp.blk_score = pp.blk_score; bp.blk_stride = plan.blk_stride; bp.idx = idx;
+    HIP_TRY(timed("select_blocks", hst, [&] { return hs::launch_select_blocks(bp, plan.rows, hst); }));
+    return ok();
+  }
 
   hs::PrefillParams pp{};
   pp.q = static_cast<const uint16_t*>(q);
@@ -610,6 +649,18 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
     zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window;
     HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
+  }
+  if (plan.block) {
+    hs::BlockMaxParams mp{};
+    mp.sigma = sigma; mp.sigma_stride = plan.sigma_stride; mp.seq_lens = seq_lens;
+    mp.B = s->batch; mp.Hkv = s->kv_heads; mp.window = s->window;
+    mp.blk_score = reinterpret_cast<float*>(w + plan.off_blk); mp.blk_stride = plan.blk_stride;
+    HIP_TRY(timed("block_max", hst, [&] { return hs::launch_block_max(mp, hst); }));
+    hs::BlockSelectParams bp{};
+    bp.B = s->batch; bp.n_q = 1; bp.Hkv = s->kv_heads; bp.top_k = s->top_k; bp.window = s->window;
+    bp.seq_lens = seq_lens; bp.blk_score = mp.blk_score; bp.blk_stride = plan.blk_stride; bp.idx = idx;
+    HIP_TRY(timed("select_blocks", hst, [&] { return hs::launch_select_blocks(bp, (int64_t)s->batch * s->kv_heads, hst); }));
+    return ok();
   }
   if (s->top_k > 0) {
     hs::SelectDecodeParams sp{};

@@ -19,8 +19,12 @@ struct PrefillParams {
   float* lse;         // [B][Hq][n_q] or null
   int B, n_q, n_kv, Hq, Hkv, window;
   float scale;
-  // selection (select == 0: no selection, buffers unused)
+  // selection (select == 0: no selection, buffers unused; 1: token-level
+  // candidates into buf_sigma / buf_j; 2: block level, the best scaled score
+  // of each 64-key block's candidates into blk_score)
   int select;
+  float* blk_score;    // [rows][blk_stride]
+  int blk_stride;
   const float* theta;  // [rows] scaled-score threshold per (b,t,g) row
   float* buf_sigma;    // [rows][cap]
   int32_t* buf_j;      // [rows][cap]
@@ -108,6 +112,27 @@ struct DecodeScoreParams {
   int max_cand;       // bound on |C(p)| over the batch (grid size)
 };
 hipError_t launch_decode_prob_score(const DecodeScoreParams& p, hipStream_t s);
+
+// Block-level selection: the top top_k/64 blocks of each row by block score
+// (ties: lower block), expanded to their candidate tokens.
+struct BlockSelectParams {
+  int B, n_q, n_kv, Hkv, top_k, window;
+  const int32_t* seq_lens;  // decode rows; null for prefill rows
+  const float* blk_score;   // [rows][blk_stride]
+  int blk_stride;
+  int32_t* idx;             // [rows][top_k]
+};
+hipError_t launch_select_blocks(const BlockSelectParams& p, int64_t rows, hipStream_t s);
+// Decode: block scores from the dense score rows.
+struct BlockMaxParams {
+  const float* sigma;
+  int64_t sigma_stride;
+  const int32_t* seq_lens;
+  int B, Hkv, window;
+  float* blk_score;
+  int blk_stride;
+};
+hipError_t launch_block_max(const BlockMaxParams& p, hipStream_t s);
 
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s);
 hipError_t launch_threshold(const ThresholdParams& p, int64_t rows, hipStream_t s);

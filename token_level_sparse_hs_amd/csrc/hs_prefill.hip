@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   int cnt[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    const bool ok = P.select && wt0 + u < P.n_q;
+    const bool ok = P.select == 1 && wt0 + u < P.n_q;
     theta[u] = ok ? __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, P.theta[row0 + (int64_t)u * P.Hkv])))
                   : kPosInf;
     cnt[u] = 0;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     asm volatile("s_barrier" ::: "memory");
     if (kt + 1 < ntiles) fetch(kt + 1, std::integral_constant<int, 1 - S>{});
     const bool sel_tile = P.select && wave_live && key0 <= p_whi - P.window;
-    stores_pending = sel_tile;
+    stores_pending = sel_tile && P.select == 1;  // exactly kStores stores follow (block level: wait for all)
     if (!(wave_live && key0 <= p_whi)) return;
     const uint8_t* Kb = S ? kv_st1[0] : kv_st0[0];
     const uint8_t* Vb = S ? kv_st1[1] : kv_st0[1];
@@ -400,7 +400,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     // threshold is appended, in ascending key order, to the row's buffer.
     // Exactly kStores range-checked stores per tile: failing lanes and
     // positions past the buffer's capacity aim beyond the row and are dropped.
-    if (sel_tile) {
+    if (sel_tile && P.select == 2) {
+      // block level: the best scaled score among the tile's candidates of
+      // each row (the tile is one 64-key block). Row u's 64 scores are spread
+      // over 64 / TPW consecutive lanes, TPW scores each, then reduced
+      // across those lanes (DPP within a 16-lane row).
+      constexpr int LPR = 64 / TPW;
+      const int u = lane / LPR, c0 = (lane % LPR) * TPW;
+      const int lim = off + wt0 + u - P.window - key0;  // last candidate, tile-relative
+      const float* ws = sig[wave] + u * 64 + c0;
+      float v = kNegInf;
+#pragma unroll
+      for (int i = 0; i < TPW; i += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(ws + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v = c0 + i + e <= lim ? fmaxf(v, x[e]) : v;
+      }
+      if constexpr (LPR >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+      if constexpr (LPR >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+      if constexpr (LPR >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+      if constexpr (LPR >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+      if (lane % LPR == 0 && wt0 + u < P.n_q)
+        P.blk_score[(row0 + (int64_t)u * P.Hkv) * P.blk_stride + (key0 >> 6)] = v * P.scale;
+    } else if (sel_tile) {
       const float* ws = sig[wave];
       const int j = key0 + lane;
 #pragma unroll
@@ -443,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       }
     if (P.lse && h == 0) P.lse[((int64_t)b * P.Hq + head) * P.n_q + tok] = m_run * kLn2 + __logf(l_tot);
   }
-  if (P.select && lane == 0) {
+  if (P.select == 1 && lane == 0) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
       if (wt0 + u < P.n_q) P.counts[row0 + (int64_t)u * P.Hkv] = cnt[u];

@@ -999,6 +999,154 @@ hipError_t launch_decode_prob_score(const DecodeScoreParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Block-level selection: the block scores of C(p) (one per aligned 64-token
+// block) go through the same exact top-k as token scores (ties: lower block
+// first), and the chosen blocks, ascending, are expanded to their candidate
+// tokens (only the last block of C(p) can be partial, and it comes last, so
+// the padding stays at the end).
+struct BlockRow {
+  int ncand, nblk, nb;
+};
+__device__ __forceinline__ BlockRow block_row(const BlockSelectParams& P, int64_t row) {
+  int p;
+  if (P.seq_lens) {
+    p = P.seq_lens[row / P.Hkv] - 1;
+  } else {
+    const int t = (int)((row / P.Hkv) % P.n_q);
+    p = P.n_kv - P.n_q + t;
+  }
+  BlockRow r;
+  r.ncand = imax(0, p - P.window + 1);
+  r.nblk = (r.ncand + 63) / 64;
+  r.nb = P.top_k / 64;
+  return r;
+}
+
+// Rows of up to 64 * kBlkWaveE blocks: one wave per row, block scores in
+// registers, the cut found by wave_radix, the chosen blocks listed in LDS in
+// ascending order, then written out 64 tokens (one block) per store.
+constexpr int kBlkWaveE = 16;
+constexpr int kMaxSelBlocks = kMaxTopK / 64;
+__global__ __launch_bounds__(256, 2) void select_blocks_wave_kernel(BlockSelectParams P, int64_t rows) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kHistCopies * kHistStride];
+  __shared__ int32_t chosen_all[4][kMaxSelBlocks];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = uniform64((int64_t)blockIdx.x * 4 + wave);
+  if (row >= rows) return;
+  const BlockRow br = block_row(P, row);
+  int32_t* out = P.idx + row * P.top_k;
+  if (br.nblk <= br.nb) {
+    for (int i = lane; i < P.top_k; i += 64) out[i] = i < br.ncand ? i : -1;
+    return;
+  }
+  const float* bs = P.blk_score + row * (int64_t)P.blk_stride;
+  uint32_t key[kBlkWaveE];
+#pragma unroll
+  for (int e = 0; e < kBlkWaveE; ++e) {
+    const int i = 64 * e + lane;
+    key[e] = i < br.nblk ? score_key(bs[i]) : 0u;
+  }
+  const RadixResult r = wave_radix<kBlkWaveE>(hist_all[wave], key, br.nblk, (uint32_t)br.nb);
+  int32_t* chosen = chosen_all[wave];
+  uint32_t out_run = 0, eq_run = 0;
+#pragma unroll
+  for (int e = 0; e < kBlkWaveE; ++e) {
+    if (64 * e >= br.nblk) continue;
+    const uint32_t kk = key[e];
+    const uint32_t km = kk & r.mask;
+    const bool gt = kk != 0u && km > r.prefix;
+    const bool eq = kk != 0u && km == r.prefix;
+    const uint64_t eqm = ballot(eq);
+    const uint32_t eq_before = eq_run + lane_prefix(eqm);
+    eq_run += (uint32_t)__popcll(eqm);
+    const bool sel = gt || (eq && (r.take_all || eq_before < r.need));
+    const uint64_t selm = ballot(sel);
+    if (sel) chosen[out_run + lane_prefix(selm)] = 64 * e + lane;
+    out_run += (uint32_t)__popcll(selm);
+  }
+  // the wave's LDS writes are complete before its reads below
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  for (int b = 0; b < P.top_k / 64; ++b) {
+    const int j = b < br.nb ? chosen[b] * 64 + lane : br.ncand;
+    out[64 * b + lane] = j < br.ncand ? j : -1;
+  }
+}
+
+// Longer rows: one block per row, through the block-wide top-k.
+__global__ __launch_bounds__(kSelThreads) void select_blocks_kernel(BlockSelectParams P) {
+  __shared__ SelShared sh;
+  __shared__ SelLds<true> lds;
+  __shared__ int32_t chosen[kMaxSelBlocks];
+  const int64_t row = blockIdx.x;
+  const BlockRow br = block_row(P, row);
+  int nsel = br.nblk;
+  if (br.nblk <= br.nb) {
+    for (int i = threadIdx.x; i < br.nblk; i += kSelThreads) chosen[i] = i;
+  } else {
+    topk_any<true>(sh, lds.key, lds.idx, DenseSrc{P.blk_score + row * P.blk_stride}, br.nblk, br.nb, chosen);
+    nsel = br.nb;
+  }
+  __syncthreads();
+  int32_t* out = P.idx + row * P.top_k;
+  for (int i = threadIdx.x; i < P.top_k; i += kSelThreads) {
+    const int r = i >> 6;
+    int v = -1;
+    if (r < nsel) {
+      const int j = chosen[r] * 64 + (i & 63);
+      if (j < br.ncand) v = j;
+    }
+    out[i] = v;
+  }
+}
+
+// Decode: block scores of each (b, g) row from its dense score row. A wave
+// reads 1 KB (four blocks) per load, 16 lanes to a block, each lane's four
+// scores reduced in registers and then across its 16 lanes; a 256-thread
+// block covers 64 blocks.
+__global__ __launch_bounds__(256) void block_max_kernel(BlockMaxParams P) {
+  const int row = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ncand = imax(0, P.seq_lens[row / P.Hkv] - P.window);
+  const int blk0 = blockIdx.x * 64 + wave * 16;  // first of the wave's 16 blocks
+  if (blk0 * 64 >= ncand) return;
+  const float* s = P.sigma + (int64_t)row * P.sigma_stride;
+  f32x4 x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = (blk0 + 4 * u) * 64 + 4 * lane;  // first of this lane's four keys
+    x[u] = j < ncand ? *reinterpret_cast<const f32x4*>(s + j) : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = (blk0 + 4 * u) * 64 + 4 * lane;
+    float v = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v = j + e < ncand ? fmaxf(v, x[u][e]) : v;
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    const int blk = blk0 + 4 * u + lane / 16;
+    if ((lane & 15) == 0 && blk * 64 < ncand) P.blk_score[(int64_t)row * P.blk_stride + blk] = v;
+  }
+}
+
+hipError_t launch_select_blocks(const BlockSelectParams& p, int64_t rows, hipStream_t s) {
+  if (p.blk_stride <= 64 * kBlkWaveE)
+    select_blocks_wave_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
+  else
+    select_blocks_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_max(const BlockMaxParams& p, hipStream_t s) {
+  const unsigned gx = (unsigned)((std::max(p.blk_stride, 1) + 63) / 64);
+  block_max_kernel<<<dim3(gx, (unsigned)(p.B * p.Hkv)), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s) {
   select_prefill_wave_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
   hipError_t e = hipGetLastError();
