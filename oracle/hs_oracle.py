@@ -50,6 +50,11 @@ design notes of the repository):
      tokens, a block scores the maximum sigma of its candidates, the top
      k / 64 blocks (ties: lower block first) are taken whole (the last block
      of C(p) may be partial), emitted ascending and padded with -1.
+  R12 (optional, union of per-head top-k, the grouped-unfolding rule of
+     [SSA-3.3]): each query head h of group g ranks C(p) by its own scaled
+     logit and keeps its top k (rules R4, R5, R8 per head); the group's set
+     is the union of the G head sets, emitted ascending in a row of G * k
+     entries padded with -1.
   R1' (optional score, score="prob"): the softmax-normalised group score
      max over h of (scale * <q_h(t), k_g(j)> - lse_h(t)), lse_h(t) the log
      of the softmax denominator of head h over keys 0..p, i.e. the log of the
@@ -71,6 +76,7 @@ __all__ = [
     "full_attention_rows",
     "selection_scores",
     "topk_select",
+    "head_union_select",
     "full_attn_select_rows",
     "sparse_attention_rows",
     "decode_step",
@@ -227,9 +233,27 @@ def block_select(sigma: np.ndarray, k: int, block: int = 64):
     return out, tau
 
 
+def head_union_select(q_group: np.ndarray, Kg: np.ndarray, p: int, window: int, scale: float, k: int):
+    """Union of per-head top-k sets for one (row, group) (reading R12,
+    [SSA-3.3] "Grouped Unfolding for GQA"): every head's own token-level
+    top-k over C(p), then the set union. Returns (idx of length G*k,
+    ascending, -1 padded; list of the G heads' (sigma_h, tau_h))."""
+    G = q_group.shape[0]
+    out = np.full(G * k, -1, dtype=np.int64)
+    chosen, heads = set(), []
+    for h in range(G):
+        s_h = selection_scores(q_group[h:h + 1], Kg, p, window, scale)
+        idx_h, tau_h = topk_select(s_h, k)
+        chosen.update(int(j) for j in idx_h if j >= 0)
+        heads.append((s_h, tau_h))
+    u = sorted(chosen)
+    out[:len(u)] = u
+    return out, heads
+
+
 def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
                           positions, k: int, window: int, scale: float, score: str = "logit",
-                          blocks: bool = False):
+                          blocks: bool = False, union: bool = False):
     """The full-attention layer of a hybrid block for the given query rows.
 
     It computes causal GQA attention and, per (row, KV group), the top-k token
@@ -238,7 +262,9 @@ def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
     layer's lse first); blocks: block-level selection (reading R11) instead of
     token-level. Returns dict with o [rows][Hq][d], lse [rows][Hq],
     idx [rows][Hkv][k] (int64), tau [rows][Hkv], sigma (list of per-(row,
-    group) float64 arrays).
+    group) float64 arrays). union: the union of per-head top-k sets
+    (reading R12, logit score only); idx is then [rows][Hkv][G*k] and
+    "heads" holds, per (row, group), the G heads' (sigma_h, tau_h).
     """
     if score not in ("logit", "prob"):
         raise ValueError("score must be 'logit' or 'prob'")
@@ -246,6 +272,19 @@ def full_attn_select_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
     Hkv = K.shape[0]
     G = _check_gqa(Hq, Hkv)
     o, lse = full_attention_rows(q, K, V, positions, scale)
+    if union:
+        if score != "logit" or blocks:
+            raise ValueError("the per-head union uses token-level logit scores")
+        idx = np.full((rows, Hkv, G * k), -1, dtype=np.int64)
+        heads = []
+        for r in range(rows):
+            row_heads = []
+            for g in range(Hkv):
+                idx[r, g], hh = head_union_select(q[r, g * G:(g + 1) * G], K[g], int(positions[r]), window,
+                                                  scale, k)
+                row_heads.append(hh)
+            heads.append(row_heads)
+        return {"o": o, "lse": lse, "idx": idx, "heads": heads}
     idx = np.full((rows, Hkv, k), -1, dtype=np.int64)
     tau = np.full((rows, Hkv), -math.inf)
     sig = []
@@ -288,7 +327,7 @@ def sparse_attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray,
 
 def decode_step(q_full: np.ndarray, q_sparse: list, kv_new: np.ndarray,
                 K: np.ndarray, V: np.ndarray, length: int, k: int,
-                window: int, scale: float, score: str = "logit", blocks: bool = False):
+                window: int, scale: float, score: str = "logit", blocks: bool = False, union: bool = False):
     """One decode step of one sequence through a hybrid block.
 
     The new token's key/value row is written at slot length-1 of the cache
@@ -296,19 +335,25 @@ def decode_step(q_full: np.ndarray, q_sparse: list, kv_new: np.ndarray,
     once; every sparse layer reuses that one selection and the same cache
     [HS2-cs], [DAIR]. q_full: [Hq][d]; q_sparse: list of [Hq][d]; kv_new:
     [Hkv][2][d]; K, V: [Hkv][cap][d] float arrays, modified in place.
-    Returns dict(o_full, lse_full, idx [Hkv][k], tau, sigma, o_sparse list).
+    Returns dict(o_full, lse_full, idx [Hkv][k], tau, sigma, o_sparse list);
+    with union (reading R12) idx is [Hkv][G*k] and "heads" replaces tau and
+    sigma.
     """
     p = length - 1
     K[:, p] = kv_new[:, 0]
     V[:, p] = kv_new[:, 1]
     pos = np.array([p])
-    res = full_attn_select_rows(q_full[None], K, V, pos, k, window, scale, score, blocks)
+    res = full_attn_select_rows(q_full[None], K, V, pos, k, window, scale, score, blocks, union)
     outs = []
     for qs in q_sparse:
         o, _ = sparse_attention_rows(qs[None], K, V, res["idx"], pos, window, scale)
         outs.append(o[0])
-    return {"o_full": res["o"][0], "lse_full": res["lse"][0], "idx": res["idx"][0],
-            "tau": res["tau"][0], "sigma": res["sigma"][0], "o_sparse": outs}
+    out = {"o_full": res["o"][0], "lse_full": res["lse"][0], "idx": res["idx"][0], "o_sparse": outs}
+    if union:
+        out["heads"] = res["heads"][0]
+    else:
+        out["tau"], out["sigma"] = res["tau"][0], res["sigma"][0]
+    return out
 
 
 def lse_combine(parts):

@@ -544,3 +544,63 @@ def test_block_selection_rows_keep_whole_blocks():
         for b in set(sel // 64):
             assert set(sel[sel // 64 == b]) == set(range(64 * b, min(64 * b + 64, c)))
         assert len(set(sel // 64)) == 2
+
+
+# ---------------------------------------------------------------- union of per-head top-k (reading R12)
+
+def test_head_union_with_one_head_is_token_select():
+    rng = np.random.default_rng(71)
+    q = bf16_exact((1, 128), rng)
+    K = bf16_exact((700, 128), rng)
+    for p, k in [(699, 64), (100, 128), (40, 8)]:
+        got, heads = orc.head_union_select(q, K, p, 16, orc.default_scale(128), k)
+        want, tau = orc.topk_select(orc.selection_scores(q, K, p, 16, orc.default_scale(128)), k)
+        assert np.array_equal(got, want) and heads[0][1] == tau
+
+
+def test_head_union_brute_force():
+    """Plain Python on small rows: each head's candidates ranked by its own
+    float32 logit (desc, index asc), the first k kept, the sets united."""
+    rng = np.random.default_rng(72)
+    G, n, W, k = 4, 90, 8, 12
+    q = np.round(rng.standard_normal((G, 128)), 1)
+    K = np.round(rng.standard_normal((n, 128)), 1)  # coarse values: ties
+    sc = 0.125
+    for p in (n - 1, 50, 15, 7):
+        got, _ = orc.head_union_select(q, K, p, W, sc, k)
+        c = max(0, p - W + 1)
+        union = set()
+        for h in range(G):
+            logit = [sum(sc * q[h, i] * K[j, i] for i in range(128)) for j in range(c)]
+            ranked = sorted(range(c), key=lambda j: (-float(np.float32(logit[j])), j))[:k]
+            union.update(ranked)
+        want = sorted(union)
+        assert list(got[:len(want)]) == want and np.all(got[len(want):] == -1), p
+
+
+def test_head_union_size_bounds_and_identical_heads():
+    rng = np.random.default_rng(73)
+    K = bf16_exact((600, 128), rng)
+    q = bf16_exact((8, 128), rng)
+    got, _ = orc.head_union_select(q, K, 599, 32, orc.default_scale(128), 40)
+    size = int((got >= 0).sum())
+    assert 40 <= size <= 8 * 40
+    # heads that are copies of one head select one set: the union is that set
+    q1 = np.repeat(q[:1], 8, axis=0)
+    same, _ = orc.head_union_select(q1, K, 599, 32, orc.default_scale(128), 40)
+    one, _ = orc.topk_select(orc.selection_scores(q[:1], K, 599, 32, orc.default_scale(128)), 40)
+    assert np.array_equal(same[:40], one) and np.all(same[40:] == -1)
+
+
+def test_head_union_contains_group_max_top_token():
+    """The group-max top-1 token is some head's top-1, so it is in the union."""
+    rng = np.random.default_rng(74)
+    K = bf16_exact((1, 500, 128), rng)
+    V = bf16_exact((1, 500, 128), rng)
+    q = bf16_exact((3, 4, 128), rng)
+    pos = [499, 300, 200]
+    u = orc.full_attn_select_rows(q, K, V, pos, 1, 16, orc.default_scale(128), union=True)
+    t = orc.full_attn_select_rows(q, K, V, pos, 1, 16, orc.default_scale(128))
+    for r in range(3):
+        assert t["idx"][r, 0, 0] in set(u["idx"][r, 0].tolist())
+        assert u["idx"].shape == (3, 1, 4)
