@@ -112,11 +112,19 @@ def prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch):
     ws_prob = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), "cuda:0")
     shape.flags = hs.HS_FLAG_BLOCK_SELECT
     ws_blk = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), "cuda:0")
+    shape.flags = hs.HS_FLAG_HEAD_UNION
+    ws_uni = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), "cuda:0")
+    _, _, idx_u = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, flags=hs.HS_FLAG_HEAD_UNION,
+                                      workspace=ws_uni)
     runs = {
         "prob_score_full_layer": lambda: hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window,
                                                              flags=hs.HS_FLAG_PROB_SCORE, workspace=ws_prob),
         "block_select_full_layer": lambda: hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window,
                                                                flags=hs.HS_FLAG_BLOCK_SELECT, workspace=ws_blk),
+        "head_union_full_layer": lambda: hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window,
+                                                             flags=hs.HS_FLAG_HEAD_UNION, workspace=ws_uni),
+        "head_union_sparse_layer": lambda: hs.sparse_attn_reuse(qs[0], kv, idx_u, top_k=w.top_k, window=w.window,
+                                                               n_kv=w.n_kv, flags=hs.HS_FLAG_HEAD_UNION),
         "fp8_cache_conversion": lambda: hs.kv_to_fp8(kv, n_kv=w.n_kv, out=copy),
         "fp8_sparse_layer": lambda: hs.sparse_attn_reuse(qs[0], kv, idx, top_k=w.top_k, window=w.window,
                                                          n_kv=w.n_kv, kv_fp8=copy),
@@ -135,7 +143,7 @@ def prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch):
         out[name] = {"ms": round(sum(t for n, t in kt.values()) / 3, 3),
                      "kernels_us": {k: round(t / n * 1e3, 1) for k, (n, t) in kt.items()}}
         log(f"[bench] {w.name} {name}: {out[name]}")
-    del copy, ws_prob, ws_blk
+    del copy, ws_prob, ws_blk, ws_uni, idx_u
     return out
 
 
@@ -263,6 +271,23 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
     blk_sel_us = sum(kb[k][1] / kb[k][0] * 1e3 for k in ("block_max", "select_blocks"))
     log(f"[bench] {wname}: block-level selection {blk_sel_us:.1f} us (block scores + top blocks)")
     del ws_blk
+    # option: union of per-head top-k (heads' score rows, their top-k, union)
+    shape.flags = hs.HS_FLAG_HEAD_UNION
+    ws_uni = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
+    shape.flags = 0
+    uni_call = lambda: hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
+                                      window=w.window, flags=hs.HS_FLAG_HEAD_UNION, workspace=ws_uni)
+    uni_call()
+    torch.cuda.synchronize()
+    _lib.timing_read()
+    _lib.timing_enable(True)
+    uni_call()
+    torch.cuda.synchronize()
+    _lib.timing_enable(False)
+    ku = _lib.timing_read()
+    uni_sel_us = sum(ku[k][1] / ku[k][0] * 1e3 for k in ("decode_score", "select_decode", "head_union"))
+    log(f"[bench] {wname}: per-head union selection {uni_sel_us:.1f} us (head scores + head top-k + union)")
+    del ws_uni
     # algorithmic bytes
     full_bytes = sum(512.0 * w.Hkv * (L + s + 1) for L in lengths for s in range(steps)) / steps
     sp_rows = sum(min(w.top_k, max(0, L + s + 1 - w.window)) + min(w.window, L + s + 1)
@@ -280,6 +305,7 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
         "fp8_sparse_layer_kernel_us": round(fp8_sparse_us, 2),
         "fp8_append_conversion_us": round(fp8_append_us, 2),
         "block_select_us": round(blk_sel_us, 2),
+        "head_union_select_us": round(uni_sel_us, 2),
         "kernels": {k: {"launches_per_step": n / steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()},
         "sparse_decode_roofline": {"bound": "hbm", "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -16,6 +16,9 @@
  *  [HS2-en]  "HySparse2 Cuts the Prefill Path for Tool-Using Agents", section
  *            "Tool Responses Turn Prefill Into the Bottleneck": prefill writes
  *            the KV cache that decoding reuses.
+ *  [SSA-3.3] "Simplified Sparse Attention via Gist Tokens", section 3.3
+ *            "Selective Unfolding and Hybrid Attention", paragraph "Grouped
+ *            Unfolding for GQA": per-head top-k, united within a KV group.
  *  [SSA-3.6] "Simplified Sparse Attention via Gist Tokens", section 3.6
  *            "Kernel Design": sparse kernels compute exact attention over the
  *            kept keys; split partials merge by the log-sum-exp correction.
@@ -130,6 +133,17 @@ typedef enum {
    combined with HS_FLAG_PROB_SCORE (HS_ERR_UNSUPPORTED). Read by
    hs_full_attn_select and hs_decode_step. */
 #define HS_FLAG_BLOCK_SELECT 8u
+/* Union of per-head top-k sets, the grouped-unfolding rule for GQA
+   ([SSA-3.3] "Grouped Unfolding for GQA"): each query head of a group ranks
+   C(p) by its own scaled logit and keeps its top top_k; the group's row is
+   the union of the G sets, ascending, in a row of G * top_k entries padded
+   with -1. With this flag, idx of hs_full_attn_select and hs_decode_step is
+   [..][Hkv][G * top_k], and hs_sparse_attn_reuse, given the same flag and
+   top_k, reads rows of that length. Prefill runs the layer as G passes of
+   one head per group (outputs and lse unchanged up to rounding order);
+   decode adds one pass over the K rows for the heads' scores. Not combined
+   with HS_FLAG_PROB_SCORE or HS_FLAG_BLOCK_SELECT (HS_ERR_UNSUPPORTED). */
+#define HS_FLAG_HEAD_UNION 16u
 #define HS_FLAG_FP8_KV 4u       /* hs_sparse_attn_reuse reads its keys and
                                    values from the FP8 copy of the cache
                                    made by hs_kv_fp8_convert (kv then points

@@ -26,6 +26,10 @@ Sources (web pages; section names as printed on them):
 [HS2-en]  "HySparse2 Cuts the Prefill Path for Tool-Using Agents", section
           "Tool Responses Turn Prefill Into the Bottleneck": prefill writes
           keys and values to the KV cache, which decoding then reuses.
+[SSA-3.3] "Simplified Sparse Attention via Gist Tokens", section 3.3
+          "Selective Unfolding and Hybrid Attention", paragraph "Grouped
+          Unfolding for GQA": each query head takes its own top-k; a KV
+          group unfolds the union of its heads' choices.
 [SSA-3.6] "Simplified Sparse Attention via Gist Tokens", section 3.6 "Kernel
           Design": sparse kernels compute exact attention over the kept keys
           (only accumulation order may differ); softmax normalises over the

@@ -94,6 +94,30 @@ def check_block_row(got: np.ndarray, ref: np.ndarray, sigma: np.ndarray, tau: fl
     return len(diff)
 
 
+def check_union_row(got: np.ndarray, ref: np.ndarray, heads, p: int, window: int, k: int, where=""):
+    """Union of per-head top-k row (G*k entries): ascending, duplicate-free,
+    inside C(p), -1 padded. A token only the GPU took must be a near-tie of
+    some head (score within 1e-3 of that head's k-th score or above it); a
+    token only the oracle took must not be a clear pick (above k-th + 1e-3)
+    of any head."""
+    G = len(heads)
+    ncand = max(0, p - window + 1)
+    got = np.asarray(got, np.int64)
+    assert got.shape == (G * k,), where
+    v = got[got >= 0]
+    n = len(v)
+    assert np.all(got[:n] >= 0) and np.all(got[n:] == -1), f"{where}: padding not at the end"
+    assert min(k, ncand) <= n <= min(G * k, ncand), f"{where}: {n} entries"
+    if n:
+        assert np.all(np.diff(v) > 0) and v[-1] <= p - window, f"{where}: not ascending or outside C(p)"
+    A, R = set(v.tolist()), set(int(x) for x in ref if x >= 0)
+    for j in A - R:
+        assert any(s[j] >= t - TIE_BAND for s, t in heads), f"{where}: token {j} is no head's pick"
+    for j in R - A:
+        assert not any(s[j] > t + TIE_BAND for s, t in heads), f"{where}: token {j} missing"
+    return len(A ^ R)
+
+
 def cache_np(kv: torch.Tensor, b: int, n: int):
     """K, V of sequence b as float64 numpy [Hkv][n][d] (exact widening of bf16;
     float64 so that the oracle takes contiguous ranges as views)."""
@@ -119,7 +143,7 @@ def sample_rows(n_q: int, n_kv: int, top_k: int, window: int, spans=(), evenly=8
 
 
 def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_sparse=(), o_sparse=(), scale=None,
-                  score="logit", blocks=False):
+                  score="logit", blocks=False, union=False):
     """Checks one prefill call (and its sparse layers) on the given query rows;
     score names the oracle's selection score ("logit" or "prob"), blocks asks
     for block-level selection."""
@@ -136,13 +160,17 @@ def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_spa
     for b in range(B):
         K, V = cache_np(kv, b, n_kv)
         qb = f32(q_full[b])[rows]
-        res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale, score, blocks=blocks)
+        res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale, score, blocks=blocks, union=union)
         check_row = check_block_row if blocks else check_idx_row
         full_stats.add(o_np[b, rows], res["o"])
         if lse_np is not None:
             lse_stats.add(lse_np[b][:, rows].T, res["lse"])
         for r, t in enumerate(rows):
             for g in range(K.shape[0]):
+                if union:
+                    swaps += check_union_row(idx_np[b, t, g], res["idx"][r, g], res["heads"][r][g], int(pos[r]),
+                                             window, top_k, where=f"b{b} t{t} g{g}")
+                    continue
                 swaps += check_row(idx_np[b, t, g], res["idx"][r, g], res["sigma"][r][g], res["tau"][r, g],
                                        int(pos[r]), window, top_k, where=f"b{b} t{t} g{g}")
         gidx = idx_np[b][rows]

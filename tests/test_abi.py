@@ -70,7 +70,8 @@ def base_shape(**kw):
     (dict(window=0), _lib.HS_ERR_INVALID_ARG),
     (dict(n_q=65), _lib.HS_ERR_INVALID_ARG),
     (dict(n_kv=65), _lib.HS_ERR_INVALID_ARG),
-    (dict(flags=16), _lib.HS_ERR_INVALID_ARG),
+    (dict(flags=32), _lib.HS_ERR_INVALID_ARG),
+    (dict(flags=_lib.HS_FLAG_HEAD_UNION | _lib.HS_FLAG_PROB_SCORE), _lib.HS_ERR_UNSUPPORTED),
     (dict(flags=_lib.HS_FLAG_BLOCK_SELECT), _lib.HS_ERR_INVALID_ARG),  # top_k 16 is not whole blocks
     (dict(flags=_lib.HS_FLAG_BLOCK_SELECT | _lib.HS_FLAG_PROB_SCORE, top_k=64), _lib.HS_ERR_UNSUPPORTED),
     (dict(kv_strides=(0, 0, 12, 0)), _lib.HS_ERR_INVALID_ARG),
@@ -99,6 +100,21 @@ def test_null_pointers_and_workspace(lib):
     assert lib.hs_decode_step(ctypes.byref(sd), fake, fake, fake, fake, 65, fake, None, fake, fake, 1 << 30, None) == _lib.HS_ERR_INVALID_ARG
     sp = base_shape(n_q=2)
     assert lib.hs_sparse_attn_reuse(ctypes.byref(sp), fake, fake, fake, fake, fake, fake, 1 << 30, None) == _lib.HS_ERR_INVALID_ARG
+
+
+def test_head_union_index_rows(lib):
+    """Under the per-head union the sparse layers read rows of G * top_k
+    entries: their decode workspace follows that row length."""
+    s = base_shape(batch=1, n_q=1, n_kv=0, kv_capacity=1 << 17, q_heads=8, kv_heads=1, top_k=512, window=64)
+    su = base_shape(batch=1, n_q=1, n_kv=0, kv_capacity=1 << 17, q_heads=8, kv_heads=1, top_k=512, window=64,
+                    flags=_lib.HS_FLAG_HEAD_UNION)
+    wide = base_shape(batch=1, n_q=1, n_kv=0, kv_capacity=1 << 17, q_heads=8, kv_heads=1, top_k=4096, window=64)
+    a = _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, su, 1 << 17)
+    assert a == _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, wide, 1 << 17)
+    assert a > _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, s, 1 << 17)
+    # prefill: the G one-head passes need the heads' lists on top of a pass's workspace
+    p = base_shape(n_q=64, n_kv=64, q_heads=8, kv_heads=2, top_k=16, window=8, flags=_lib.HS_FLAG_HEAD_UNION)
+    assert _lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, p) >= 4 * 64 * 2 * 16 * 4
 
 
 def test_workspace_sizes(lib):

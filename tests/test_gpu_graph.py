@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("option", ["default", "prob_score", "fp8_cache", "block_select"])
+@pytest.mark.parametrize("option", ["default", "prob_score", "fp8_cache", "block_select", "head_union"])
 def test_decode_graph_matches_eager(option):
     lengths = [4093, 700, 64, 2500, 1, 3000]  # the longest crosses 4096 -> a second bucket
     B, Hq, Hkv, k, W, nsl, steps = len(lengths), 32, 4, 256, 64, 2, 6
@@ -22,7 +22,8 @@ def test_decode_graph_matches_eager(option):
     for b, L in enumerate(lengths):
         kv_a[b, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 700 + b, DEV)
     kv_b = kv_a.clone()
-    flags = {"prob_score": hs.HS_FLAG_PROB_SCORE, "block_select": hs.HS_FLAG_BLOCK_SELECT}.get(option, 0)
+    flags = {"prob_score": hs.HS_FLAG_PROB_SCORE, "block_select": hs.HS_FLAG_BLOCK_SELECT,
+             "head_union": hs.HS_FLAG_HEAD_UNION}.get(option, 0)
     f8_a = hs.kv_to_fp8(kv_a, n_kv=cap) if option == "fp8_cache" else None
     f8_b = f8_a.clone() if f8_a is not None else None
     g = hs.DecodeStepGraph(kv_b, batch=B, q_heads=Hq, sparse_layers=nsl, top_k=k, window=W, flags=flags,
@@ -44,7 +45,8 @@ def test_decode_graph_matches_eager(option):
         o, lse, idx = hs.decode_step(q, kv_new, kv_a, seq, g.bound, top_k=k, window=W, flags=flags)
         if f8_a is not None:
             hs.kv_to_fp8(kv_a, seq_lens=seq, out=f8_a)
-        osp = [hs.sparse_attn_reuse(x, kv_a, idx, top_k=k, window=W, seq_lens=seq, kv_fp8=f8_a) for x in qs]
+        osp = [hs.sparse_attn_reuse(x, kv_a, idx, top_k=k, window=W, seq_lens=seq, kv_fp8=f8_a, flags=flags)
+               for x in qs]
         torch.cuda.synchronize()
         assert torch.equal(idx_g, idx), s
         assert torch.equal(o_g, o), s

@@ -18,18 +18,19 @@ def run_prefill_workload(name, evenly=8, flags=0):
     w = synth.WORKLOADS[name]
     score = "prob" if flags & hs.HS_FLAG_PROB_SCORE else "logit"
     blocks = bool(flags & hs.HS_FLAG_BLOCK_SELECT)
+    union = bool(flags & hs.HS_FLAG_HEAD_UNION)
     print(f"[case] workload {name}: B={w.B} n_q={w.n_q} n_kv={w.n_kv} k={w.top_k} W={w.window} score={score} blocks={blocks}",
           flush=True)
     case = synth.make_prefill_case(w, DEV, kv_capacity=w.n_kv + w.decode_steps)
     q, kv, qs = case["q_full"], case["kv"], case["q_sparse"]
     o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, flags=flags)
-    osp = [hs.sparse_attn_reuse(x, kv, idx, top_k=w.top_k, window=w.window, n_kv=w.n_kv) for x in qs]
+    osp = [hs.sparse_attn_reuse(x, kv, idx, top_k=w.top_k, window=w.window, n_kv=w.n_kv, flags=flags) for x in qs]
     torch.cuda.synchronize()
     pos, spans = case["needles"]
     rows = sample_rows(w.n_q, w.n_kv, w.top_k, w.window, spans, evenly)
     print(f"[case] checking rows {rows}", flush=True)
     res = check_prefill(q, kv, w.n_kv, w.top_k, w.window, o, lse, idx, rows=rows, q_sparse=qs, o_sparse=osp,
-                        score=score, blocks=blocks)
+                        score=score, blocks=blocks, union=union)
     print(f"[case] {name}: near-tie swaps {res['swaps']}, full max-abs {res['full'].max_abs:.2e} "
           f"mean {res['full'].mean_abs:.2e}, sparse max-abs {res['sparse'].max_abs:.2e}", flush=True)
     # needles: the planted keys should mostly be selected by their span rows
@@ -59,6 +60,12 @@ def test_prefill32k_full_size_block_select():
     """Block-level selection at full size: block scores from the attention
     pass, then the top top_k/64 blocks per row."""
     run_prefill_workload("prefill32k", evenly=4, flags=hs.HS_FLAG_BLOCK_SELECT)
+
+
+def test_prefill32k_full_size_head_union():
+    """Union of per-head top-k at full size: eight one-head passes, the
+    union rows of 8 * 2048 entries, the sparse layers over them."""
+    run_prefill_workload("prefill32k", evenly=3, flags=hs.HS_FLAG_HEAD_UNION)
 
 
 def test_chunk128k_full_size():

@@ -18,10 +18,11 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import HS_FLAG_BLOCK_SELECT, HS_FLAG_EXACT_RESCAN, HS_FLAG_FP8_KV, HS_FLAG_PROB_SCORE, HsError, HsShape  # noqa: F401
+from ._lib import (HS_FLAG_BLOCK_SELECT, HS_FLAG_EXACT_RESCAN, HS_FLAG_FP8_KV, HS_FLAG_HEAD_UNION,  # noqa: F401
+                   HS_FLAG_PROB_SCORE, HsError, HsShape)
 
 __all__ = ["full_attn_select", "sparse_attn_reuse", "decode_step", "make_shape", "HsError",
-           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "HS_FLAG_BLOCK_SELECT", "kv_to_fp8", "version"]
+           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "HS_FLAG_BLOCK_SELECT", "HS_FLAG_HEAD_UNION", "kv_to_fp8", "version"]
 
 
 def version() -> int:
@@ -57,13 +58,18 @@ def _kv_dims(kv, kv_strides):
     raise ValueError("explicit kv_strides need kv_heads and kv_capacity arguments")
 
 
+def _idx_row(flags, top_k, q_heads, kv_heads):
+    """Entries per index row: G * top_k under the per-head union."""
+    return top_k * (q_heads // kv_heads) if flags & _lib.HS_FLAG_HEAD_UNION else top_k
+
+
 def full_attn_select(q, kv, n_kv, *, top_k, window, scale=0.0, with_lse=True, flags=0,
                      kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None):
     """Full-attention layer with token selection over a prefill chunk.
 
     q: bf16 [B][n_q][Hq][128] (the chunk's rows sit at the end of the n_kv-token
     cache). Returns (o bf16 [B][n_q][Hq][128], lse fp32 [B][Hq][n_q] or None,
-    idx int32 [B][n_q][Hkv][top_k]).
+    idx int32 [B][n_q][Hkv][top_k], or [..][G*top_k] with HS_FLAG_HEAD_UNION).
     """
     _check_bf16("q", q, 4)
     B, n_q, Hq, d = q.shape
@@ -74,7 +80,7 @@ def full_attn_select(q, kv, n_kv, *, top_k, window, scale=0.0, with_lse=True, fl
     dev = q.device
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=dev) if with_lse else None
-    idx = torch.empty((B, n_q, kv_heads, top_k), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, n_q, kv_heads, _idx_row(flags, top_k, Hq, kv_heads)), dtype=torch.int32, device=dev)
     nbytes = _lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape)
     ws = workspace if workspace is not None else _lib.alloc_workspace(nbytes, dev)
     lib = _lib.load()
@@ -85,13 +91,15 @@ def full_attn_select(q, kv, n_kv, *, top_k, window, scale=0.0, with_lse=True, fl
 
 
 def sparse_attn_reuse(q, kv, idx, *, top_k, window, n_kv=None, seq_lens=None, scale=0.0,
-                      kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None, kv_fp8=None):
+                      kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None, kv_fp8=None, flags=0):
     """Sparse layer reusing the full layer's cache and selection.
 
     Prefill: q bf16 [B][n_q][Hq][128], idx [B][n_q][Hkv][k], n_kv given.
     Decode:  q bf16 [B][Hq][128], idx [B][Hkv][k], seq_lens int32 [B] on device.
     kv_fp8: the cache's FP8 copy from kv_to_fp8 to gather from instead of kv
-    (kv then only gives the shape). Returns o with q's shape.
+    (kv then only gives the shape). flags: HS_FLAG_HEAD_UNION when idx came
+    from a full layer with that flag (rows of G*k entries). Returns o with
+    q's shape.
     """
     decode = seq_lens is not None
     _check_bf16("q", q, 3 if decode else 4)
@@ -108,7 +116,8 @@ def sparse_attn_reuse(q, kv, idx, *, top_k, window, n_kv=None, seq_lens=None, sc
         raise TypeError("seq_lens must be an int32 device tensor")
     shape = make_shape(batch=B, n_q=n_q, n_kv=0 if decode else n_kv, kv_capacity=kv_capacity, q_heads=Hq,
                        kv_heads=kv_heads, top_k=top_k, window=window, scale=scale, kv_strides=kv_strides,
-                       flags=_lib.HS_FLAG_FP8_KV if kv_fp8 is not None else 0, head_dim=d)
+                       flags=(flags & _lib.HS_FLAG_HEAD_UNION) | (_lib.HS_FLAG_FP8_KV if kv_fp8 is not None else 0),
+                       head_dim=d)
     dev = q.device
     o = torch.empty_like(q)
     nbytes = _lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, shape, 1 if decode else 0)
@@ -126,7 +135,7 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
 
     q bf16 [B][Hq][128]; kv_new bf16 [B][Hkv][2][128]; seq_lens int32 [B] (device,
     including the new token). Returns (o [B][Hq][128], lse [B][Hq] or None,
-    idx int32 [B][Hkv][top_k]).
+    idx int32 [B][Hkv][top_k], or [B][Hkv][G*top_k] with HS_FLAG_HEAD_UNION).
     """
     _check_bf16("q", q, 3)
     _check_bf16("kv_new", kv_new, 4)
@@ -140,7 +149,7 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
     dev = q.device
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if with_lse else None
-    idx = torch.empty((B, kv_heads, top_k), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, kv_heads, _idx_row(flags, top_k, Hq, kv_heads)), dtype=torch.int32, device=dev)
     nbytes = _lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max_seq_len)
     ws = workspace if workspace is not None else _lib.alloc_workspace(nbytes, dev)
     lib = _lib.load()

@@ -22,6 +22,7 @@ HS_FLAG_EXACT_RESCAN = 1
 HS_FLAG_PROB_SCORE = 2
 HS_FLAG_FP8_KV = 4
 HS_FLAG_BLOCK_SELECT = 8
+HS_FLAG_HEAD_UNION = 16
 
 EXPORTED = ("hs_workspace_size", "hs_full_attn_select", "hs_sparse_attn_reuse", "hs_decode_step",
             "hs_kv_fp8_size", "hs_kv_fp8_convert",

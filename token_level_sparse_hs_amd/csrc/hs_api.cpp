@@ -82,8 +82,11 @@ hs_status validate_common(const hs_shape* s, Layout* lay) {
   if (s->window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", s->window);
   if (s->kv_capacity < 1) return fail(HS_ERR_INVALID_ARG, "kv_capacity must be >= 1");
   if (!(s->scale >= 0.f) || std::isinf(s->scale)) return fail(HS_ERR_INVALID_ARG, "scale must be finite and >= 0");
-  if ((s->flags & ~(HS_FLAG_EXACT_RESCAN | HS_FLAG_PROB_SCORE | HS_FLAG_FP8_KV | HS_FLAG_BLOCK_SELECT)) != 0)
+  if ((s->flags & ~(HS_FLAG_EXACT_RESCAN | HS_FLAG_PROB_SCORE | HS_FLAG_FP8_KV | HS_FLAG_BLOCK_SELECT |
+                    HS_FLAG_HEAD_UNION)) != 0)
     return fail(HS_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  if ((s->flags & HS_FLAG_HEAD_UNION) && (s->flags & (HS_FLAG_PROB_SCORE | HS_FLAG_BLOCK_SELECT)))
+    return fail(HS_ERR_UNSUPPORTED, "the per-head union uses token-level logit scores");
   if ((s->flags & HS_FLAG_BLOCK_SELECT) && s->top_k % 64 != 0)
     return fail(HS_ERR_INVALID_ARG, "block-level selection needs top_k %% 64 == 0 (got %d)", s->top_k);
   if ((s->flags & HS_FLAG_BLOCK_SELECT) && (s->flags & HS_FLAG_PROB_SCORE))
@@ -115,6 +118,26 @@ hs_status validate_common(const hs_shape* s, Layout* lay) {
 
 float eff_scale(const hs_shape* s) { return s->scale == 0.f ? 1.0f / std::sqrt((float)s->head_dim) : s->scale; }
 
+bool head_union(const hs_shape* s) { return (s->flags & HS_FLAG_HEAD_UNION) && s->top_k > 0; }
+
+// The sparse layers see an index row of G * top_k entries under the per-head
+// union: their shape is the caller's with that row length.
+hs_shape sparse_shape(const hs_shape* s) {
+  hs_shape t = *s;
+  if (head_union(s)) t.top_k = s->top_k * (s->q_heads / s->kv_heads);
+  t.flags &= ~HS_FLAG_HEAD_UNION;
+  return t;
+}
+
+// Prefill under the per-head union: the layer runs as G passes of a one-head-
+// per-group layer (query heads g*G + r for pass r), whose shape this is.
+hs_shape union_pass_shape(const hs_shape* s) {
+  hs_shape t = *s;
+  t.q_heads = s->kv_heads;
+  t.flags &= ~HS_FLAG_HEAD_UNION;
+  return t;
+}
+
 hs::KvView kv_view(const void* kv, const Layout& l) {
   return hs::KvView{static_cast<const uint16_t*>(kv), l.sb, l.sh, (int32_t)l.st, (int32_t)l.voff};
 }
@@ -133,6 +156,29 @@ struct PrefillPlan {
   bool block = false; // block-level selection: block scores at off_blk
   int blk_stride = 0;
 };
+
+struct UnionPlan {
+  size_t inner = 0, off_q = 0, off_o = 0, off_lse = 0, off_lists = 0, total = 0;
+};
+PrefillPlan plan_prefill(const hs_shape* s);
+UnionPlan plan_union_prefill(const hs_shape* s) {
+  UnionPlan u;
+  const hs_shape si = union_pass_shape(s);
+  const int G = s->q_heads / s->kv_heads;
+  const int64_t rows = (int64_t)s->batch * s->n_q * s->kv_heads;
+  size_t o = align_up(plan_prefill(&si).total);
+  u.inner = o;
+  u.off_q = o;
+  o = align_up(o + (size_t)rows * 128 * 2);
+  u.off_o = o;
+  o = align_up(o + (size_t)rows * 128 * 2);
+  u.off_lse = o;
+  o = align_up(o + (size_t)rows * 4);
+  u.off_lists = o;
+  o = align_up(o + (size_t)G * rows * s->top_k * 4);
+  u.total = o;
+  return u;
+}
 
 PrefillPlan plan_prefill(const hs_shape* s) {
   PrefillPlan p;
@@ -181,9 +227,10 @@ struct DecodePlan {
   int sel_slices = 0;     // sliced selection (0: one block per row)
   bool prob = false;      // probability score: score pass after the full layer
   bool block = false;     // block-level selection from the score rows
+  bool head_union = false; // per-head score rows and lists, then their union
   int blk_stride = 0;
   size_t off_sigma = 0, off_part = 0, off_theta = 0, off_segcnt = 0, off_segkey = 0, off_segidx = 0, off_lse = 0,
-         off_blk = 0, total = 0;
+         off_blk = 0, off_hidx = 0, total = 0;
 };
 
 // Splits a per-(b, g) key stream of up to `nkeys` keys so that the grid holds
@@ -217,9 +264,12 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   p.split_len = (int)len;
   p.splits = (int)((max_seq_len + len - 1) / len);
   p.sigma_stride = round_up(max_seq_len, 64);
+  // score rows: one per (b, g), or one per query head under the per-head union
+  p.head_union = head_union(s);
+  const int64_t sel_rows = p.head_union ? (int64_t)s->batch * s->q_heads : bg;
   size_t o = 0;
   p.off_sigma = o;
-  o = align_up(o + (s->top_k > 0 ? (size_t)bg * p.sigma_stride * 4 : 0));
+  o = align_up(o + (s->top_k > 0 ? (size_t)sel_rows * p.sigma_stride * 4 : 0));
   p.off_part = o;
   o = align_up(o + (size_t)bg * p.splits * G * (128 + 2) * 4);
   // Rows longer than one block's registers hold are selected in slices spread
@@ -230,14 +280,15 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   // row, are selected in slices instead.
   const int64_t max_cand = (int64_t)max_seq_len - s->window;
   const double expect = s->top_k + 6.0 * std::sqrt((double)s->top_k * (double)max_cand / 2048.0);
-  if (s->top_k > 0 && !(s->flags & HS_FLAG_BLOCK_SELECT) && max_cand > hs::kSelRegKeys && (bg < kChipSimds / 4 || expect > 0.75 * hs::kSelRegKeys)) {
+  if (s->top_k > 0 && !(s->flags & HS_FLAG_BLOCK_SELECT) && max_cand > hs::kSelRegKeys &&
+      (sel_rows < kChipSimds / 4 || expect > 0.75 * hs::kSelRegKeys)) {
     const int64_t ns = (max_cand + hs::kDecSlice - 1) / hs::kDecSlice;
     if (ns <= hs::kMaxDecSlices) p.sel_slices = (int)ns;
   }
   if (p.sel_slices > 0) {
-    const size_t seg = (size_t)bg * p.sel_slices;
+    const size_t seg = (size_t)sel_rows * p.sel_slices;
     p.off_theta = o;
-    o = align_up(o + (size_t)bg * 4);
+    o = align_up(o + (size_t)sel_rows * 4);
     p.off_segcnt = o;
     o = align_up(o + seg * 4);
     p.off_segkey = o;
@@ -249,6 +300,10 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   if (p.prob) {
     p.off_lse = o;
     o = align_up(o + (size_t)s->batch * s->q_heads * 4);
+  }
+  if (p.head_union) {  // the heads' own top-k lists
+    p.off_hidx = o;
+    o = align_up(o + (size_t)sel_rows * s->top_k * 4);
   }
   p.block = s->top_k > 0 && (s->flags & HS_FLAG_BLOCK_SELECT) != 0;
   if (p.block) {
@@ -407,11 +462,13 @@ hs_status hs_workspace_size(hs_op op, const hs_shape* s, int32_t max_seq_len, si
   switch (op) {
     case HS_OP_FULL_ATTN_SELECT:
       if (s->n_q < 1 || s->n_kv < s->n_q) return fail(HS_ERR_INVALID_ARG, "need 1 <= n_q <= n_kv");
-      *bytes = plan_prefill(s).total;
+      *bytes = head_union(s) ? plan_union_prefill(s).total : plan_prefill(s).total;
       return ok();
-    case HS_OP_SPARSE_ATTN_REUSE:
-      *bytes = max_seq_len > 0 ? plan_decode_sparse(s).total : 0;
+    case HS_OP_SPARSE_ATTN_REUSE: {
+      const hs_shape su = sparse_shape(s);
+      *bytes = max_seq_len > 0 ? plan_decode_sparse(&su).total : 0;
       return ok();
+    }
     case HS_OP_DECODE_STEP:
       if (max_seq_len < 1) return fail(HS_ERR_INVALID_ARG, "max_seq_len must be >= 1");
       *bytes = plan_decode_full(s, max_seq_len).total;
@@ -433,6 +490,45 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
   if (!aligned16(q) || !aligned16(kv) || !aligned16(o)) return fail(HS_ERR_INVALID_ARG, "q, kv and o must be 16-byte aligned");
   if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3)) || (idx && (reinterpret_cast<uintptr_t>(idx) & 3)))
     return fail(HS_ERR_INVALID_ARG, "lse and idx must be 4-byte aligned");
+  if (head_union(s)) {
+    // G passes of the one-head-per-group layer (pass r: query heads g*G + r),
+    // which give those heads' outputs, lse and own top-k lists; then the
+    // union of each group's G lists [SSA-3.3 grouped unfolding].
+    const UnionPlan up = plan_union_prefill(s);
+    if (!ws || ws_bytes < up.total) return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", up.total, ws_bytes);
+    if (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) return fail(HS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    st = check_device();
+    if (st != HS_OK) return st;
+    hipStream_t hst = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    const hs_shape si = union_pass_shape(s);
+    const int G = s->q_heads / s->kv_heads;
+    const int64_t bt = (int64_t)s->batch * s->n_q, rows = bt * s->kv_heads;
+    uint16_t* qr = reinterpret_cast<uint16_t*>(w + up.off_q);
+    uint16_t* orr = reinterpret_cast<uint16_t*>(w + up.off_o);
+    float* lr = lse ? reinterpret_cast<float*>(w + up.off_lse) : nullptr;
+    int32_t* lists = reinterpret_cast<int32_t*>(w + up.off_lists);
+    for (int r = 0; r < G; ++r) {
+      HIP_TRY(timed("head_slice", hst, [&] {
+        return hs::launch_head_slice(static_cast<const uint16_t*>(q), qr, bt, s->kv_heads, G, r, true, hst);
+      }));
+      st = hs_full_attn_select(&si, qr, kv, orr, lr, lists + (size_t)r * rows * s->top_k, w, up.inner, stream);
+      if (st != HS_OK) return st;
+      HIP_TRY(timed("head_slice", hst, [&] {
+        return hs::launch_head_slice(orr, static_cast<uint16_t*>(o), bt, s->kv_heads, G, r, false, hst);
+      }));
+      if (lse)
+        HIP_TRY(timed("lse_scatter", hst, [&] {
+          return hs::launch_lse_scatter(lr, lse, s->batch, s->kv_heads, G, r, s->n_q, hst);
+        }));
+    }
+    hs::UnionParams un{};
+    un.lists = lists; un.row_stride = s->top_k; un.head_stride = rows * s->top_k; un.G = G; un.k = s->top_k;
+    un.B = s->batch; un.n_q = s->n_q; un.n_kv = s->n_kv; un.Hkv = s->kv_heads; un.window = s->window;
+    un.seq_lens = nullptr; un.out = idx;
+    HIP_TRY(timed("head_union", hst, [&] { return hs::launch_head_union(un, rows, hst); }));
+    return ok();
+  }
   const PrefillPlan plan = plan_prefill(s);
   if (plan.total > 0 && (!ws || ws_bytes < plan.total))
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, ws_bytes);
@@ -531,11 +627,13 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
   return ok();
 }
 
-hs_status hs_sparse_attn_reuse(const hs_shape* s, const void* q, const void* kv, const int32_t* idx,
+hs_status hs_sparse_attn_reuse(const hs_shape* s_in, const void* q, const void* kv, const int32_t* idx,
                                const int32_t* seq_lens, void* o, void* ws, size_t ws_bytes, void* stream) {
   Layout lay;
-  hs_status st = validate_common(s, &lay);
+  hs_status st = validate_common(s_in, &lay);
   if (st != HS_OK) return st;
+  const hs_shape su = sparse_shape(s_in);  // index rows of G * top_k entries under the per-head union
+  const hs_shape* s = &su;
   const bool decode = seq_lens != nullptr;
   if (decode) {
     if (s->n_q != 1) return fail(HS_ERR_INVALID_ARG, "decode calls need n_q == 1 (got %d)", s->n_q);
@@ -633,7 +731,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   dp.lse = lse_buf;
   dp.part = reinterpret_cast<float*>(w + plan.off_part);
   float* sigma = s->top_k > 0 ? reinterpret_cast<float*>(w + plan.off_sigma) : nullptr;
-  dp.sigma = plan.prob ? nullptr : sigma;  // the probability score is written by its own pass
+  dp.sigma = plan.prob || plan.head_union ? nullptr : sigma;  // those scores are written by their own pass
   dp.sigma_stride = plan.sigma_stride;
   HIP_TRY(timed("decode_full", hst, [&] { return hs::launch_decode_full(dp, hst); }));
   if (plan.splits > 1) {
@@ -649,6 +747,32 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
     zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window;
     HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
+  }
+  if (plan.head_union) {
+    const int G = s->q_heads / s->kv_heads;
+    hs::DecodeScoreParams zp{};
+    zp.q = dp.q; zp.kv = dp.kv; zp.seq_lens = seq_lens; zp.lse = nullptr;
+    zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
+    zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window;
+    zp.per_head = 1;
+    HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
+    int32_t* hidx = reinterpret_cast<int32_t*>(w + plan.off_hidx);
+    hs::SelectDecodeParams sp{};
+    sp.B = s->batch; sp.Hkv = s->q_heads; sp.top_k = s->top_k; sp.window = s->window;
+    sp.seq_lens = seq_lens; sp.sigma = sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = hidx;
+    sp.nslices = plan.sel_slices;
+    if (plan.sel_slices > 0) {
+      sp.theta_key = reinterpret_cast<uint32_t*>(w + plan.off_theta);
+      sp.seg_count = reinterpret_cast<uint32_t*>(w + plan.off_segcnt);
+      sp.seg_key = reinterpret_cast<uint32_t*>(w + plan.off_segkey);
+      sp.seg_idx = reinterpret_cast<int32_t*>(w + plan.off_segidx);
+    }
+    HIP_TRY(timed("select_decode", hst, [&] { return hs::launch_select_decode(sp, s->batch * s->q_heads, hst); }));
+    hs::UnionParams un{};
+    un.lists = hidx; un.row_stride = (int64_t)G * s->top_k; un.head_stride = s->top_k; un.G = G; un.k = s->top_k;
+    un.B = s->batch; un.n_q = 1; un.Hkv = s->kv_heads; un.window = s->window; un.seq_lens = seq_lens; un.out = idx;
+    HIP_TRY(timed("head_union", hst, [&] { return hs::launch_head_union(un, (int64_t)s->batch * s->kv_heads, hst); }));
+    return ok();
   }
   if (plan.block) {
     hs::BlockMaxParams mp{};

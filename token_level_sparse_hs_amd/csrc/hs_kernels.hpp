@@ -110,8 +110,28 @@ struct DecodeScoreParams {
   float* sigma;       // [B*Hkv][sigma_stride]
   int64_t sigma_stride;
   int max_cand;       // bound on |C(p)| over the batch (grid size)
+  int per_head;       // 1: each head's scaled logit into row b*Hq + h (lse unused)
 };
 hipError_t launch_decode_prob_score(const DecodeScoreParams& p, hipStream_t s);
+
+// Union of per-head top-k lists: output row `row` (a (b, t, g) or (b, g)
+// row) merges lists lists + row*row_stride + r*head_stride, r < G, each k
+// entries ascending and -1 padded, into G*k entries ascending, -1 padded.
+struct UnionParams {
+  const int32_t* lists;
+  int64_t row_stride, head_stride;
+  int G, k;
+  int B, n_q, n_kv, Hkv, window;
+  const int32_t* seq_lens;  // decode rows; null for prefill rows
+  int32_t* out;
+};
+hipError_t launch_head_union(const UnionParams& p, int64_t rows, hipStream_t s);
+// Head slices: dst row (bt, g) <- src row (bt, g*G + r) (gather) or dst row
+// (bt, g*G + r) <- src row (bt, g) (scatter), 128 bf16 each; lse scatter:
+// dst [B][Hkv*G][n] row (b, g*G + r) <- src [B][Hkv][n] row (b, g).
+hipError_t launch_head_slice(const uint16_t* src, uint16_t* dst, int64_t bt, int Hkv, int G, int r, bool gather,
+                             hipStream_t s);
+hipError_t launch_lse_scatter(const float* src, float* dst, int B, int Hkv, int G, int r, int n, hipStream_t s);
 
 // Block-level selection: the top top_k/64 blocks of each row by block score
 // (ties: lower block), expanded to their candidate tokens.

@@ -947,7 +947,7 @@ __global__ __launch_bounds__(256) void decode_prob_score_kernel(DecodeScoreParam
   const uint16_t* qrow = P.q + ((int64_t)b * P.Hq + g * G + (col < G ? col : 0)) * kHeadDim;
 #pragma unroll
   for (int s = 0; s < 4; ++s) qb[s] = as_bf16x8(col < G ? ld16(qrow + 32 * s + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
-  const float lse_col = col < G ? P.lse[(int64_t)b * P.Hq + g * G + col] : 0.f;
+  const float lse_col = col < G && !P.per_head ? P.lse[(int64_t)b * P.Hq + g * G + col] : 0.f;
   const uint16_t* slab = P.kv.slab(b, g);
   float* srow = P.sigma + (int64_t)row * P.sigma_stride;
   const int jend = imin(ncand, j0 + kDecScoreWaveKeys);
@@ -969,10 +969,24 @@ __global__ __launch_bounds__(256) void decode_prob_score_kernel(DecodeScoreParam
       for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(kw[ch][s]), qb[s], acc);
       mfma_settle<kSettle16>(acc);
       // lane (kg, col) holds keys 4kg + i of the chunk for head col
+      const int jk = c0 + 16 * ch + 4 * kg;
+      if (P.per_head) {  // each head's own scaled logit, its own row
+        if (col < G) {
+          float* hrow = P.sigma + ((int64_t)b * P.Hq + g * G + col) * P.sigma_stride;
+          if (jk + 3 < ncand) {
+            *reinterpret_cast<f32x4*>(hrow + jk) =
+                f32x4{acc[0] * P.scale, acc[1] * P.scale, acc[2] * P.scale, acc[3] * P.scale};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (jk + i < ncand) hrow[jk + i] = acc[i] * P.scale;
+          }
+        }
+        continue;
+      }
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = group_max<G>(col < G ? fmaf(acc[i], P.scale, -lse_col) : kNegInf);
-      const int jk = c0 + 16 * ch + 4 * kg;
       if (col == 0) {
         if (jk + 3 < ncand) {
           *reinterpret_cast<f32x4*>(srow + jk) = f32x4{v[0], v[1], v[2], v[3]};
@@ -1131,6 +1145,98 @@ __global__ __launch_bounds__(256) void block_max_kernel(BlockMaxParams P) {
     const int blk = blk0 + 4 * u + lane / 16;
     if ((lane & 15) == 0 && blk * 64 < ncand) P.blk_score[(int64_t)row * P.blk_stride + blk] = v;
   }
+}
+
+// Union of the G heads' top-k lists of one row: a bitmap over a window of
+// kUnionWords * 32 token positions in LDS takes every listed token of the
+// window (LDS atomic or), then the set bits are emitted in ascending order
+// (each thread scans a contiguous run of words at its exclusive prefix of the
+// bit counts); windows follow one another up to |C(p)|.
+constexpr int kUnionWords = 8192;
+__global__ __launch_bounds__(kSelThreads) void head_union_kernel(UnionParams P) {
+  __shared__ uint32_t bits[kUnionWords];
+  __shared__ SelShared sh;
+  const int64_t row = blockIdx.x;
+  int p;
+  if (P.seq_lens) {
+    p = P.seq_lens[row / P.Hkv] - 1;
+  } else {
+    p = P.n_kv - P.n_q + (int)((row / P.Hkv) % P.n_q);
+  }
+  const int ncand = imax(0, p - P.window + 1);
+  const int width = P.G * P.k;
+  int32_t* out = P.out + row * width;
+  const int tid = threadIdx.x;
+  int emitted = 0;
+  for (int w0 = 0; w0 < ncand; w0 += 32 * kUnionWords) {
+    const int nw = imin(kUnionWords, (ncand - w0 + 31) / 32);
+    const int wend = imin(ncand, w0 + 32 * kUnionWords);
+    for (int i = tid; i < nw; i += kSelThreads) bits[i] = 0u;
+    __syncthreads();
+    for (int r = 0; r < P.G; ++r) {
+      const int32_t* L = P.lists + row * P.row_stride + (int64_t)r * P.head_stride;
+      for (int i = tid; i < P.k; i += kSelThreads) {
+        const int x = L[i];
+        if (x >= w0 && x < wend) atomicOr(&bits[(x - w0) >> 5], 1u << ((x - w0) & 31));
+      }
+    }
+    __syncthreads();
+    const int per = (nw + kSelThreads - 1) / kSelThreads;
+    const int wb = imin(nw, tid * per), we = imin(nw, wb + per);
+    uint32_t cnt = 0;
+    for (int i = wb; i < we; ++i) cnt += (uint32_t)__popc(bits[i]);
+    uint32_t total;
+    int pos = emitted + (int)block_scan_total(sh, cnt, &total);
+    for (int i = wb; i < we; ++i) {
+      uint32_t m = bits[i];
+      while (m) {
+        out[pos++] = w0 + 32 * i + __builtin_ctz(m);
+        m &= m - 1u;
+      }
+    }
+    emitted += (int)total;
+    __syncthreads();
+  }
+  for (int i = emitted + tid; i < width; i += kSelThreads) out[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void head_slice_kernel(const uint16_t* src, uint16_t* dst, int64_t bt, int Hkv,
+                                                         int G, int r, int gather) {
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (bt, g) row
+  if (i >= bt * Hkv) return;
+  const int64_t t = i / Hkv;
+  const int g = (int)(i % Hkv), c = threadIdx.x & 15;
+  const int64_t narrow = i, wide = t * Hkv * G + (int64_t)g * G + r;
+  const int64_t s_row = gather ? wide : narrow, d_row = gather ? narrow : wide;
+  *reinterpret_cast<u32x4*>(dst + d_row * kHeadDim + 8 * c) =
+      *reinterpret_cast<const u32x4*>(src + s_row * kHeadDim + 8 * c);
+}
+
+__global__ __launch_bounds__(256) void lse_scatter_kernel(const float* src, float* dst, int B, int Hkv, int G, int r,
+                                                          int n) {
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  dst[((int64_t)b * Hkv * G + (int64_t)g * G + r) * n + t] = src[(int64_t)bg * n + t];
+}
+
+hipError_t launch_head_union(const UnionParams& p, int64_t rows, hipStream_t s) {
+  head_union_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_slice(const uint16_t* src, uint16_t* dst, int64_t bt, int Hkv, int G, int r, bool gather,
+                             hipStream_t s) {
+  const int64_t rows = bt * Hkv;
+  head_slice_kernel<<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s>>>(src, dst, bt, Hkv, G, r, gather ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_scatter(const float* src, float* dst, int B, int Hkv, int G, int r, int n, hipStream_t s) {
+  lse_scatter_kernel<<<dim3((unsigned)((n + 255) / 256), (unsigned)(B * Hkv)), dim3(256), 0, s>>>(src, dst, B, Hkv, G,
+                                                                                                  r, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_select_blocks(const BlockSelectParams& p, int64_t rows, hipStream_t s) {

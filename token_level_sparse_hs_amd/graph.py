@@ -87,7 +87,8 @@ class DecodeStepGraph:
             if self.kv_fp8 is not None:
                 kv_to_fp8(self.kv, seq_lens=self.seq_lens, out=self.kv_fp8)
             o_sp = [sparse_attn_reuse(x, self.kv, idx, top_k=self.top_k, window=self.window, scale=self.scale,
-                                      seq_lens=self.seq_lens, workspace=self.ws_sparse, kv_fp8=self.kv_fp8)
+                                      seq_lens=self.seq_lens, workspace=self.ws_sparse, kv_fp8=self.kv_fp8,
+                                      flags=self.flags)
                     for x in self.q_sparse]
         self.graph, self.ws_full, self.bound = g, ws_full, bound
         self.o, self.lse, self.idx, self.o_sparse = o, lse, idx, o_sp
