@@ -10,6 +10,7 @@ import oracle as orc
 import token_level_sparse_hs_amd as hs
 from token_level_sparse_hs_amd import synth
 from parity import OutStats, check_prefill, check_union_row, f32
+from test_gpu_fp8 import split_copy
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -91,3 +92,44 @@ def test_union_widens_the_selection():
     torch.cuda.synchronize()
     counts = (iu >= 0).sum(-1).cpu().numpy()
     assert counts.min() > k and counts.max() <= 8 * k
+
+
+def test_union_prefill_exact_rescan():
+    """The one-head passes take the flag through (forced exact rescan)."""
+    print("[case] union prefill exact rescan", flush=True)
+    n_kv, n_q, Hq, Hkv, k, W = 500, 150, 8, 2, 48, 16
+    kv = synth.randn_bf16((1, Hkv, n_kv, 2, 128), 3600, DEV)
+    q = synth.randn_bf16((1, n_q, Hq, 128), 3601, DEV)
+    o, lse, idx = hs.full_attn_select(q, kv, n_kv, top_k=k, window=W, flags=UNI | hs.HS_FLAG_EXACT_RESCAN)
+    torch.cuda.synchronize()
+    check_prefill(q, kv, n_kv, k, W, o, lse, idx, union=True)
+
+
+def test_union_decode_sparse_from_fp8_copy():
+    """Sparse decode layers over union rows (8 * k entries) gathering from
+    the FP8 copy, against the oracle on the dequantised copy."""
+    lengths = [700, 5000]
+    B, Hq, Hkv, k, W = len(lengths), 32, 4, 64, 32
+    print(f"[case] union decode + fp8 sparse lengths={lengths}", flush=True)
+    cap = max(lengths) + 1
+    kv = torch.zeros((B, Hkv, cap, 2, 128), dtype=torch.bfloat16, device=DEV)
+    for b, L in enumerate(lengths):
+        kv[b, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 3700 + b, DEV)
+    seq = torch.tensor([L + 1 for L in lengths], dtype=torch.int32, device=DEV)
+    q = synth.randn_bf16((B, Hq, 128), 3710, DEV)
+    qs = synth.randn_bf16((B, Hq, 128), 3711, DEV)
+    kv_new = synth.randn_bf16((B, Hkv, 2, 128), 3712, DEV)
+    _, _, idx = hs.decode_step(q, kv_new, kv, seq, cap, top_k=k, window=W, flags=UNI)
+    f8 = hs.kv_to_fp8(kv, n_kv=cap)
+    o8 = hs.sparse_attn_reuse(qs, kv, idx, top_k=k, window=W, seq_lens=seq, flags=UNI, kv_fp8=f8)
+    torch.cuda.synchronize()
+    codes, scales = split_copy(f8, B, Hkv, cap)
+    deq = codes.view(torch.float8_e4m3fn).double().cpu().numpy() * scales.double().cpu().numpy()[:, :, None, :, None]
+    idx_np = idx.cpu().numpy()
+    assert idx_np.shape[-1] == 8 * k
+    stats = OutStats()
+    for b, L in enumerate(lengths):
+        ref, _ = orc.sparse_attention_rows(f32(qs[b])[None], deq[b, :, :, 0], deq[b, :, :, 1], idx_np[b][None],
+                                           np.array([L]), W, orc.default_scale(128))
+        stats.add(f32(o8[b]), ref[0])
+    stats.check("union fp8 sparse decode o")
