@@ -36,7 +36,7 @@ L1_FILL_GBS = 256 * 64 * 2.4  # 256 CUs x 64 B/clk x 2.4 GHz: vector-memory fill
 # Bytes per launch past L2 from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
 # a calibration copy's reading (bench.py --traffic-probe); taken for the
 # current kernels and refreshed by hand whenever they change.
-TRAFFIC = {"sparse_prefill": 1.497e10, "prefill_attn": 6.406e9, "decode_full": 2.064e10, "sparse_decode": 3.391e8}
+TRAFFIC = {"sparse_prefill": 1.327e10, "prefill_attn": 6.403e9, "decode_full": 2.064e10, "sparse_decode": 3.391e8}
 
 
 def log(*a):
