@@ -564,7 +564,10 @@ __global__ __launch_bounds__(256, 3) void select_prefill_wave_kernel(SelectParam
   }
   uint32_t key[kWaveE];
 #pragma unroll
-  for (int e = 0; e < kWaveE; ++e) key[e] = buf_ld4(rs_s, 4u * (uint32_t)lane + 256u * (uint32_t)e);
+  for (int e = 0; e < kWaveE; ++e) {  // slots past the count: no load issued (wave-uniform branch)
+    key[e] = 0u;
+    if (64 * e < cnt) key[e] = buf_ld4(rs_s, 4u * (uint32_t)lane + 256u * (uint32_t)e);
+  }
 #pragma unroll
   for (int e = 0; e < kWaveE; ++e) key[e] = 64 * e + lane < cnt ? score_key(__uint_as_float(key[e])) : 0u;
   const RadixResult r = wave_radix<kWaveE>(hist_all[wave], key, cnt, (uint32_t)k);
@@ -695,6 +698,7 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(ThresholdParams 
 
 // The same threshold with one wave per row, for calls whose rows hold at
 // most 64 * kWaveE samples (lane-strided register keys, wave_radix).
+template <int E>  // register slots per lane: rows of up to 64 * E samples
 __global__ __launch_bounds__(256, 2) void threshold_wave_kernel(ThresholdParams P, int64_t rows) {
   __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kHistCopies * kHistStride];
   const int lane = threadIdx.x & 63;
@@ -718,12 +722,12 @@ __global__ __launch_bounds__(256, 2) void threshold_wave_kernel(ThresholdParams 
     return;
   }
   const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(P.samples + row * (int64_t)P.max_samples, 4u * (uint32_t)nsamp);
-  uint32_t key[kWaveE];
+  uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < kWaveE; ++e) key[e] = buf_ld4(rs, 4u * (uint32_t)lane + 256u * (uint32_t)e);
+  for (int e = 0; e < E; ++e) key[e] = buf_ld4(rs, 4u * (uint32_t)lane + 256u * (uint32_t)e);
 #pragma unroll
-  for (int e = 0; e < kWaveE; ++e) key[e] = 64 * e + lane < nsamp ? score_key(__uint_as_float(key[e])) : 0u;
-  const RadixResult r = wave_radix<kWaveE>(hist_all[wave], key, nsamp, (uint32_t)m);
+  for (int e = 0; e < E; ++e) key[e] = 64 * e + lane < nsamp ? score_key(__uint_as_float(key[e])) : 0u;
+  const RadixResult r = wave_radix<E>(hist_all[wave], key, nsamp, (uint32_t)m);
   // take_all leaves the low bits open: prefix is then a lower bound
   if (lane == 0) P.theta[row] = key_to_score(r.prefix);
 }
@@ -1265,8 +1269,13 @@ hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_
   return hipGetLastError();
 }
 hipError_t launch_threshold(const ThresholdParams& p, int64_t rows, hipStream_t s) {
-  if (p.max_samples <= 64 * kWaveE)
-    threshold_wave_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
+  const dim3 g((unsigned)((rows + 3) / 4));
+  if (p.max_samples <= 64 * 16)
+    threshold_wave_kernel<16><<<g, dim3(256), 0, s>>>(p, rows);
+  else if (p.max_samples <= 64 * 32)
+    threshold_wave_kernel<32><<<g, dim3(256), 0, s>>>(p, rows);
+  else if (p.max_samples <= 64 * kWaveE)
+    threshold_wave_kernel<kWaveE><<<g, dim3(256), 0, s>>>(p, rows);
   else
     threshold_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
   return hipGetLastError();
