@@ -96,7 +96,7 @@ def run_prefill(args, hs, synth, _lib, torch):
     log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step")
     for k, (n, tot) in sorted(kt.items(), key=lambda x: -x[1][1]):
         log(f"[bench]   {k:16s} launches={n:5d} avg={tot / n * 1e3:10.1f} us  share/step={tot / args.steps:8.3f} ms")
-    variants = prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch)
+    variants = None if args.no_options else prefill_variants(args, hs, w, q, kv, qs, ws, _lib, torch)
     return w, ms_per_step, kt, case, variants
 
 
@@ -231,63 +231,65 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
     torch.cuda.synchronize()
     us_graph = (time.perf_counter() - t0) * 1e6 / steps
     log(f"[bench] {wname}: {us_graph:.1f} us/step as one graph launch")
-    # option: the sparse layers gathering from the FP8 copy of the cache
-    copy = hs.kv_to_fp8(kv, n_kv=cap)
-    st = case["steps"][0]
-    _, _, idx0 = hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
-                                window=w.window, workspace=ws_full)
-    hs.kv_to_fp8(kv, seq_lens=seqs[0], out=copy)
-    hs.sparse_attn_reuse(st["q_sparse"][0], kv, idx0, top_k=w.top_k, window=w.window, seq_lens=seqs[0],
-                         workspace=ws_sp, kv_fp8=copy)
-    torch.cuda.synchronize()
-    _lib.timing_read()
-    _lib.timing_enable(True)
-    for x in st["q_sparse"]:
-        hs.sparse_attn_reuse(x, kv, idx0, top_k=w.top_k, window=w.window, seq_lens=seqs[0], workspace=ws_sp,
-                             kv_fp8=copy)
-    hs.kv_to_fp8(kv, seq_lens=seqs[0], out=copy)
-    torch.cuda.synchronize()
-    _lib.timing_enable(False)
-    kf = _lib.timing_read()
-    fp8_sparse_us = kf["sparse_decode"][1] / kf["sparse_decode"][0] * 1e3
-    fp8_append_us = kf["kv_fp8_convert"][1] / kf["kv_fp8_convert"][0] * 1e3
-    log(f"[bench] {wname}: fp8 sparse layer {fp8_sparse_us:.1f} us, appended-row conversion {fp8_append_us:.1f} us")
-    del copy
-    # option: block-level selection (block scores from the score rows, then
-    # the top blocks), against the token-level selection timed above
-    shape.flags = hs.HS_FLAG_BLOCK_SELECT
-    ws_blk = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
-    shape.flags = 0
-    blk_call = lambda: hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
-                                      window=w.window, flags=hs.HS_FLAG_BLOCK_SELECT, workspace=ws_blk)
-    blk_call()
-    torch.cuda.synchronize()
-    _lib.timing_read()
-    _lib.timing_enable(True)
-    blk_call()
-    torch.cuda.synchronize()
-    _lib.timing_enable(False)
-    kb = _lib.timing_read()
-    blk_sel_us = sum(kb[k][1] / kb[k][0] * 1e3 for k in ("block_max", "select_blocks"))
-    log(f"[bench] {wname}: block-level selection {blk_sel_us:.1f} us (block scores + top blocks)")
-    del ws_blk
-    # option: union of per-head top-k (heads' score rows, their top-k, union)
-    shape.flags = hs.HS_FLAG_HEAD_UNION
-    ws_uni = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
-    shape.flags = 0
-    uni_call = lambda: hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
-                                      window=w.window, flags=hs.HS_FLAG_HEAD_UNION, workspace=ws_uni)
-    uni_call()
-    torch.cuda.synchronize()
-    _lib.timing_read()
-    _lib.timing_enable(True)
-    uni_call()
-    torch.cuda.synchronize()
-    _lib.timing_enable(False)
-    ku = _lib.timing_read()
-    uni_sel_us = sum(ku[k][1] / ku[k][0] * 1e3 for k in ("decode_score", "select_decode", "head_union"))
-    log(f"[bench] {wname}: per-head union selection {uni_sel_us:.1f} us (head scores + head top-k + union)")
-    del ws_uni
+    fp8_sparse_us = fp8_append_us = blk_sel_us = uni_sel_us = None
+    if not args.no_options:
+        # option: the sparse layers gathering from the FP8 copy of the cache
+        copy = hs.kv_to_fp8(kv, n_kv=cap)
+        st = case["steps"][0]
+        _, _, idx0 = hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
+                                    window=w.window, workspace=ws_full)
+        hs.kv_to_fp8(kv, seq_lens=seqs[0], out=copy)
+        hs.sparse_attn_reuse(st["q_sparse"][0], kv, idx0, top_k=w.top_k, window=w.window, seq_lens=seqs[0],
+                             workspace=ws_sp, kv_fp8=copy)
+        torch.cuda.synchronize()
+        _lib.timing_read()
+        _lib.timing_enable(True)
+        for x in st["q_sparse"]:
+            hs.sparse_attn_reuse(x, kv, idx0, top_k=w.top_k, window=w.window, seq_lens=seqs[0], workspace=ws_sp,
+                                 kv_fp8=copy)
+        hs.kv_to_fp8(kv, seq_lens=seqs[0], out=copy)
+        torch.cuda.synchronize()
+        _lib.timing_enable(False)
+        kf = _lib.timing_read()
+        fp8_sparse_us = kf["sparse_decode"][1] / kf["sparse_decode"][0] * 1e3
+        fp8_append_us = kf["kv_fp8_convert"][1] / kf["kv_fp8_convert"][0] * 1e3
+        log(f"[bench] {wname}: fp8 sparse layer {fp8_sparse_us:.1f} us, appended-row conversion {fp8_append_us:.1f} us")
+        del copy
+        # option: block-level selection (block scores from the score rows, then
+        # the top blocks), against the token-level selection timed above
+        shape.flags = hs.HS_FLAG_BLOCK_SELECT
+        ws_blk = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
+        shape.flags = 0
+        blk_call = lambda: hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
+                                          window=w.window, flags=hs.HS_FLAG_BLOCK_SELECT, workspace=ws_blk)
+        blk_call()
+        torch.cuda.synchronize()
+        _lib.timing_read()
+        _lib.timing_enable(True)
+        blk_call()
+        torch.cuda.synchronize()
+        _lib.timing_enable(False)
+        kb = _lib.timing_read()
+        blk_sel_us = sum(kb[k][1] / kb[k][0] * 1e3 for k in ("block_max", "select_blocks"))
+        log(f"[bench] {wname}: block-level selection {blk_sel_us:.1f} us (block scores + top blocks)")
+        del ws_blk
+        # option: union of per-head top-k (heads' score rows, their top-k, union)
+        shape.flags = hs.HS_FLAG_HEAD_UNION
+        ws_uni = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max(lengths) + steps), dev)
+        shape.flags = 0
+        uni_call = lambda: hs.decode_step(st["q_full"], st["kv_new"], kv, seqs[0], max(lengths) + 1, top_k=w.top_k,
+                                          window=w.window, flags=hs.HS_FLAG_HEAD_UNION, workspace=ws_uni)
+        uni_call()
+        torch.cuda.synchronize()
+        _lib.timing_read()
+        _lib.timing_enable(True)
+        uni_call()
+        torch.cuda.synchronize()
+        _lib.timing_enable(False)
+        ku = _lib.timing_read()
+        uni_sel_us = sum(ku[k][1] / ku[k][0] * 1e3 for k in ("decode_score", "select_decode", "head_union"))
+        log(f"[bench] {wname}: per-head union selection {uni_sel_us:.1f} us (head scores + head top-k + union)")
+        del ws_uni
     # algorithmic bytes
     full_bytes = sum(512.0 * w.Hkv * (L + s + 1) for L in lengths for s in range(steps)) / steps
     sp_rows = sum(min(w.top_k, max(0, L + s + 1 - w.window)) + min(w.window, L + s + 1)
@@ -302,10 +304,10 @@ def run_decode(args, hs, synth, _lib, torch, wname, lengths, steps):
         "us_per_step": round(us_step, 2),
         "us_per_step_graph": round(us_graph, 2),
         "sparse_layer_kernel_us": round(sp_us, 2),
-        "fp8_sparse_layer_kernel_us": round(fp8_sparse_us, 2),
-        "fp8_append_conversion_us": round(fp8_append_us, 2),
-        "block_select_us": round(blk_sel_us, 2),
-        "head_union_select_us": round(uni_sel_us, 2),
+        "fp8_sparse_layer_kernel_us": None if fp8_sparse_us is None else round(fp8_sparse_us, 2),
+        "fp8_append_conversion_us": None if fp8_append_us is None else round(fp8_append_us, 2),
+        "block_select_us": None if blk_sel_us is None else round(blk_sel_us, 2),
+        "head_union_select_us": None if uni_sel_us is None else round(uni_sel_us, 2),
         "kernels": {k: {"launches_per_step": n / steps, "avg_us": round(tot / n * 1e3, 1)} for k, (n, tot) in kt.items()},
         "sparse_decode_roofline": {"bound": "hbm", "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -402,6 +404,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-options", action="store_true",
+                    help="time the default path only (no selection-score, block, union or FP8 option runs)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="one prefill32k full + sparse layer, one decode64 step and a 1 GiB calibration copy, for counter runs")
