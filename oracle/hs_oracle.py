@@ -59,6 +59,11 @@ design notes of the repository):
      logit and keeps its top k (rules R4, R5, R8 per head); the group's set
      is the union of the G head sets, emitted ascending in a row of G * k
      entries padded with -1.
+  R13 KV Bridging: the cross-decoder's full-attention K and V rows of a token
+     are linear projections of the self-decoder's hidden state of that token,
+     K_g = h W_K,g and V_g = h W_V,g per KV head g, with no bias, norm or
+     position rotation (the pages name the inputs and outputs only); the
+     cache stores them in bf16, rounded to nearest even.
   R1' (optional score, score="prob"): the softmax-normalised group score
      max over h of (scale * <q_h(t), k_g(j)> - lse_h(t)), lse_h(t) the log
      of the softmax denominator of head h over keys 0..p, i.e. the log of the
@@ -88,6 +93,8 @@ __all__ = [
     "fp8_scale_exponent",
     "quantize_fp8",
     "block_select",
+    "kv_bridge",
+    "bf16_round",
 ]
 
 
@@ -404,3 +411,36 @@ def quantize_fp8(x: np.ndarray, e: int):
     y = torch.from_numpy(np.asarray(x, np.float64) * 2.0 ** (-e)).clamp(-E4M3_MAX, E4M3_MAX)
     q = y.to(torch.float32).to(torch.float8_e4m3fn)
     return q.view(torch.uint8).numpy(), q.to(torch.float64).numpy() * 2.0 ** e
+
+
+# ---------------------------------------------------------------- KV Bridging
+
+def kv_bridge(h: np.ndarray, w_kv: np.ndarray):
+    """KV Bridging (reading R13), [HS2-cs] "Proc neni nutne znovu zpracovat
+    cely dlouhy vstup" and [DAIR] "Two levels of KV sharing": the
+    full-attention layers of the cross-decoder take their keys and values from
+    the hidden states of the self-decoder, so prefill can stop after the
+    self-decoder ([DAIR] "Prefill exits early").
+
+    h: [n][d_model] hidden states of n tokens; w_kv: [Hkv][2][d][d_model], the
+    projection rows (index 0: keys, 1: values) of each KV head, laid out as a
+    linear layer's weight (one row per output feature). Returns (K, V), each
+    [Hkv][n][d] float64: K[g][t][e] = sum_i h[t][i] * w_kv[g][0][e][i],
+    V[g][t][e] = sum_i h[t][i] * w_kv[g][1][e][i]."""
+    h = np.asarray(h, np.float64)
+    w = np.asarray(w_kv, np.float64)
+    Hkv, two, d, d_model = w.shape
+    if two != 2 or h.shape[1] != d_model:
+        raise ValueError("w_kv must be [Hkv][2][d][d_model] with d_model = h.shape[1]")
+    K = np.stack([h @ w[g, 0].T for g in range(Hkv)])
+    V = np.stack([h @ w[g, 1].T for g in range(Hkv)])
+    return K, V
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even to bfloat16 precision (8 significant bits), as
+    float64 values: the precision the cache stores. Finite inputs within the
+    normal range of bf16."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)                    # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)  # rint: ties to even

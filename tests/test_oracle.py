@@ -604,3 +604,64 @@ def test_head_union_contains_group_max_top_token():
     for r in range(3):
         assert t["idx"][r, 0, 0] in set(u["idx"][r, 0].tolist())
         assert u["idx"].shape == (3, 1, 4)
+
+
+# ---------------------------------------------------------------- KV Bridging (R13)
+
+def test_kv_bridge_one_hot_hidden_states_pick_weight_columns():
+    """Pin of the layout: a hidden state that is the unit vector e_i gives, for
+    every KV head g, key row = column i of that head's key projection rows and
+    value row = column i of its value projection rows. A transposed weight, a
+    head or K/V mix-up, or a dropped row fails this."""
+    rng = np.random.default_rng(7)
+    Hkv, d, d_model = 3, 128, 40
+    w = bf16_exact((Hkv, 2, d, d_model), rng)
+    cols = [0, 5, 39, 17]
+    h = np.zeros((len(cols), d_model), np.float32)
+    for t, i in enumerate(cols):
+        h[t, i] = 1.0
+    K, V = orc.kv_bridge(h, w)
+    assert K.shape == (Hkv, len(cols), d) and V.shape == (Hkv, len(cols), d)
+    for g in range(Hkv):
+        for t, i in enumerate(cols):
+            assert np.array_equal(K[g, t], w[g, 0, :, i])
+            assert np.array_equal(V[g, t], w[g, 1, :, i])
+
+
+def test_kv_bridge_matches_torch_linear_in_float64():
+    """Pin against a library routine: torch.nn.functional.linear (float64)
+    with the heads' K rows and V rows stacked as one weight."""
+    rng = np.random.default_rng(8)
+    Hkv, d, d_model, n = 2, 128, 96, 33
+    h = bf16_exact((n, d_model), rng)
+    w = bf16_exact((Hkv, 2, d, d_model), rng, 1 / math.sqrt(d_model))
+    K, V = orc.kv_bridge(h, w)
+    y = torch.nn.functional.linear(torch.from_numpy(h).double(), torch.from_numpy(w).double().reshape(-1, d_model))
+    y = y.reshape(n, Hkv, 2, d).numpy()
+    assert np.allclose(K, y[:, :, 0].transpose(1, 0, 2), rtol=0, atol=1e-12)
+    assert np.allclose(V, y[:, :, 1].transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+def test_kv_bridge_rows_independent():
+    """Each token's K/V depend on its own hidden state only: bridging a chunk
+    equals the matching rows of bridging the whole sequence (a chunked
+    prefill writes the same cache rows)."""
+    rng = np.random.default_rng(9)
+    h = bf16_exact((50, 64), rng)
+    w = bf16_exact((2, 2, 128, 64), rng, 0.125)
+    K, V = orc.kv_bridge(h, w)
+    K2, V2 = orc.kv_bridge(h[20:35], w)
+    assert np.array_equal(K[:, 20:35], K2) and np.array_equal(V[:, 20:35], V2)
+
+
+def test_bf16_round_matches_torch_and_ties_to_even():
+    """Pin of the cache rounding against torch's float32 -> bfloat16
+    conversion (round to nearest even) on random values and on exact halfway
+    cases, where the even neighbour must win."""
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(orc.bf16_round(x.astype(np.float64)), want)
+    half = 2.0 ** -8  # half a bf16 ulp of [1, 2)
+    ties = np.array([1 + half, 1 + 3 * half, -(1 + half), 2 + 2 * half, 1 + 5 * half])
+    assert np.array_equal(orc.bf16_round(ties), [1.0, 1 + 4 * half, -1.0, 2.0, 1 + 4 * half])
