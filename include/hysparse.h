@@ -144,15 +144,22 @@ typedef enum {
    decode adds one pass over the K rows for the heads' scores. Not combined
    with HS_FLAG_PROB_SCORE or HS_FLAG_BLOCK_SELECT (HS_ERR_UNSUPPORTED). */
 #define HS_FLAG_HEAD_UNION 16u
-#define HS_FLAG_FP8_KV 4u       /* hs_sparse_attn_reuse reads its keys and
-                                   values from the FP8 copy of the cache
-                                   made by hs_kv_fp8_convert (kv then points
-                                   to that copy; strides must be 0). The
-                                   pages leave the cache precision open
-                                   ([DAIR] "Cheaper at 1M tokens" gives
-                                   the cache size only): this halves the
-                                   gathered bytes.
-                                   Rejected by the other calls. */
+#define HS_FLAG_FP8_KV 4u       /* hs_sparse_attn_reuse and hs_decode_step
+                                   read keys and values from the FP8 copy
+                                   of the cache made by hs_kv_fp8_convert
+                                   (kv then points to that copy; strides
+                                   must be 0). The pages leave the cache
+                                   precision open ([DAIR] "Cheaper at 1M
+                                   tokens" gives the cache size only): this
+                                   halves the bytes read. hs_decode_step
+                                   then writes kv_new into the copy,
+                                   quantised with the stored scales of its
+                                   KV head (values beyond the range
+                                   saturate), and leaves any bf16 cache
+                                   alone; it takes the logit score (token
+                                   or block level), not HS_FLAG_PROB_SCORE
+                                   or HS_FLAG_HEAD_UNION (HS_ERR_UNSUPPORTED).
+                                   Rejected by hs_full_attn_select. */
 
 typedef struct {
   int32_t batch;       /* B >= 1                                            */
@@ -194,6 +201,24 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv,
                               void* o, float* lse, int32_t* idx, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* Diagnostics of the token-level selection of hs_full_attn_select (not
+ * needed to use the library). After a call with workspace ws (and once the
+ * stream has reached it), the workspace holds, at these byte offsets from ws:
+ *   defer_count_off   uint32: rows the one-wave selection queued for the
+ *                     block-wide path (candidate count outside [k, buffer],
+ *                     more candidates than one wave holds, or a forced rescan);
+ *   defer_rows_off    int32[that count]: those rows, as (b*n_q + t)*Hkv + g,
+ *                     in no particular order;
+ *   rescan_count_off  uint32: queued rows whose scores were recomputed
+ *                     exactly because the candidate buffer could not be
+ *                     trusted (too few or too many entries).
+ * Returns HS_ERR_UNSUPPORTED when the shape's selection keeps no such record
+ * (top_k == 0, HS_FLAG_BLOCK_SELECT, HS_FLAG_HEAD_UNION). Runs on the host
+ * only; reads nothing. */
+hs_status hs_select_diagnostics(const hs_shape* s, size_t* defer_rows_off,
+                                size_t* defer_count_off,
+                                size_t* rescan_count_off);
+
 /* One sparse layer of a hybrid block ([HS2-cs], [DAIR]): reuses the full
  * layer's KV cache and selection. For every row and head h (group g):
  * o = softmax over j in S of s_h(j), weighted sum of v_g(j), where
@@ -227,6 +252,32 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new,
                          int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* KV Bridging ([HS2-cs] section "Proc neni nutne znovu zpracovat cely dlouhy
+ * vstup": the cross-decoder's full-attention layers build their keys and
+ * values from the self-decoder's hidden states; [DAIR] bullets "Two levels
+ * of KV sharing" and "Prefill exits early": since every cross-decoder cache
+ * comes from the self-decoder, prefill can stop once the self-decoder is
+ * done). Writes, for every batch entry b, chunk row t < n_q and KV head g,
+ * cache row p = n_kv - n_q + t:
+ *   K_g(p) = h[b][t] W[g][0]^T,   V_g(p) = h[b][t] W[g][1]^T
+ * (a linear projection with no bias, norm or position rotation: the pages
+ * name only its input and output), fp32 accumulation, stored as bf16 rounded
+ * to nearest even.
+ *   hidden  bf16 [B][n_q][d_model], the self-decoder's hidden states of the
+ *           chunk's tokens;
+ *   w_kv    bf16 [Hkv][2][128][d_model], the projection rows (index 0: keys,
+ *           1: values) of each KV head, laid out as a linear layer's weight;
+ *   kv      the cache, in the layout of s (strides allowed); only the rows
+ *           above are written.
+ * Uses s->batch, n_q, n_kv, kv_capacity, kv_heads, the strides (q_heads,
+ * top_k and window are validated as for the other calls but not used).
+ * Needs 1 <= n_q <= n_kv <= kv_capacity and d_model a multiple of 64 in
+ * [64, 65536] (else HS_ERR_UNSUPPORTED). A decode step bridges its token by
+ * treating kv_new [B][Hkv][2][128] as a cache of capacity 1 (n_q = n_kv = 1).
+ * Runs on `stream`; errors as for the other calls. */
+hs_status hs_kv_bridge(const hs_shape* s, const void* hidden, int32_t d_model,
+                       const void* w_kv, void* kv, void* stream);
+
 /* Diagnostics: per-kernel timing. While enabled (on != 0), every kernel the
  * library launches is bracketed by a pair of HIP events recorded on the
  * call's stream, so durations are those of the kernels themselves on the
@@ -244,7 +295,6 @@ hs_status hs_timing_enable(int32_t on);
  * sets *count to the number of distinct kernels, and clears the totals. */
 hs_status hs_timing_read(hs_kernel_time* out, int32_t max, int32_t* count);
 
-/* Static English name of a status code. */
 /* FP8 (e4m3) copy of a bf16 cache for the sparse layers (HS_FLAG_FP8_KV).
  *
  * Layout of the copy (caller-owned device buffer of hs_kv_fp8_size bytes,
@@ -270,6 +320,19 @@ hs_status hs_timing_read(hs_kernel_time* out, int32_t max, int32_t* count);
 hs_status hs_kv_fp8_size(const hs_shape* s, size_t* bytes);
 hs_status hs_kv_fp8_convert(const hs_shape* s, const void* kv, void* kv8, const int32_t* seq_lens, void* stream);
 
+/* Diagnostics: gather-rate probe (not needed to use the library). Reads
+ * the 512-byte rows src[idx[i]] (i < n; K half then V half, the layout of one
+ * token of one KV head in the default cache) with the memory access pattern
+ * of the sparse layers' gathers and none of their arithmetic, per_wave keys
+ * per wave (1..2048, staged in LDS like the sparse layers' key lists), and writes one folded word per lane to out (uint32 [64 * ceil(n /
+ * per_wave)], rounded up to whole 4-wave blocks). Every idx[i] must lie in
+ * [0, src_rows); rows beyond src_rows * 512 bytes read as zero. Measures the
+ * rate at which the chip can gather rows from a buffer of a given size (L2,
+ * last-level cache or HBM resident). Runs on `stream`. */
+hs_status hs_gather_probe(const void* src, int64_t src_rows, const int32_t* idx, int64_t n, int32_t per_wave,
+                          uint32_t* out, void* stream);
+
+/* Static English name of a status code. */
 const char* hs_status_string(hs_status st);
 
 /* Detail message of the calling thread's most recent failed call ("" if

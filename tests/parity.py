@@ -142,8 +142,34 @@ def sample_rows(n_q: int, n_kv: int, top_k: int, window: int, spans=(), evenly=8
     return sorted(r for r in rows if 0 <= r < n_q)
 
 
+def check_idx_structure(idx, positions, window, k, chunk=4096):
+    """Oracle-free check of EVERY index row, on the device: row r (positions[r]
+    = p) must hold min(k, |C(p)|) valid entries, strictly ascending (so no
+    duplicates), all in C(p) = [0, p - W], followed by -1 padding.
+    idx: int32 tensor [R][Hkv][k] (or [R][k]); positions: int64 tensor [R] on
+    the same device. Returns the number of rows checked."""
+    if idx.dim() == 2:
+        idx = idx[:, None, :]
+    R = idx.shape[0]
+    assert positions.shape == (R,)
+    ar = torch.arange(k, device=idx.device)
+    for r0 in range(0, R, chunk):
+        blk = idx[r0:r0 + chunk].long()
+        p = positions[r0:r0 + chunk].long()
+        cnt = (p - window + 1).clamp(min=0, max=k)
+        want = ar[None, None, :] < cnt[:, None, None]
+        bad = ~torch.where(want, blk >= 0, blk == -1)
+        assert not bool(bad.any()), f"rows {r0}..: padding or count wrong at {bad.nonzero()[:4].tolist()}"
+        lim = (p - window)[:, None, None]
+        assert not bool((want & ((blk > lim) | (blk < 0))).any()), f"rows {r0}..: entry outside C(p)"
+        if k > 1:
+            up = blk[..., 1:] > blk[..., :-1]
+            assert not bool((want[..., 1:] & ~up).any()), f"rows {r0}..: not strictly ascending"
+    return R
+
+
 def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_sparse=(), o_sparse=(), scale=None,
-                  score="logit", blocks=False, union=False):
+                  score="logit", blocks=False, union=False, progress=0):
     """Checks one prefill call (and its sparse layers) on the given query rows;
     score names the oracle's selection score ("logit" or "prob"), blocks asks
     for block-level selection."""
@@ -160,7 +186,21 @@ def check_prefill(q_full, kv, n_kv, top_k, window, o, lse, idx, rows=None, q_spa
     for b in range(B):
         K, V = cache_np(kv, b, n_kv)
         qb = f32(q_full[b])[rows]
-        res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale, score, blocks=blocks, union=union)
+        if progress:  # long contexts: the oracle in row batches, with a line per batch
+            parts = []
+            for r0 in range(0, len(rows), progress):
+                parts.append(orc.full_attn_select_rows(qb[r0:r0 + progress], K, V, pos[r0:r0 + progress], top_k,
+                                                       window, scale, score, blocks=blocks, union=union))
+                print(f"[case] oracle rows {r0 + len(parts[-1]['o'])}/{len(rows)}", flush=True)
+            res = {"o": np.concatenate([x["o"] for x in parts]), "lse": np.concatenate([x["lse"] for x in parts]),
+                   "idx": np.concatenate([x["idx"] for x in parts])}
+            if union:
+                res["heads"] = sum((x["heads"] for x in parts), [])
+            else:
+                res["tau"] = np.concatenate([x["tau"] for x in parts])
+                res["sigma"] = sum((x["sigma"] for x in parts), [])
+        else:
+            res = orc.full_attn_select_rows(qb, K, V, pos, top_k, window, scale, score, blocks=blocks, union=union)
         check_row = check_block_row if blocks else check_idx_row
         full_stats.add(o_np[b, rows], res["o"])
         if lse_np is not None:

@@ -144,3 +144,40 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libhysparse.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_select_diagnostics_offsets(lib):
+    """The selection records lie inside the workspace, one int32 per row then
+    two uint32 counters; shapes without such records are rejected."""
+    s = base_shape(n_q=300, n_kv=900, kv_capacity=900)
+    ws = _lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, s)
+    a, b, c = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _lib.check(lib.hs_select_diagnostics(ctypes.byref(s), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    rows = s.batch * s.n_q * s.kv_heads
+    assert b.value == a.value + 4 * rows and c.value == b.value + 4 and c.value + 4 <= ws
+    for flags in (hs.HS_FLAG_BLOCK_SELECT, hs.HS_FLAG_HEAD_UNION):
+        s2 = base_shape(top_k=64, flags=flags)
+        assert lib.hs_select_diagnostics(ctypes.byref(s2), ctypes.byref(a), ctypes.byref(b),
+                                         ctypes.byref(c)) == _lib.HS_ERR_UNSUPPORTED
+    s3 = base_shape(top_k=0)
+    assert lib.hs_select_diagnostics(ctypes.byref(s3), ctypes.byref(a), ctypes.byref(b),
+                                     ctypes.byref(c)) == _lib.HS_ERR_UNSUPPORTED
+    assert lib.hs_select_diagnostics(ctypes.byref(s), None, ctypes.byref(b),
+                                     ctypes.byref(c)) == _lib.HS_ERR_INVALID_ARG
+
+
+def test_kv_bridge_arguments_rejected_before_launch(lib):
+    """hs_kv_bridge validates on the host: d_model a multiple of 64, rows
+    inside the cache, non-NULL aligned pointers."""
+    fake = ctypes.c_void_p(1 << 20)
+    s = base_shape(n_q=32, n_kv=64, kv_capacity=64)
+    for d_model, status in ((100, _lib.HS_ERR_UNSUPPORTED), (0, _lib.HS_ERR_UNSUPPORTED),
+                            (70000, _lib.HS_ERR_UNSUPPORTED)):
+        assert lib.hs_kv_bridge(ctypes.byref(s), fake, d_model, fake, fake, None) == status, lib.hs_last_error()
+    assert lib.hs_kv_bridge(ctypes.byref(s), None, 128, fake, fake, None) == _lib.HS_ERR_INVALID_ARG
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.hs_kv_bridge(ctypes.byref(s), fake, 128, mis, fake, None) == _lib.HS_ERR_INVALID_ARG
+    s2 = base_shape(n_q=65, n_kv=64, kv_capacity=64)
+    assert lib.hs_kv_bridge(ctypes.byref(s2), fake, 128, fake, fake, None) == _lib.HS_ERR_INVALID_ARG
+    s3 = base_shape(n_q=1, n_kv=64, kv_capacity=64, flags=_lib.HS_FLAG_FP8_KV)
+    assert lib.hs_kv_bridge(ctypes.byref(s3), fake, 128, fake, fake, None) == _lib.HS_ERR_UNSUPPORTED

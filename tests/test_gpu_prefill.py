@@ -117,3 +117,10 @@ def test_rescan_streaming_long_rows():
     n = 9500
     rows = [100, 8000, 9499]
     run(1, n, n, 4, 1, 64, 16, seed=900, rows=rows, flags=hs.HS_FLAG_EXACT_RESCAN)
+
+
+def test_threshold_wave32_all_rows():
+    """Rows of 1025..2048 samples take the one-wave threshold with 32
+    register slots per lane (n = 1800, k = 64, stride 1: 1792 samples);
+    every row is checked."""
+    run(1, 1800, 1800, 8, 2, 64, 32, seed=1000)

@@ -1,59 +1,82 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times, checked on sampled rows (sequences) the oracle can compute
-one by one."""
+benchmark times: the oracle checks sampled rows (sequences, steps) one by
+one; every index row of every call is also checked on the device for its
+structure (count, order, range, padding), which needs no oracle."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as orc
 import token_level_sparse_hs_amd as hs
-from token_level_sparse_hs_amd import synth
-from parity import OutStats, cache_np, check_idx_row, check_prefill, f32, sample_rows
+from token_level_sparse_hs_amd import _lib, synth
+from parity import OutStats, cache_np, check_idx_row, check_idx_structure, check_prefill, f32, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
+# Needle sanity floors: the fraction of (needle, KV group) pairs whose planted
+# key is among the selection of the first row of its query span. The recipe
+# makes selection non-trivial without forcing it; the floors sit at about half
+# of the rates these seeded inputs give (0.41, 0.13, 0.05), far above chance
+# (k / |C| per pair: 0.06-0.12, 0.015, 0.004).
+NEEDLE_FLOOR = {"prefill32k": 0.2, "chunk128k": 0.06, "ctx1m": 0.02}
 
-def run_prefill_workload(name, evenly=8, flags=0):
+
+def run_prefill_workload(name, evenly=8, flags=0, progress=0, max_deferred=8):
     w = synth.WORKLOADS[name]
     score = "prob" if flags & hs.HS_FLAG_PROB_SCORE else "logit"
     blocks = bool(flags & hs.HS_FLAG_BLOCK_SELECT)
     union = bool(flags & hs.HS_FLAG_HEAD_UNION)
-    print(f"[case] workload {name}: B={w.B} n_q={w.n_q} n_kv={w.n_kv} k={w.top_k} W={w.window} score={score} blocks={blocks}",
-          flush=True)
+    print(f"[case] workload {name}: B={w.B} n_q={w.n_q} n_kv={w.n_kv} k={w.top_k} W={w.window} score={score} "
+          f"blocks={blocks} union={union}", flush=True)
     case = synth.make_prefill_case(w, DEV, kv_capacity=w.n_kv + w.decode_steps)
     q, kv, qs = case["q_full"], case["kv"], case["q_sparse"]
-    o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, flags=flags)
+    shape = hs.make_shape(batch=w.B, n_q=w.n_q, n_kv=w.n_kv, kv_capacity=kv.shape[2], q_heads=w.Hq,
+                          kv_heads=w.Hkv, top_k=w.top_k, window=w.window, flags=flags)
+    ws = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_FULL_ATTN_SELECT, shape), DEV)
+    o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window, flags=flags, workspace=ws)
     osp = [hs.sparse_attn_reuse(x, kv, idx, top_k=w.top_k, window=w.window, n_kv=w.n_kv, flags=flags) for x in qs]
     torch.cuda.synchronize()
+    pos_all = torch.arange(w.n_kv - w.n_q, w.n_kv, device=DEV).repeat(w.B)
+    if not blocks and not union:
+        n = check_idx_structure(idx.view(w.B * w.n_q, w.Hkv, w.top_k), pos_all, w.window, w.top_k)
+        print(f"[case] {name}: structure of all {n * w.Hkv} index rows ok", flush=True)
     pos, spans = case["needles"]
-    rows = sample_rows(w.n_q, w.n_kv, w.top_k, w.window, spans, evenly)
-    print(f"[case] checking rows {rows}", flush=True)
+    rows = set(sample_rows(w.n_q, w.n_kv, w.top_k, w.window, spans, evenly))
+    if not blocks and not union:
+        diag = hs.select_diagnostics(q, kv, w.n_kv, ws, top_k=w.top_k, window=w.window, flags=flags)
+        dr = diag["deferred_rows"]
+        print(f"[case] {name}: {len(dr)} rows took the block-wide selection, {diag['rescans']} exact rescans",
+              flush=True)
+        # rows of batch entry 0 that took the block-wide path join the oracle sample
+        ts = sorted(set(int(r) // w.Hkv for r in dr.tolist() if int(r) // w.Hkv < w.n_q))
+        rows.update(ts[:: max(1, len(ts) // max_deferred)][:max_deferred])
+    rows = sorted(rows)
+    print(f"[case] checking {len(rows)} rows against the oracle: {rows[:12]}...", flush=True)
     res = check_prefill(q, kv, w.n_kv, w.top_k, w.window, o, lse, idx, rows=rows, q_sparse=qs, o_sparse=osp,
-                        score=score, blocks=blocks, union=union)
+                        score=score, blocks=blocks, union=union, progress=progress)
     print(f"[case] {name}: near-tie swaps {res['swaps']}, full max-abs {res['full'].max_abs:.2e} "
           f"mean {res['full'].mean_abs:.2e}, sparse max-abs {res['sparse'].max_abs:.2e}", flush=True)
-    # needles: the planted keys should mostly be selected by their span rows
-    if pos:
-        idx_np = idx.cpu().numpy()
+    if pos and not blocks and not union:
+        idx_np = idx[0].cpu().numpy()
         hit = tot = 0
         for p_, t0 in zip(pos, spans):
             for g in range(w.Hkv):
                 tot += 1
-                hit += int(p_ in set(idx_np[0, t0, g].tolist()))
+                hit += int(p_ in set(idx_np[t0, g].tolist()))
         print(f"[case] {name}: needles selected by their span's first row: {hit}/{tot}", flush=True)
-        assert hit > 0
+        assert hit >= NEEDLE_FLOOR[name] * tot, f"needle hit rate {hit}/{tot} below {NEEDLE_FLOOR[name]}"
     return w, case, idx
 
 
 def test_prefill32k_full_size():
-    run_prefill_workload("prefill32k")
+    run_prefill_workload("prefill32k", evenly=64)
 
 
 def test_prefill32k_full_size_prob_score():
     """The probability selection score at full size (attention, then the
     sampled threshold and the QK-only candidate pass on its lse)."""
-    run_prefill_workload("prefill32k", evenly=4, flags=hs.HS_FLAG_PROB_SCORE)
+    run_prefill_workload("prefill32k", evenly=8, flags=hs.HS_FLAG_PROB_SCORE)
 
 
 def test_prefill32k_full_size_block_select():
@@ -68,13 +91,14 @@ def test_prefill32k_full_size_head_union():
     run_prefill_workload("prefill32k", evenly=3, flags=hs.HS_FLAG_HEAD_UNION)
 
 
+@pytest.mark.timeout(600)
 def test_chunk128k_full_size():
-    run_prefill_workload("chunk128k", evenly=4)
+    run_prefill_workload("chunk128k", evenly=64, progress=16)
 
 
 def decode_check(kv, lengths, steps_data, w, seqs_to_check, steps):
-    """Runs `steps` decode steps on the whole batch; checks chosen sequences."""
-    B = len(lengths)
+    """Runs `steps` decode steps on the whole batch; checks chosen sequences
+    against the oracle and every sequence's index rows for structure."""
     host = {b: cache_np(kv, b, lengths[b] + steps) for b in seqs_to_check}
     scale = orc.default_scale(128)
     full, sparse = OutStats(), OutStats()
@@ -88,6 +112,7 @@ def decode_check(kv, lengths, steps_data, w, seqs_to_check, steps):
         osp = [hs.sparse_attn_reuse(x, kv, idx, top_k=w.top_k, window=w.window, seq_lens=seq_lens)
                for x in st["q_sparse"]]
         torch.cuda.synchronize()
+        check_idx_structure(idx, seq_lens.long() - 1, w.window, w.top_k)
         idx_np = idx.cpu().numpy()
         for b in seqs_to_check:
             K, V = host[b]
@@ -101,25 +126,27 @@ def decode_check(kv, lengths, steps_data, w, seqs_to_check, steps):
                 r, _ = orc.sparse_attention_rows(f32(x[b])[None], K, V, idx_np[b][None], np.array([cur[b] - 1]),
                                                  w.window, scale)
                 sparse.add(f32(osx[b]), r[0])
-        print(f"[case] decode step {s} checked", flush=True)
+        print(f"[case] decode step {s} checked ({len(seqs_to_check)} sequences)", flush=True)
     full.check("decode full o")
     sparse.check("decode sparse o")
     return swaps
 
 
+@pytest.mark.timeout(600)
 def test_decode64_full_size():
     w = synth.WORKLOADS["decode64"]
     lengths = synth.decode_lengths(w)
-    steps = 2
+    steps = 4
     print(f"[case] decode64: {len(lengths)} sequences, sum of lengths {sum(lengths)}", flush=True)
     case = synth.make_decode_case(w, DEV, lengths, steps)
     order = np.argsort(lengths)
-    check = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    check = sorted(set(int(order[i]) for i in np.linspace(0, len(order) - 1, 8).round().astype(int)))
     decode_check(case["kv"], lengths, case["steps"], w, check, steps)
 
 
+@pytest.mark.timeout(900)
 def test_ctx1m_prefill_and_decode():
-    w, case, idx = run_prefill_workload("ctx1m", evenly=2)
+    w, case, idx = run_prefill_workload("ctx1m", evenly=16, progress=4, max_deferred=2)
     # decode on the same cache: the chunk's rows are in place, append after
     kv = case["kv"]
     del case["q_full"], case["q_sparse"]

@@ -22,7 +22,8 @@ from ._lib import (HS_FLAG_BLOCK_SELECT, HS_FLAG_EXACT_RESCAN, HS_FLAG_FP8_KV, H
                    HS_FLAG_PROB_SCORE, HsError, HsShape)
 
 __all__ = ["full_attn_select", "sparse_attn_reuse", "decode_step", "make_shape", "HsError",
-           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "HS_FLAG_BLOCK_SELECT", "HS_FLAG_HEAD_UNION", "kv_to_fp8", "version"]
+           "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "HS_FLAG_BLOCK_SELECT", "HS_FLAG_HEAD_UNION", "kv_to_fp8", "version",
+           "select_diagnostics", "kv_bridge"]
 
 
 def version() -> int:
@@ -130,12 +131,14 @@ def sparse_attn_reuse(q, kv, idx, *, top_k, window, n_kv=None, seq_lens=None, sc
 
 
 def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.0, with_lse=True, flags=0,
-                kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None):
+                kv_heads=None, kv_capacity=None, kv_strides=None, workspace=None, kv_fp8=None):
     """Decode full-attention layer: append kv_new at seq_lens[b]-1, attend, select once.
 
     q bf16 [B][Hq][128]; kv_new bf16 [B][Hkv][2][128]; seq_lens int32 [B] (device,
     including the new token). Returns (o [B][Hq][128], lse [B][Hq] or None,
     idx int32 [B][Hkv][top_k], or [B][Hkv][G*top_k] with HS_FLAG_HEAD_UNION).
+    kv_fp8: the cache's FP8 copy (from kv_to_fp8) to append to and read
+    instead of kv, which then only gives the shape and is left unchanged.
     """
     _check_bf16("q", q, 3)
     _check_bf16("kv_new", kv_new, 4)
@@ -144,6 +147,8 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
         kv_heads, kv_capacity = _kv_dims(kv, None)
     if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda:
         raise TypeError("seq_lens must be an int32 device tensor")
+    if kv_fp8 is not None:
+        flags |= _lib.HS_FLAG_FP8_KV
     shape = make_shape(batch=B, n_q=1, n_kv=0, kv_capacity=kv_capacity, q_heads=Hq, kv_heads=kv_heads,
                        top_k=top_k, window=window, scale=scale, kv_strides=kv_strides, flags=flags, head_dim=d)
     dev = q.device
@@ -153,11 +158,54 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
     nbytes = _lib.workspace_size(_lib.HS_OP_DECODE_STEP, shape, max_seq_len)
     ws = workspace if workspace is not None else _lib.alloc_workspace(nbytes, dev)
     lib = _lib.load()
-    _lib.check(lib.hs_decode_step(ctypes.byref(shape), _lib.ptr(q), _lib.ptr(kv_new), _lib.ptr(kv),
+    _lib.check(lib.hs_decode_step(ctypes.byref(shape), _lib.ptr(q), _lib.ptr(kv_new),
+                                  _lib.ptr(kv if kv_fp8 is None else kv_fp8),
                                   _lib.ptr(seq_lens), max_seq_len, _lib.ptr(o), _lib.ptr(lse),
                                   _lib.ptr(idx) if top_k > 0 else None, _lib.ptr(ws),
                                   0 if ws is None else ws.numel(), _lib.stream_handle(dev)))
     return o, lse, idx
+
+
+def kv_bridge(hidden, w_kv, kv, n_kv, *, kv_strides=None, kv_heads=None, kv_capacity=None):
+    """KV Bridging: writes cache rows [n_kv - n_q, n_kv) of every (b, KV head)
+    of kv from the self-decoder's hidden states (include/hysparse.h,
+    hs_kv_bridge): K = hidden W[g][0]^T, V = hidden W[g][1]^T, bf16.
+
+    hidden: bf16 [B][n_q][d_model]; w_kv: bf16 [Hkv][2][128][d_model]; kv: the
+    cache [B][Hkv][capacity][2][128] (or kv_new [B][Hkv][2][128] viewed as a
+    cache of capacity 1 with n_kv = 1). Returns kv."""
+    _check_bf16("hidden", hidden, 3)
+    _check_bf16("w_kv", w_kv, 4)
+    B, n_q, d_model = hidden.shape
+    if kv_strides is None:
+        kv_heads, kv_capacity = _kv_dims(kv, None)
+    if tuple(w_kv.shape) != (kv_heads, 2, 128, d_model):
+        raise ValueError(f"w_kv must be [{kv_heads}][2][128][{d_model}] (got {tuple(w_kv.shape)})")
+    shape = make_shape(batch=B, n_q=n_q, n_kv=n_kv, kv_capacity=kv_capacity, q_heads=kv_heads, kv_heads=kv_heads,
+                       top_k=0, window=1, kv_strides=kv_strides)
+    _lib.check(_lib.load().hs_kv_bridge(ctypes.byref(shape), _lib.ptr(hidden), d_model, _lib.ptr(w_kv), _lib.ptr(kv),
+                                        _lib.stream_handle(hidden.device)))
+    return kv
+
+
+def select_diagnostics(q, kv, n_kv, workspace, *, top_k, window, flags=0):
+    """Records of the token-level selection that full_attn_select(q, kv, n_kv,
+    ..., workspace=workspace) left in `workspace` (include/hysparse.h,
+    hs_select_diagnostics): {"deferred_rows": int64 tensor of the rows
+    (b*n_q + t)*Hkv + g that took the block-wide path, "rescans": rows whose
+    scores were recomputed exactly}. Synchronises the device."""
+    B, n_q, Hq, d = q.shape
+    kv_heads, kv_capacity = _kv_dims(kv, None)
+    shape = make_shape(batch=B, n_q=n_q, n_kv=n_kv, kv_capacity=kv_capacity, q_heads=Hq, kv_heads=kv_heads,
+                       top_k=top_k, window=window, flags=flags, head_dim=d)
+    a, b, c = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _lib.check(_lib.load().hs_select_diagnostics(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b),
+                                                 ctypes.byref(c)))
+    torch.cuda.synchronize(workspace.device)
+    words = workspace[b.value:c.value + 4].view(torch.int32).cpu()
+    n = int(words[0])
+    rows = workspace[a.value:a.value + 4 * n].view(torch.int32).to(torch.int64).cpu()
+    return {"deferred_rows": rows, "rescans": int(words[-1])}
 
 
 def kv_to_fp8(kv, *, n_kv=None, seq_lens=None, out=None):

@@ -25,7 +25,7 @@ HS_FLAG_BLOCK_SELECT = 8
 HS_FLAG_HEAD_UNION = 16
 
 EXPORTED = ("hs_workspace_size", "hs_full_attn_select", "hs_sparse_attn_reuse", "hs_decode_step",
-            "hs_kv_fp8_size", "hs_kv_fp8_convert",
+            "hs_kv_fp8_size", "hs_kv_fp8_convert", "hs_select_diagnostics", "hs_gather_probe", "hs_kv_bridge",
             "hs_timing_enable", "hs_timing_read", "hs_status_string", "hs_last_error", "hs_version")
 
 
@@ -75,6 +75,12 @@ def load() -> ctypes.CDLL:
     lib.hs_kv_fp8_size.restype = c_int32
     lib.hs_kv_fp8_convert.argtypes = [POINTER(HsShape), c_void_p, c_void_p, c_void_p, c_void_p]
     lib.hs_kv_fp8_convert.restype = c_int32
+    lib.hs_select_diagnostics.argtypes = [POINTER(HsShape), POINTER(c_size_t), POINTER(c_size_t), POINTER(c_size_t)]
+    lib.hs_select_diagnostics.restype = c_int32
+    lib.hs_kv_bridge.argtypes = [POINTER(HsShape), c_void_p, c_int32, c_void_p, c_void_p, c_void_p]
+    lib.hs_kv_bridge.restype = c_int32
+    lib.hs_gather_probe.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_void_p]
+    lib.hs_gather_probe.restype = c_int32
     lib.hs_status_string.argtypes = [c_int32]
     lib.hs_status_string.restype = ctypes.c_char_p
     lib.hs_last_error.argtypes = []

@@ -209,8 +209,8 @@ PrefillPlan plan_prefill(const hs_shape* s) {
   o = align_up(o + (size_t)p.rows * p.max_samples * 4);
   p.off_stat = o;
   o = align_up(o + 4);
-  p.off_defer = o;  // queued rows of the selection, then their count
-  o = align_up(o + (size_t)p.rows * 4 + 4);
+  p.off_defer = o;  // queued rows of the selection, then their count and the rescan count
+  o = align_up(o + (size_t)p.rows * 4 + 8);
   p.prob = (s->flags & HS_FLAG_PROB_SCORE) != 0;
   if (p.prob) {
     p.off_lse = o;
@@ -618,12 +618,29 @@ hs_status hs_full_attn_select(const hs_shape* s, const void* q, const void* kv, 
     sp.buf_sigma = pp.buf_sigma; sp.buf_j = pp.buf_j; sp.counts = pp.counts; sp.cap = plan.cap;
     sp.force_rescan = (s->flags & HS_FLAG_EXACT_RESCAN) ? 1 : 0;
     sp.idx = idx;
-    sp.rescan_count = nullptr;
+    sp.rescan_count = reinterpret_cast<uint32_t*>(w + plan.off_defer + (size_t)plan.rows * 4 + 4);
     sp.defer_rows = reinterpret_cast<int32_t*>(w + plan.off_defer);
     sp.defer_count = reinterpret_cast<uint32_t*>(w + plan.off_defer + (size_t)plan.rows * 4);
     sp.lse = prob ? lse_buf : nullptr;
     HIP_TRY(timed("select_prefill", hst, [&] { return hs::launch_select_prefill(sp, plan.rows, hst); }));
   }
+  return ok();
+}
+
+hs_status hs_select_diagnostics(const hs_shape* s, size_t* defer_rows_off, size_t* defer_count_off,
+                                size_t* rescan_count_off) {
+  Layout lay;
+  if (!defer_rows_off || !defer_count_off || !rescan_count_off)
+    return fail(HS_ERR_INVALID_ARG, "offset pointers must be non-NULL");
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  if (s->n_q < 1 || s->n_kv < s->n_q) return fail(HS_ERR_INVALID_ARG, "need 1 <= n_q <= n_kv");
+  if (s->top_k == 0 || (s->flags & (HS_FLAG_BLOCK_SELECT | HS_FLAG_HEAD_UNION)))
+    return fail(HS_ERR_UNSUPPORTED, "only the token-level selection of hs_full_attn_select keeps these records");
+  const PrefillPlan plan = plan_prefill(s);
+  *defer_rows_off = plan.off_defer;
+  *defer_count_off = plan.off_defer + (size_t)plan.rows * 4;
+  *rescan_count_off = plan.off_defer + (size_t)plan.rows * 4 + 4;
   return ok();
 }
 
@@ -699,7 +716,9 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   if (s->n_q != 1) return fail(HS_ERR_INVALID_ARG, "decode calls need n_q == 1 (got %d)", s->n_q);
   if (max_seq_len < 1 || max_seq_len > s->kv_capacity)
     return fail(HS_ERR_INVALID_ARG, "need 1 <= max_seq_len (%d) <= kv_capacity (%d)", max_seq_len, s->kv_capacity);
-  if (s->flags & HS_FLAG_FP8_KV) return fail(HS_ERR_UNSUPPORTED, "the FP8 cache copy serves hs_sparse_attn_reuse only");
+  const bool fp8 = (s->flags & HS_FLAG_FP8_KV) != 0;
+  if (fp8 && (s->flags & (HS_FLAG_PROB_SCORE | HS_FLAG_HEAD_UNION)))
+    return fail(HS_ERR_UNSUPPORTED, "the FP8 decode step takes the logit score (token or block level)");
   if (!q || !kv_new || !kv || !seq_lens || !o) return fail(HS_ERR_INVALID_ARG, "q, kv_new, kv, seq_lens and o must be non-NULL");
   if (s->top_k > 0 && !idx) return fail(HS_ERR_INVALID_ARG, "idx must be non-NULL when top_k > 0");
   if (!aligned16(q) || !aligned16(kv_new) || !aligned16(kv) || !aligned16(o))
@@ -712,14 +731,30 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   hipStream_t hst = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
 
-  hs::AppendParams ap{};
-  ap.kv_new = static_cast<const uint16_t*>(kv_new);
-  ap.kv = static_cast<uint16_t*>(kv);
-  ap.sb = lay.sb; ap.sh = lay.sh; ap.st = lay.st; ap.voff = lay.voff;
-  ap.seq_lens = seq_lens; ap.B = s->batch; ap.Hkv = s->kv_heads; ap.cap = max_seq_len;
-  HIP_TRY(timed("kv_append", hst, [&] { return hs::launch_append(ap, hst); }));
-
   hs::DecodeParams dp{};
+  if (fp8) {
+    // kv is the FP8 copy: the new token's rows are quantised with the stored
+    // scales of its KV head into slot seq_lens[b] - 1, and the layer reads
+    // codes (kv_new seen as a one-row cache: token stride 0)
+    hs::Fp8ConvertParams cp{};
+    cp.kv = hs::KvView{static_cast<const uint16_t*>(kv_new), (int64_t)s->kv_heads * 256, 256, 0, 128};
+    cp.kv8 = static_cast<uint8_t*>(kv);
+    cp.B = s->batch; cp.Hkv = s->kv_heads; cp.n_kv = 1; cp.cap = s->kv_capacity;
+    cp.seq_lens = seq_lens;
+    HIP_TRY(timed("kv_append", hst, [&] { return hs::launch_kv_convert_fp8(cp, hst); }));
+    dp.kv8 = static_cast<const uint8_t*>(kv);
+    dp.kv8_scale = reinterpret_cast<const float*>(dp.kv8 + hs::kv8_codes_bytes(s->batch, s->kv_heads, s->kv_capacity) +
+                                                  (size_t)s->batch * s->kv_heads * 8);
+    dp.kv8_cap = s->kv_capacity;
+  } else {
+    hs::AppendParams ap{};
+    ap.kv_new = static_cast<const uint16_t*>(kv_new);
+    ap.kv = static_cast<uint16_t*>(kv);
+    ap.sb = lay.sb; ap.sh = lay.sh; ap.st = lay.st; ap.voff = lay.voff;
+    ap.seq_lens = seq_lens; ap.B = s->batch; ap.Hkv = s->kv_heads; ap.cap = max_seq_len;
+    HIP_TRY(timed("kv_append", hst, [&] { return hs::launch_append(ap, hst); }));
+  }
+
   dp.q = static_cast<const uint16_t*>(q);
   dp.kv = kv_view(kv, lay);
   dp.B = s->batch; dp.n_q = 1; dp.n_kv = max_seq_len; dp.Hq = s->q_heads; dp.Hkv = s->kv_heads;
@@ -745,7 +780,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     hs::DecodeScoreParams zp{};
     zp.q = dp.q; zp.kv = dp.kv; zp.seq_lens = seq_lens; zp.lse = lse_buf;
     zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
-    zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window;
+    zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window; zp.max_len = max_seq_len;
     HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
   }
   if (plan.head_union) {
@@ -753,13 +788,13 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     hs::DecodeScoreParams zp{};
     zp.q = dp.q; zp.kv = dp.kv; zp.seq_lens = seq_lens; zp.lse = nullptr;
     zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
-    zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window;
+    zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window; zp.max_len = max_seq_len;
     zp.per_head = 1;
     HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
     int32_t* hidx = reinterpret_cast<int32_t*>(w + plan.off_hidx);
     hs::SelectDecodeParams sp{};
     sp.B = s->batch; sp.Hkv = s->q_heads; sp.top_k = s->top_k; sp.window = s->window;
-    sp.seq_lens = seq_lens; sp.sigma = sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = hidx;
+    sp.seq_lens = seq_lens; sp.max_len = max_seq_len; sp.sigma = sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = hidx;
     sp.nslices = plan.sel_slices;
     if (plan.sel_slices > 0) {
       sp.theta_key = reinterpret_cast<uint32_t*>(w + plan.off_theta);
@@ -770,26 +805,26 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     HIP_TRY(timed("select_decode", hst, [&] { return hs::launch_select_decode(sp, s->batch * s->q_heads, hst); }));
     hs::UnionParams un{};
     un.lists = hidx; un.row_stride = (int64_t)G * s->top_k; un.head_stride = s->top_k; un.G = G; un.k = s->top_k;
-    un.B = s->batch; un.n_q = 1; un.Hkv = s->kv_heads; un.window = s->window; un.seq_lens = seq_lens; un.out = idx;
+    un.B = s->batch; un.n_q = 1; un.Hkv = s->kv_heads; un.window = s->window; un.seq_lens = seq_lens; un.max_len = max_seq_len; un.out = idx;
     HIP_TRY(timed("head_union", hst, [&] { return hs::launch_head_union(un, (int64_t)s->batch * s->kv_heads, hst); }));
     return ok();
   }
   if (plan.block) {
     hs::BlockMaxParams mp{};
-    mp.sigma = sigma; mp.sigma_stride = plan.sigma_stride; mp.seq_lens = seq_lens;
+    mp.sigma = sigma; mp.sigma_stride = plan.sigma_stride; mp.seq_lens = seq_lens; mp.max_len = max_seq_len;
     mp.B = s->batch; mp.Hkv = s->kv_heads; mp.window = s->window;
     mp.blk_score = reinterpret_cast<float*>(w + plan.off_blk); mp.blk_stride = plan.blk_stride;
     HIP_TRY(timed("block_max", hst, [&] { return hs::launch_block_max(mp, hst); }));
     hs::BlockSelectParams bp{};
     bp.B = s->batch; bp.n_q = 1; bp.Hkv = s->kv_heads; bp.top_k = s->top_k; bp.window = s->window;
-    bp.seq_lens = seq_lens; bp.blk_score = mp.blk_score; bp.blk_stride = plan.blk_stride; bp.idx = idx;
+    bp.seq_lens = seq_lens; bp.max_len = max_seq_len; bp.blk_score = mp.blk_score; bp.blk_stride = plan.blk_stride; bp.idx = idx;
     HIP_TRY(timed("select_blocks", hst, [&] { return hs::launch_select_blocks(bp, (int64_t)s->batch * s->kv_heads, hst); }));
     return ok();
   }
   if (s->top_k > 0) {
     hs::SelectDecodeParams sp{};
     sp.B = s->batch; sp.Hkv = s->kv_heads; sp.top_k = s->top_k; sp.window = s->window;
-    sp.seq_lens = seq_lens; sp.sigma = sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = idx;
+    sp.seq_lens = seq_lens; sp.max_len = max_seq_len; sp.sigma = sigma; sp.sigma_stride = plan.sigma_stride; sp.idx = idx;
     sp.nslices = plan.sel_slices;
     if (plan.sel_slices > 0) {
       sp.theta_key = reinterpret_cast<uint32_t*>(w + plan.off_theta);
@@ -799,6 +834,48 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     }
     HIP_TRY(timed("select_decode", hst, [&] { return hs::launch_select_decode(sp, s->batch * s->kv_heads, hst); }));
   }
+  return ok();
+}
+
+hs_status hs_kv_bridge(const hs_shape* s, const void* hidden, int32_t d_model, const void* w_kv, void* kv,
+                       void* stream) {
+  Layout lay;
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  if (s->flags & HS_FLAG_FP8_KV) return fail(HS_ERR_UNSUPPORTED, "the bridge writes the bf16 cache");
+  if (s->n_q < 1 || s->n_kv < s->n_q || s->n_kv > s->kv_capacity)
+    return fail(HS_ERR_INVALID_ARG, "need 1 <= n_q (%d) <= n_kv (%d) <= kv_capacity (%d)", s->n_q, s->n_kv, s->kv_capacity);
+  if (d_model < 64 || d_model % 64 != 0 || d_model > 65536)
+    return fail(HS_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in [64, 65536] (got %d)", d_model);
+  if (!hidden || !w_kv || !kv) return fail(HS_ERR_INVALID_ARG, "hidden, w_kv and kv must be non-NULL");
+  if (!aligned16(hidden) || !aligned16(w_kv) || !aligned16(kv))
+    return fail(HS_ERR_INVALID_ARG, "hidden, w_kv and kv must be 16-byte aligned");
+  st = check_device();
+  if (st != HS_OK) return st;
+  hipStream_t hst = static_cast<hipStream_t>(stream);
+  hs::BridgeParams p{};
+  p.h = static_cast<const uint16_t*>(hidden);
+  p.w = static_cast<const uint16_t*>(w_kv);
+  p.kv = static_cast<uint16_t*>(kv);
+  p.sb = lay.sb; p.sh = lay.sh; p.st = lay.st; p.voff = lay.voff;
+  p.B = s->batch; p.n_q = s->n_q; p.n_kv = s->n_kv; p.Hkv = s->kv_heads; p.d_model = d_model;
+  HIP_TRY(timed("kv_bridge", hst, [&] { return hs::launch_kv_bridge(p, hst); }));
+  return ok();
+}
+
+hs_status hs_gather_probe(const void* src, int64_t src_rows, const int32_t* idx, int64_t n, int32_t per_wave,
+                          uint32_t* out, void* stream) {
+  if (!src || !idx || !out) return fail(HS_ERR_INVALID_ARG, "src, idx and out must be non-NULL");
+  if (!aligned16(src)) return fail(HS_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if (src_rows < 1 || src_rows > (int64_t)(0xffffffffu / 512u))
+    return fail(HS_ERR_INVALID_ARG, "src_rows must be in [1, 2^32 / 512)");
+  if (n < 1 || per_wave < 1 || per_wave > 2048)
+    return fail(HS_ERR_INVALID_ARG, "need n >= 1 and 1 <= per_wave <= 2048");
+  hs_status st = check_device();
+  if (st != HS_OK) return st;
+  hipStream_t hst = static_cast<hipStream_t>(stream);
+  hs::ProbeParams p{static_cast<const uint8_t*>(src), (uint32_t)(src_rows * 512), idx, n, per_wave, out};
+  HIP_TRY(timed("gather_probe", hst, [&] { return hs::launch_gather_probe(p, hst); }));
   return ok();
 }
 

@@ -130,8 +130,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
-constexpr int kDppRowRor4 = 0x124;    // lane i <- lane (i+4) mod 16 within 16
-constexpr int kDppRowRor8 = 0x128;    // lane i <- lane (i+8) mod 16 within 16
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8: lane i <-> lane i ^ 8 within 16
 
 // With NaN-free, non-IEEE-mode compilation (see the build flags) a DPP move
 // feeding a max folds into a single v_max_f32_dpp.
@@ -269,6 +268,14 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+// Decode length of sequence b as the kernels read it: seq_lens[b] clamped to
+// the host bound the launch was sized for, so that a caller's length beyond
+// that bound (an error, or a graph replayed past its bucket) yields a wrong
+// but in-bounds result rather than accesses past the workspace rows.
+__device__ __forceinline__ int dec_len(const int32_t* seq_lens, int b, int max_len) {
+  return imin(seq_lens[b], max_len);
+}
 
 // Cache addressing. One (b, g) slab spans fewer than 2^31 elements (checked
 // on the host), so rows inside a slab use 32-bit offsets from a 64-bit slab

@@ -69,9 +69,10 @@ struct ChunkT<true> {
 };
 
 // SIGMA (full rows only): also write the group score row of the candidates.
+// FP8: keys and values from the FP8 copy of the cache (sparse layers, and the
+// decode full layer).
 template <int G, bool SPARSE, bool SIGMA, bool FP8 = false>
 __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
-  static_assert(!FP8 || (SPARSE && !SIGMA), "the FP8 cache serves the sparse layers");
   using Chunk = ChunkT<FP8>;
   // Per-wave K tiles and key lists; in prefill SPARSE mode the block's
   // shared window tiles alias this region before the lists are built.
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   f32x4 oacc[8] = {};
   float m_run = kNegInf, l_part = 0.f;
   const float cexp = P.scale * kscale * kLog2e;
+  const float sig_scale = P.scale * kscale;  // exact product: kscale is a power of two
   const int cand_end = lim;  // last candidate position (FULL score row)
   // Score row: the group maxima of each chunk are staged in the wave's LDS
   // segment buffer and written out once the segment's gathers are done: a
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
     if constexpr (SIGMA) {
       f32x4 mxh;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * P.scale;
+      for (int i = 0; i < 4; ++i) mxh[i] = group_max<G>(acc[i]) * sig_scale;
       if (n == 0) *reinterpret_cast<f32x4*>(&sig_stage[v - sig_v0 + 4 * gq]) = mxh;
     }
     if constexpr (FP8) {
@@ -751,11 +753,68 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams P) 
   if (P.lse && tid == 0) P.lse[(int64_t)b * P.Hq + head] = M * kLn2 + __logf(l);
 }
 
+// Gather-rate probe (diagnostics): the memory access pattern of the sparse
+// layers without their arithmetic. Wave w stages its keys idx[w * per_wave
+// ..) in LDS as byte offsets (as the sparse kernel stages its compacted key
+// list), then walks them in 16-key chunks, three in flight; lane (n = l % 16,
+// gq = l / 16) loads 16 bytes of the K half and 16 bytes of the V half of
+// token rows 4gq..4gq+3 of a chunk (512-byte rows, K then V, as in the
+// default cache layout). The loaded words are folded into one value per lane
+// and stored, so no load is dead.
+constexpr int kProbeMaxKeys = 2048;
+__global__ __launch_bounds__(256) void gather_probe_kernel(ProbeParams P) {
+  __shared__ uint32_t offs[4][kProbeMaxKeys];
+  const int lane = threadIdx.x & 63, n = lane & 15, gq = lane >> 4;
+  const int wv = threadIdx.x >> 6;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t k0 = wave * P.per_wave;
+  if (k0 >= P.n) return;
+  const int nk = (int)(P.n - k0 < P.per_wave ? P.n - k0 : P.per_wave);
+  uint32_t* lst = offs[wv];
+  for (int i = lane; i < nk; i += 64) lst[i] = (uint32_t)P.idx[k0 + i] * 512u;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): one wave, LDS operations in order
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(P.src, P.src_bytes);  // reads past the buffer return 0
+  uint32_t acc = 0;
+  auto issue = [&](u32x4* kw, u32x4* vw, int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t off = lst[imin(16 * c + 4 * gq + r, nk - 1)] + 16u * (uint32_t)n;
+      kw[r] = buf_ld16(rs, off);
+      vw[r] = buf_ld16(rs, off + 256u);
+    }
+  };
+  auto fold = [&](const u32x4* kw, const u32x4* vw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc += (kw[r][0] ^ kw[r][1] ^ kw[r][2] ^ kw[r][3]) + (vw[r][0] ^ vw[r][3]);
+  };
+  const int nch = (nk + 15) / 16;
+  u32x4 ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
+  issue(ka, va, 0);
+  if (nch > 1) issue(kb, vb, 1);
+  int c = 0;
+#pragma unroll 1
+  for (; c + 2 < nch; c += 3) {
+    issue(kc, vc, c + 2);
+    fold(ka, va);
+    if (c + 3 < nch) issue(ka, va, c + 3);
+    fold(kb, vb);
+    if (c + 4 < nch) issue(kb, vb, c + 4);
+    fold(kc, vc);
+  }
+  if (c < nch) fold(ka, va);
+  if (c + 1 < nch) fold(kb, vb);
+  P.out[wave * 64 + lane] = acc;
+}
+
 template <int G, bool SPARSE>
 hipError_t launch_gather_g(const DecodeParams& p, hipStream_t s) {
   const int64_t blocks = p.seq_lens ? ((int64_t)p.B * p.Hkv * p.splits + 3) / 4
                                     : (((int64_t)p.B * p.n_q + 3) / 4) * p.Hkv;
-  if (!SPARSE && p.sigma)
+  if (!SPARSE && p.kv8 && p.sigma)
+    flash_gather_kernel<G, false, true, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  else if (!SPARSE && p.kv8)
+    flash_gather_kernel<G, false, false, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  else if (!SPARSE && p.sigma)
     flash_gather_kernel<G, false, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
   else if (SPARSE && p.kv8)
     flash_gather_kernel<G, true, false, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
@@ -801,6 +860,12 @@ hipError_t launch_kv_convert_fp8(const Fp8ConvertParams& p, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   fp8_convert_kernel<<<grid, dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_probe(const ProbeParams& p, hipStream_t s) {
+  const int64_t waves = (p.n + p.per_wave - 1) / p.per_wave;
+  gather_probe_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }
 

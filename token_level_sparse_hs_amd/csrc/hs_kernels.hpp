@@ -71,7 +71,8 @@ struct SelectParams {
 
 struct ThresholdParams {
   int B, n_q, n_kv, Hkv, top_k, window, cap, stride, max_samples;
-  uint32_t* defer_count;  // zeroed here (block 0) for the selection that follows
+  uint32_t* defer_count;  // [2]: queued rows, rescanned rows; zeroed here (block 0)
+                          // for the selection that follows
   const float* samples;
   float* theta;
 };
@@ -79,6 +80,7 @@ struct ThresholdParams {
 struct SelectDecodeParams {
   int B, Hkv, top_k, window;
   const int32_t* seq_lens;
+  int max_len;         // host bound on seq_lens (longer lengths are read as max_len)
   const float* sigma;  // [B*Hkv][sigma_stride]
   int64_t sigma_stride;
   int32_t* idx;        // [B][Hkv][top_k]
@@ -110,6 +112,7 @@ struct DecodeScoreParams {
   float* sigma;       // [B*Hkv][sigma_stride]
   int64_t sigma_stride;
   int max_cand;       // bound on |C(p)| over the batch (grid size)
+  int max_len;        // host bound on seq_lens (longer lengths are read as max_len)
   int per_head;       // 1: each head's scaled logit into row b*Hq + h (lse unused)
 };
 hipError_t launch_decode_prob_score(const DecodeScoreParams& p, hipStream_t s);
@@ -123,6 +126,7 @@ struct UnionParams {
   int G, k;
   int B, n_q, n_kv, Hkv, window;
   const int32_t* seq_lens;  // decode rows; null for prefill rows
+  int max_len;              // decode rows: host bound on seq_lens
   int32_t* out;
 };
 hipError_t launch_head_union(const UnionParams& p, int64_t rows, hipStream_t s);
@@ -138,6 +142,7 @@ hipError_t launch_lse_scatter(const float* src, float* dst, int B, int Hkv, int 
 struct BlockSelectParams {
   int B, n_q, n_kv, Hkv, top_k, window;
   const int32_t* seq_lens;  // decode rows; null for prefill rows
+  int max_len;              // decode rows: host bound on seq_lens
   const float* blk_score;   // [rows][blk_stride]
   int blk_stride;
   int32_t* idx;             // [rows][top_k]
@@ -148,6 +153,7 @@ struct BlockMaxParams {
   const float* sigma;
   int64_t sigma_stride;
   const int32_t* seq_lens;
+  int max_len;  // host bound on seq_lens
   int B, Hkv, window;
   float* blk_score;
   int blk_stride;
@@ -227,6 +233,29 @@ struct CombineParams {
   int window;
   int max_len;   // host bound on seq_lens
 };
+
+// KV Bridging: rows [n_kv - n_q, n_kv) of every (b, g) of the cache from
+// hidden states h [B][n_q][d_model] and weights w [Hkv][2][128][d_model].
+struct BridgeParams {
+  const uint16_t* h;
+  const uint16_t* w;
+  uint16_t* kv;
+  int64_t sb, sh, st, voff;  // cache strides (elements)
+  int B, n_q, n_kv, Hkv, d_model;
+};
+hipError_t launch_kv_bridge(const BridgeParams& p, hipStream_t s);
+
+// Gather-rate probe: 512-byte token rows of src at the indices idx[0..n),
+// per_wave keys per wave; out gets one folded word per lane.
+struct ProbeParams {
+  const uint8_t* src;
+  uint32_t src_bytes;
+  const int32_t* idx;
+  int64_t n;
+  int per_wave;
+  uint32_t* out;  // [waves * 64]
+};
+hipError_t launch_gather_probe(const ProbeParams& p, hipStream_t s);
 
 hipError_t launch_decode_full(const DecodeParams& p, hipStream_t s);
 hipError_t launch_sparse(const DecodeParams& p, hipStream_t s);

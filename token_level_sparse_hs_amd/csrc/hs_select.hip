@@ -662,7 +662,7 @@ __global__ __launch_bounds__(kSelThreads) void select_prefill_deferred_kernel(Se
 __global__ __launch_bounds__(kSelThreads) void threshold_kernel(ThresholdParams P) {
   __shared__ SelShared sh;
   const int64_t row = blockIdx.x;
-  if (row == 0 && threadIdx.x == 0 && P.defer_count) *P.defer_count = 0u;
+  if (row == 0 && threadIdx.x == 0 && P.defer_count) P.defer_count[0] = P.defer_count[1] = 0u;
   const int64_t bt = row / P.Hkv;
   const int t = (int)(bt % P.n_q);
   const int p = P.n_kv - P.n_q + t;
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(256, 2) void threshold_wave_kernel(ThresholdParams 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = uniform((int)blockIdx.x * 4 + wave);  // rows < 2^31
   if (row >= rows) return;
-  if (row == 0 && lane == 0 && P.defer_count) *P.defer_count = 0u;
+  if (row == 0 && lane == 0 && P.defer_count) P.defer_count[0] = P.defer_count[1] = 0u;
   const int64_t bt = row / P.Hkv;
   const int t = (int)(bt % P.n_q);
   const int p = P.n_kv - P.n_q + t;
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecode
   __shared__ SelLds<true> lds;
   const int row = blockIdx.x;  // b * Hkv + g
   const int b = row / P.Hkv;
-  const int p = P.seq_lens[b] - 1;
+  const int p = dec_len(P.seq_lens, b, P.max_len) - 1;
   const int ncand = imax(0, p - P.window + 1);
   int32_t* out = P.idx + (int64_t)row * P.top_k;
   if (ncand <= P.top_k) {
@@ -793,7 +793,7 @@ struct DecRow {
 };
 __device__ __forceinline__ DecRow dec_row(const SelectDecodeParams& P, int row) {
   const int b = row / P.Hkv;
-  const int p = P.seq_lens[b] - 1;
+  const int p = dec_len(P.seq_lens, b, P.max_len) - 1;
   return DecRow{imax(0, p - P.window + 1), P.sigma + (int64_t)row * P.sigma_stride};
 }
 
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(256) void decode_prob_score_kernel(DecodeScoreParam
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.y;  // b * Hkv + g
   const int b = row / P.Hkv, g = row % P.Hkv;
-  const int ncand = imax(0, P.seq_lens[b] - P.window);  // p - W + 1 with p = seq_len - 1
+  const int ncand = imax(0, dec_len(P.seq_lens, b, P.max_len) - P.window);  // p - W + 1 with p = seq_len - 1
   const int j0 = ((int)blockIdx.x * 4 + wave) * kDecScoreWaveKeys;
   if (j0 >= ncand) return;
   const int col = lane & 15, kg = lane >> 4;
@@ -1028,7 +1028,7 @@ struct BlockRow {
 __device__ __forceinline__ BlockRow block_row(const BlockSelectParams& P, int64_t row) {
   int p;
   if (P.seq_lens) {
-    p = P.seq_lens[row / P.Hkv] - 1;
+    p = dec_len(P.seq_lens, (int)(row / P.Hkv), P.max_len) - 1;
   } else {
     const int t = (int)((row / P.Hkv) % P.n_q);
     p = P.n_kv - P.n_q + t;
@@ -1126,7 +1126,7 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks_kernel(BlockSelectP
 __global__ __launch_bounds__(256) void block_max_kernel(BlockMaxParams P) {
   const int row = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncand = imax(0, P.seq_lens[row / P.Hkv] - P.window);
+  const int ncand = imax(0, dec_len(P.seq_lens, row / P.Hkv, P.max_len) - P.window);
   const int blk0 = blockIdx.x * 64 + wave * 16;  // first of the wave's 16 blocks
   if (blk0 * 64 >= ncand) return;
   const float* s = P.sigma + (int64_t)row * P.sigma_stride;
@@ -1163,7 +1163,7 @@ __global__ __launch_bounds__(kSelThreads) void head_union_kernel(UnionParams P) 
   const int64_t row = blockIdx.x;
   int p;
   if (P.seq_lens) {
-    p = P.seq_lens[row / P.Hkv] - 1;
+    p = dec_len(P.seq_lens, (int)(row / P.Hkv), P.max_len) - 1;
   } else {
     p = P.n_kv - P.n_q + (int)((row / P.Hkv) % P.n_q);
   }

@@ -49,7 +49,7 @@ class DecodeStepGraph:
     """
 
     def __init__(self, kv, *, batch, q_heads, sparse_layers, top_k, window, scale=0.0, with_lse=True, flags=0,
-                 kv_fp8=None):
+                 kv_fp8=None, fp8_full_layer=False):
         if not isinstance(kv, torch.Tensor) or kv.dim() != 5:
             raise ValueError("kv must be the [B][Hkv][capacity][2][128] cache tensor")
         self.kv = kv
@@ -61,14 +61,18 @@ class DecodeStepGraph:
         self.top_k, self.window, self.scale, self.with_lse = top_k, window, scale, with_lse
         # options: selection flags of the full layer; an FP8 copy of the cache
         # (from kv_to_fp8) that the step refreshes at the appended row and the
-        # sparse layers gather from
-        self.flags, self.kv_fp8 = flags, kv_fp8
+        # sparse layers gather from; with fp8_full_layer the full layer also
+        # reads the copy (and appends to it; the bf16 cache is then untouched)
+        if fp8_full_layer and kv_fp8 is None:
+            raise ValueError("fp8_full_layer needs the FP8 copy kv_fp8")
+        self.flags, self.kv_fp8, self.fp8_full_layer = flags, kv_fp8, fp8_full_layer
         self.q = torch.zeros((B, q_heads, 128), dtype=torch.bfloat16, device=dev)
         self.kv_new = torch.zeros((B, Hkv, 2, 128), dtype=torch.bfloat16, device=dev)
         self.q_sparse = [torch.zeros_like(self.q) for _ in range(sparse_layers)]
         self.seq_lens = torch.ones((B,), dtype=torch.int32, device=dev)
         shape = make_shape(batch=B, n_q=1, n_kv=0, kv_capacity=cap, q_heads=q_heads, kv_heads=Hkv,
-                           top_k=top_k, window=window, scale=scale, flags=flags)
+                           top_k=top_k, window=window, scale=scale,
+                           flags=flags | (_lib.HS_FLAG_FP8_KV if fp8_full_layer else 0))
         self.ws_sparse = _lib.alloc_workspace(_lib.workspace_size(_lib.HS_OP_SPARSE_ATTN_REUSE, shape, 1), dev)
         self._shape = shape
         self.graph = None
@@ -83,8 +87,9 @@ class DecodeStepGraph:
         with torch.cuda.graph(g):
             o, lse, idx = decode_step(self.q, self.kv_new, self.kv, self.seq_lens, bound, top_k=self.top_k,
                                       window=self.window, scale=self.scale, with_lse=self.with_lse,
-                                      flags=self.flags, workspace=ws_full)
-            if self.kv_fp8 is not None:
+                                      flags=self.flags, workspace=ws_full,
+                                      kv_fp8=self.kv_fp8 if self.fp8_full_layer else None)
+            if self.kv_fp8 is not None and not self.fp8_full_layer:
                 kv_to_fp8(self.kv, seq_lens=self.seq_lens, out=self.kv_fp8)
             o_sp = [sparse_attn_reuse(x, self.kv, idx, top_k=self.top_k, window=self.window, scale=self.scale,
                                       seq_lens=self.seq_lens, workspace=self.ws_sparse, kv_fp8=self.kv_fp8,
