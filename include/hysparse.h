@@ -278,6 +278,26 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new,
 hs_status hs_kv_bridge(const hs_shape* s, const void* hidden, int32_t d_model,
                        const void* w_kv, void* kv, void* stream);
 
+/* hs_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory or manage a workspace (code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation): identical
+ * arguments and results except ws, which is the library's own scratch, a
+ * static device array of 64 MiB per GPU (held from the library's first use
+ * on that GPU until the process ends). Calls whose step needs more scratch
+ * than that (hs_workspace_size(HS_OP_DECODE_STEP, s, max_seq_len) > 64 MiB;
+ * e.g. a single sequence of up to about a million tokens fits, 64
+ * sequences of 256K tokens do not) fail with HS_ERR_WORKSPACE before
+ * anything is enqueued. The call allocates nothing; its first call on a
+ * device looks up the scratch address there. Every call on one GPU shares
+ * that GPU's scratch, which keeps the last call's contents (the step needs
+ * none of it cleared): calls that may overlap on one GPU (other streams, or
+ * other threads) race and must be serialised by the caller. */
+hs_status hs_decode_step_noalloc(const hs_shape* s, const void* q,
+                                 const void* kv_new, void* kv,
+                                 const int32_t* seq_lens, int32_t max_seq_len,
+                                 void* o, float* lse, int32_t* idx,
+                                 void* stream);
+
 /* Diagnostics: per-kernel timing. While enabled (on != 0), every kernel the
  * library launches is bracketed by a pair of HIP events recorded on the
  * call's stream, so durations are those of the kernels themselves on the

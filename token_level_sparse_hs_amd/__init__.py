@@ -23,7 +23,7 @@ from ._lib import (HS_FLAG_BLOCK_SELECT, HS_FLAG_EXACT_RESCAN, HS_FLAG_FP8_KV, H
 
 __all__ = ["full_attn_select", "sparse_attn_reuse", "decode_step", "make_shape", "HsError",
            "HS_FLAG_EXACT_RESCAN", "HS_FLAG_PROB_SCORE", "HS_FLAG_FP8_KV", "HS_FLAG_BLOCK_SELECT", "HS_FLAG_HEAD_UNION", "kv_to_fp8", "version",
-           "select_diagnostics", "kv_bridge"]
+           "select_diagnostics", "kv_bridge", "decode_step_noalloc"]
 
 
 def version() -> int:
@@ -163,6 +163,33 @@ def decode_step(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.
                                   _lib.ptr(seq_lens), max_seq_len, _lib.ptr(o), _lib.ptr(lse),
                                   _lib.ptr(idx) if top_k > 0 else None, _lib.ptr(ws),
                                   0 if ws is None else ws.numel(), _lib.stream_handle(dev)))
+    return o, lse, idx
+
+
+def decode_step_noalloc(q, kv_new, kv, seq_lens, max_seq_len, *, top_k, window, scale=0.0, with_lse=True, flags=0,
+                        kv_fp8=None):
+    """decode_step with the library's own static scratch instead of a
+    workspace (include/hysparse.h, hs_decode_step_noalloc): no device memory
+    is allocated for the step itself (outputs excepted). Steps that need more
+    than the 64 MiB scratch raise HsError (HS_ERR_WORKSPACE)."""
+    _check_bf16("q", q, 3)
+    _check_bf16("kv_new", kv_new, 4)
+    B, Hq, d = q.shape
+    kv_heads, kv_capacity = _kv_dims(kv, None)
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda:
+        raise TypeError("seq_lens must be an int32 device tensor")
+    if kv_fp8 is not None:
+        flags |= _lib.HS_FLAG_FP8_KV
+    shape = make_shape(batch=B, n_q=1, n_kv=0, kv_capacity=kv_capacity, q_heads=Hq, kv_heads=kv_heads,
+                       top_k=top_k, window=window, scale=scale, flags=flags, head_dim=d)
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if with_lse else None
+    idx = torch.empty((B, kv_heads, _idx_row(flags, top_k, Hq, kv_heads)), dtype=torch.int32, device=dev)
+    _lib.check(_lib.load().hs_decode_step_noalloc(ctypes.byref(shape), _lib.ptr(q), _lib.ptr(kv_new),
+                                                  _lib.ptr(kv if kv_fp8 is None else kv_fp8), _lib.ptr(seq_lens),
+                                                  max_seq_len, _lib.ptr(o), _lib.ptr(lse),
+                                                  _lib.ptr(idx) if top_k > 0 else None, _lib.stream_handle(dev)))
     return o, lse, idx
 
 

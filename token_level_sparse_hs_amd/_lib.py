@@ -25,7 +25,7 @@ HS_FLAG_BLOCK_SELECT = 8
 HS_FLAG_HEAD_UNION = 16
 
 EXPORTED = ("hs_workspace_size", "hs_full_attn_select", "hs_sparse_attn_reuse", "hs_decode_step",
-            "hs_kv_fp8_size", "hs_kv_fp8_convert", "hs_select_diagnostics", "hs_gather_probe", "hs_kv_bridge",
+            "hs_kv_fp8_size", "hs_kv_fp8_convert", "hs_select_diagnostics", "hs_gather_probe", "hs_kv_bridge", "hs_decode_step_noalloc",
             "hs_timing_enable", "hs_timing_read", "hs_status_string", "hs_last_error", "hs_version")
 
 
@@ -71,6 +71,9 @@ def load() -> ctypes.CDLL:
     lib.hs_decode_step.argtypes = [POINTER(HsShape), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.hs_decode_step.restype = c_int32
+    lib.hs_decode_step_noalloc.argtypes = [POINTER(HsShape), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                           c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.hs_decode_step_noalloc.restype = c_int32
     lib.hs_kv_fp8_size.argtypes = [POINTER(HsShape), POINTER(c_size_t)]
     lib.hs_kv_fp8_size.restype = c_int32
     lib.hs_kv_fp8_convert.argtypes = [POINTER(HsShape), c_void_p, c_void_p, c_void_p, c_void_p]

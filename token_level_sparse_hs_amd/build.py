@@ -11,7 +11,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["hs_api.cpp", "hs_prefill.hip", "hs_select.hip", "hs_decode.hip", "hs_bridge.hip"]
+SOURCES = ["hs_api.cpp", "hs_prefill.hip", "hs_select.hip", "hs_decode.hip", "hs_bridge.hip", "hs_static.hip"]
 LIB = os.path.join(PKG, "libhysparse.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

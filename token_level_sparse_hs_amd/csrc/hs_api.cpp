@@ -707,6 +707,26 @@ hs_status hs_sparse_attn_reuse(const hs_shape* s_in, const void* q, const void* 
   return ok();
 }
 
+hs_status hs_decode_step_noalloc(const hs_shape* s, const void* q, const void* kv_new, void* kv,
+                                 const int32_t* seq_lens, int32_t max_seq_len, void* o, float* lse, int32_t* idx,
+                                 void* stream) {
+  Layout lay;
+  hs_status st = validate_common(s, &lay);
+  if (st != HS_OK) return st;
+  if (max_seq_len < 1 || max_seq_len > s->kv_capacity)
+    return fail(HS_ERR_INVALID_ARG, "need 1 <= max_seq_len (%d) <= kv_capacity (%d)", max_seq_len, s->kv_capacity);
+  const size_t need = plan_decode_full(s, max_seq_len).total;
+  if (need > hs::kStaticScratchBytes)
+    return fail(HS_ERR_WORKSPACE, "this step needs %zu bytes of scratch; the library's static scratch holds %zu "
+                "(use hs_decode_step with a caller workspace)", need, hs::kStaticScratchBytes);
+  st = check_device();
+  if (st != HS_OK) return st;
+  void* scratch = nullptr;
+  HIP_TRY(hs::static_scratch(&scratch));
+  return hs_decode_step(s, q, kv_new, kv, seq_lens, max_seq_len, o, lse, idx, scratch, hs::kStaticScratchBytes,
+                        stream);
+}
+
 hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, void* kv, const int32_t* seq_lens,
                          int32_t max_seq_len, void* o, float* lse, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream) {

@@ -9,6 +9,11 @@
 namespace hs {
 
 constexpr int kMaxTopK = 8192;   // largest supported top_k
+
+// Library-owned device scratch of hs_decode_step_noalloc: one array per GPU
+// (a file-scope __device__ array), its address looked up once per device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void** ptr);
 constexpr int kPrefillKeyTile = 64;
 
 // ----------------------------------------------------------- prefill attention
