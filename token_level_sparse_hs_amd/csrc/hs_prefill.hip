@@ -75,29 +75,18 @@ __device__ __forceinline__ void qk_tile(const uint16_t* Ks, const bf16x8* qb, f3
 }
 
 // MFMA row n (= lane % 32) of a wave stands for token tok_of(n) of the
-// wave's 32/G tokens and head g*G + head_of(n). Within each 16-lane row the
-// head index sits on the lane bits of kHeadBits (bits 3, 1, 0 as G grows:
-// the lane pairs i^8, i^2, i^1 that full-row DPP patterns reach in both
-// directions) and the token on the remaining bits, so the group maximum over
-// heads runs as DPP steps within rows.
-template <int G>
-constexpr int kHeadBits = G >= 8 ? 0xB : G == 4 ? 0xA : G == 2 ? 0x8 : 0x0;
+// wave's 32/G tokens and head g*G + head_of(n). Each 16-lane row of the wave
+// holds 16/G tokens, and a token's G heads sit 16/G lanes apart inside one
+// row, so the group maximum runs on DPP within rows.
 template <int G>
 __device__ __forceinline__ int tok_of(int n) {
   constexpr int TR = 16 / (G > 16 ? 16 : G);
-  int t = 0, k = 0;
-#pragma unroll
-  for (int bit = 0; bit < 4; ++bit)
-    if (!((kHeadBits<G> >> bit) & 1)) t |= ((n >> bit) & 1) << k++;
-  return (n >> 4) * TR + t;
+  return (n >> 4) * TR + (n & 15) % TR;
 }
 template <int G>
 __device__ __forceinline__ int head_of(int n) {
-  int hd = 0, k = 0;
-#pragma unroll
-  for (int bit = 0; bit < 4; ++bit)
-    if ((kHeadBits<G> >> bit) & 1) hd |= ((n >> bit) & 1) << k++;
-  return hd;
+  constexpr int TR = 16 / (G > 16 ? 16 : G);
+  return (n & 15) / TR;
 }
 
 // Loads this lane's query operand: row n = l%32 of the wave (token
@@ -113,17 +102,46 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int b, int n_q, int Hq
   for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(ok ? ld16(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u});
 }
 
+// dst = max(src[partner], src) in the lanes of the DPP banks (4-lane groups
+// of a row) named by BANKS; the other lanes of dst keep their value. Row
+// rotations: ror:8 pairs lane i with i^8; ror:4 feeds lane i from i-4,
+// ror:12 from i+4. The first form defines dst, the second updates it.
+// One bank-masked v_max_f32_dpp per value and half-row: the compiler's DPP
+// builtins cannot keep the other lanes of dst without a copy of it (three
+// instructions per value instead of two; measured 5% slower on this kernel).
+// Wait states the compiler cannot see here are placed by hand:
+//  * matrix results: every caller settles the accumulators first
+//    (mfma_settle, the count the CDNA4 rules give for these instructions);
+//  * a DPP read needs two wait states after a vector write of its source:
+//    scores rewritten by vector code (the causal mask, the probability
+//    score's rescaling) are followed by a two-state pause tied to them, the
+//    statements below read r and r2 at least eight instructions after
+//    writing them (volatile asm keeps their order; the compiler can only add
+//    instructions between them), and `dep` orders the first read after the
+//    caller's last use of the scores.
+#define HS_DPP_MAX_DEF(dst, src, ROR, BANKS, dep)                                                        \
+  asm volatile("v_max_f32_dpp %0, %1, %1 row_ror:" #ROR " row_mask:0xf bank_mask:" #BANKS : "=v"(dst) \
+               : "v"(src), "v"(dep))
+#define HS_DPP_MAX_UPD(dst, src, ROR, BANKS, dep)                                                        \
+  asm volatile("v_max_f32_dpp %0, %1, %1 row_ror:" #ROR " row_mask:0xf bank_mask:" #BANKS : "+v"(dst) \
+               : "v"(src), "v"(dep))
+
+// The group maximum reads the scores through DPP from inline assembly, so
+// the compiler does not insert the two wait states a DPP read needs after a
+// vector write of its source: callers that have just rewritten the scores
+// with vector code pause here first.
+__device__ __forceinline__ void dpp_read_pause(f32x16& a, f32x16& b) { asm volatile("s_nop 1" : "+v"(a), "+v"(b)); }
+
 // Writes the group-max scores of the wave's tile into sig[TPW][64] (raw,
 // unscaled). acc[c][i] holds key 32c + 8(i/4) + 4h + i%4 of MFMA row n.
-// Transposing steps halve the values each lane carries instead of reducing
-// all 32 in every lane: across lane^8, lanes with bit 3 clear keep the keys
-// of acc[0] and the others those of acc[1]; across lane^2, lanes with bit 1
-// clear keep i < 8 and the others i >= 8; then (G = 8) a plain step across
-// lane^1. A transposing step is one select per kept value, one for the value
-// handed over, and one v_max_f32_dpp. The DPP reads are compiler builtins,
-// so the compiler orders them after the vector writes they depend on.
+// Transposing steps halve the values each lane carries instead of
+// reducing all 32 in every lane: across lane^8 (banks 0-1 keep the keys of
+// acc[0], banks 2-3 those of acc[1]), then across lane^4 (even banks keep
+// i < 8, odd banks i >= 8), then a plain step across lane^2 for G = 8. `dep`
+// is any value computed after the last use of acc by ordinary code (the
+// DPP sources must not be read before the matrix results have landed).
 template <int G>
-__device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig) {
+__device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig, float dep) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, q = lane & 15;
   if constexpr (G == 1) {
@@ -135,37 +153,36 @@ __device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig) {
         *reinterpret_cast<f32x4*>(row + 32 * c + 8 * q4 + 4 * h) =
             f32x4{acc[c][4 * q4], acc[c][4 * q4 + 1], acc[c][4 * q4 + 2], acc[c][4 * q4 + 3]};
   } else {
-    const bool b3 = (q & 8) != 0;
+    const int c = (q >> 3) & 1;
     float r[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float own = b3 ? acc[1][i] : acc[0][i];
-      const float give = b3 ? acc[0][i] : acc[1][i];
-      r[i] = fmaxf(own, dpp<kDppRowRor8>(give));
+      HS_DPP_MAX_DEF(r[i], acc[1][i], 8, 0xc, dep);
+      HS_DPP_MAX_UPD(r[i], acc[0][i], 8, 0x3, dep);
     }
-    float* trow = sig + tok_of<G>(lane & 31) * 64 + 32 * (b3 ? 1 : 0) + 4 * h;
+    float* trow = sig + tok_of<G>(lane & 31) * 64 + 32 * c + 4 * h;
     if constexpr (G == 2) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<f32x4*>(trow + 8 * q4) = f32x4{r[4 * q4], r[4 * q4 + 1], r[4 * q4 + 2], r[4 * q4 + 3]};
     } else {
-      const bool b1 = (q & 2) != 0;
+      const int ih = (q >> 2) & 1;
       float r2[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float own = b1 ? r[8 + i] : r[i];
-        const float give = b1 ? r[i] : r[8 + i];
-        r2[i] = fmaxf(own, dpp<kDppXor2>(give));
+        HS_DPP_MAX_DEF(r2[i], r[8 + i], 4, 0xa, dep);
+        HS_DPP_MAX_UPD(r2[i], r[i], 12, 0x5, dep);
       }
-      if constexpr (G == 8) {
+      if constexpr (G == 8) {  // in order after every write of r2 above (8+ statements back)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r2[i] = fmaxf(r2[i], dpp<kDppXor1>(r2[i]));
+        for (int i = 0; i < 8; ++i)
+          asm volatile("v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(r2[i]));
       }
       f32x4 v0 = {r2[0], r2[1], r2[2], r2[3]}, v1 = {r2[4], r2[5], r2[6], r2[7]};
       asm volatile("" : "+v"(v0), "+v"(v1));  // computed by all lanes before the writer branch
-      if (G == 4 || (q & 1) == 0) {
-        *reinterpret_cast<f32x4*>(trow + 16 * (b1 ? 1 : 0)) = v0;
-        *reinterpret_cast<f32x4*>(trow + 16 * (b1 ? 1 : 0) + 8) = v1;
+      if (G == 4 || (q & 2) == 0) {
+        *reinterpret_cast<f32x4*>(trow + 16 * ih) = v0;
+        *reinterpret_cast<f32x4*>(trow + 16 * ih + 8) = v1;
       }
     }
   }
@@ -335,6 +352,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           const int j = key0 + 32 * c + 8 * (i >> 2) + 4 * h + (i & 3);
           if (j > p_lane) acc[c][i] = kNegInf;
         }
+      // the group maximum reads the masked scores through DPP from inline
+      // assembly: two wait states after their vector writes
+      asm volatile("s_nop 1" : "+v"(acc[0]), "+v"(acc[1]));
     }
     // online softmax (exp2 domain); O is rescaled only when some row's
     // running maximum moved
@@ -345,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[c][i]);
     // Selection, part 1: the group maxima of the tile's candidate keys go
     // to the wave's LDS rows now, while the raw scores are still in place.
-    if (sel_tile) stage_group_max<G>(acc, sig[wave]);
+    if (sel_tile) stage_group_max<G>(acc, sig[wave], mx);
     mx = xor32_max(mx);
     // deferred rescaling (see the gather kernel): P <= 2^kRescaleLog2
     const float m_cand = mx * cexp;
@@ -530,9 +550,10 @@ __global__ __launch_bounds__(256, 2) void sample_scores_kernel(SampleParams P) {
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(acc[c][i], P.scale, -lse_col);
+        dpp_read_pause(acc[0], acc[1]);
       }
       float* ws = sig[wave];
-      stage_group_max<G>(acc, ws);
+      stage_group_max<G>(acc, ws, fmaxf(acc[0][15], acc[1][15]));
       lds_wait();
       const int s = s0 + lane;
 #pragma unroll
@@ -632,8 +653,9 @@ __global__ __launch_bounds__(256, 2) void score_pass_kernel(PrefillParams P) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(acc[c][i], P.scale, -lse_col);
+      dpp_read_pause(acc[0], acc[1]);
       float* ws = sig[wave];
-      stage_group_max<G>(acc, ws);
+      stage_group_max<G>(acc, ws, fmaxf(acc[0][15], acc[1][15]));
       lds_wait();
       const int j = key0 + lane;
 #pragma unroll
