@@ -234,7 +234,7 @@ def timed_steps(c, fn, steps, warmup, label):
 
 
 PREFILL_KERNELS = ("prefill_attn", "sample_scores", "threshold", "select_prefill", "sparse_prefill", "score_pass",
-                   "select_blocks", "head_slice", "head_union", "lse_scatter")
+                   "select_blocks", "head_slice", "head_union", "lse_scatter", "kv_bridge")
 
 
 # ---------------------------------------------------------------- headline
@@ -456,6 +456,16 @@ def decode_options(c, w, kv, lengths, dec, st):
     _, kt = timed_steps(c, fp8_sparse, 2, 1, f"{w.name} option fp8 sparse layers")
     out["fp8_sparse_layer_us"] = round(avg_us(kt, "sparse_decode"), 2)
     out["fp8_append_conversion_us"] = round(avg_us(kt, "kv_fp8_convert"), 2)
+
+    # the full layer reading the FP8 copy too (appending the token to it)
+    def fp8_full():
+        hs.decode_step(st["q_full"], st["kv_new"], kv, seq0, bound, top_k=w.top_k, window=w.window,
+                       workspace=dec.ws_full, kv_fp8=copy)
+    _, kt = timed_steps(c, fp8_full, 2, 1, f"{w.name} option fp8 full layer")
+    fp8_bytes = sum(256.0 * w.Hkv * (L + 1) for L in lengths)
+    out["fp8_full_layer_us"] = round(avg_us(kt, "decode_full"), 2)
+    out["fp8_full_layer_roofline"] = hbm_roof(fp8_bytes, avg_us(kt, "decode_full"))
+    out["fp8_full_layer_step_kernels_us"] = round(sum(t / n * 1e3 for n, t in kt.values()), 2)
     for flag, key, kernels in ((hs.HS_FLAG_BLOCK_SELECT, "block_select_us", ("block_max", "select_blocks")),
                                (hs.HS_FLAG_HEAD_UNION, "head_union_select_us",
                                 ("decode_score", "select_decode", "head_union"))):
@@ -492,6 +502,40 @@ def graph_ctx1m(c, pre, dec):
     us = (time.perf_counter() - t0) * 1e6 / w.decode_steps
     log(f"[bench] ctx1m decode step as one graph launch: {us:.1f} us")
     return round(us, 2)
+
+
+BRIDGE_D_MODEL = 2048  # hidden width of the bridged self-decoder states (the pages give no width)
+
+
+def kv_bridge_leg(c, head):
+    """KV Bridging and the early-exit prefill on the 1M-token workload's
+    chunk: with early exit the cross-decoder's prefill work for the chunk is
+    only the bridge (its full-attention K/V rows from the self-decoder's
+    hidden states); without it, the chunk also runs the full layer with
+    selection and the sparse layers (the headline's prefill block). Reports
+    both FLOP counts and times; the bridge is a bf16 GEMM priced against the
+    matrix peak."""
+    torch, hs, synth = c.torch, c.hs, c.synth
+    w = synth.WORKLOADS["ctx1m"]
+    d_model = BRIDGE_D_MODEL
+    h = synth.randn_bf16((1, w.n_q, d_model), synth.seed_for(w.cid, 10), c.dev)
+    wt = (synth.randn_bf16((w.Hkv, 2, 128, d_model), synth.seed_for(w.cid, 11), c.dev).float()
+          / d_model ** 0.5).to(torch.bfloat16)
+    kv = torch.empty((1, w.Hkv, w.n_q, 2, 128), dtype=torch.bfloat16, device=c.dev)
+    ms, kt = timed_steps(c, lambda: hs.kv_bridge(h, wt, kv, w.n_q), 10, 2, "kv bridge over the ctx1m chunk")
+    us = avg_us(kt, "kv_bridge")
+    bridge_flops = 2.0 * w.n_q * d_model * w.Hkv * 2 * 128
+    counts = prefill_counts(w)
+    full_flops = counts["full_flops"] + w.sparse_layers * counts["sparse_flops_per_layer"] + bridge_flops
+    out = {"d_model": d_model, "tokens": w.n_q, "bridge_us": round(us, 1),
+           "bridge_roofline": mfma_roof(bridge_flops, us, "kv_bridge"),
+           "prefill_flops_with_early_exit": bridge_flops, "prefill_flops_without_early_exit": full_flops,
+           "flop_ratio": round(full_flops / bridge_flops, 1),
+           "prefill_ms_with_early_exit": round(us * 1e-3, 3),
+           "prefill_ms_without_early_exit": round(head["prefill_block_ms"] + us * 1e-3, 3)}
+    del h, wt, kv
+    torch.cuda.empty_cache()
+    return out
 
 
 def copy_ceiling(c):
@@ -568,14 +612,18 @@ def cpu_model():
 # ---------------------------------------------------------------- counter runs
 
 def traffic_probe(c, args):
-    """For counter runs (rocprofv3 --pmc ...): one launch of each kernel of
+    """For counter runs (rocprofv3 --pmc ... --kernel-include-regex "hs::|MulFunctor"):
+    one launch of each kernel of
     the 1M-token step (full layer with selection, one sparse layer, one
     decode step with one sparse layer), the 32K full and sparse layers and one
     batched decode step, then a plain elementwise copy of known size (reads
     and writes 1 GiB) whose counter reading calibrates bytes per counter
     unit. Markers on stderr name each phase."""
+    import dataclasses
     torch, hs, synth = c.torch, c.hs, c.synth
-    w = synth.WORKLOADS["ctx1m"]
+    # no needles: planting them launches ~1000 tiny kernels, which the counter
+    # mode of the profiler has failed on, and they do not change the traffic
+    w = dataclasses.replace(synth.WORKLOADS["ctx1m"], needles=0)
     case = synth.make_prefill_case(w, c.dev, kv_capacity=w.n_kv + 1, sparse_layers=1)
     q, kv, qs = case["q_full"], case["kv"], case["q_sparse"][0]
     o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window)
@@ -588,7 +636,7 @@ def traffic_probe(c, args):
     log("[bench] traffic probe: ctx1m layers done")
     del case, q, kv, qs, o, lse, idx, o2, idx2
     torch.cuda.empty_cache()
-    w = synth.WORKLOADS["prefill32k"]
+    w = dataclasses.replace(synth.WORKLOADS["prefill32k"], needles=0)
     case = synth.make_prefill_case(w, c.dev, sparse_layers=1)
     q, kv, qs = case["q_full"], case["kv"], case["q_sparse"][0]
     o, lse, idx = hs.full_attn_select(q, kv, w.n_kv, top_k=w.top_k, window=w.window)
@@ -705,6 +753,7 @@ def main():
         wd = c.synth.WORKLOADS["decode64"]
         extras["decode64"] = run_decode_extra(c, args, "decode64", c.synth.decode_lengths(wd), args.decode_steps,
                                               not args.no_options)
+        extras["kv_bridge_early_exit"] = kv_bridge_leg(c, head)
         extras["copy_ceiling_GBs"] = copy_ceiling(c)
         extras["gather_ceiling_GBs"] = gather_ceilings(c)
         for key in ("decode_full_roofline", "decode_sparse_roofline"):
