@@ -86,8 +86,9 @@ def test_decode_long_rows_filtered_select():
 
 
 def test_decode_sampled_threshold_overshoot():
-    """Long rows are filtered by the m-th largest of 8192 evenly spaced
-    samples. Keys placed exactly at the sampled positions and aimed at the
+    """Long rows are filtered by the m-th largest of their samples: every
+    2^s-th candidate score, s >= 2 the smallest shift leaving at most 8192
+    of them. Keys placed exactly at the sampled positions and aimed at the
     queries push that threshold above the row's k-th score, so fewer than k
     keys survive the filter: the selection must fall back to the whole row
     and still return the exact top k (most of them those planted keys)."""
@@ -99,7 +100,10 @@ def test_decode_sampled_threshold_overshoot():
     u = q[0].float().sum(0)
     u = u / u.norm() * (128 ** 0.5)
     ncand = L - W + 1  # candidates of the row after the append (p = L)
-    pos = torch.tensor(sorted({(s * ncand) // 8192 for s in range(8192)}), device=DEV)
+    shift = 2
+    while -(-ncand // (1 << shift)) > 8192:
+        shift += 1
+    pos = torch.arange(0, ncand, 1 << shift, device=DEV)
     noise = synth.randn_bf16((len(pos), 128), 83, DEV).float()
     kv[0, 0, pos, 0] = (0.8 * u[None] + 0.6 * noise).to(torch.bfloat16)
     kv_new = synth.randn_bf16((1, Hkv, 2, 128), 84, DEV)

@@ -229,8 +229,8 @@ struct DecodePlan {
   bool block = false;     // block-level selection from the score rows
   bool head_union = false; // per-head score rows and lists, then their union
   int blk_stride = 0;
-  size_t off_sigma = 0, off_part = 0, off_theta = 0, off_segcnt = 0, off_segkey = 0, off_segidx = 0, off_lse = 0,
-         off_blk = 0, off_hidx = 0, total = 0;
+  size_t off_sigma = 0, off_part = 0, off_theta = 0, off_samp = 0, off_segcnt = 0, off_segkey = 0, off_segidx = 0,
+         off_lse = 0, off_blk = 0, off_hidx = 0, total = 0;
 };
 
 // Splits a per-(b, g) key stream of up to `nkeys` keys so that the grid holds
@@ -273,15 +273,12 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
   p.off_part = o;
   o = align_up(o + (size_t)bg * p.splits * G * (128 + 2) * 4);
   // Rows longer than one block's registers hold are selected in slices spread
-  // over the chip; survivors get room for a whole slice each (no overflow).
-  // One block per row filters with 2048 samples into 8192 register slots,
-  // expecting about k + 6 sqrt(k n / 2048) survivors; rows whose survivors
-  // would not fit, or a batch too small to occupy the chip with one block per
-  // row, are selected in slices instead.
+  // over the chip (a threshold block per row, a filter block per slice of a
+  // row, a final block per row); survivors get room for a whole slice each
+  // (no overflow). With one block per row instead, even 256 rows of 64K-256K
+  // candidates left the chip mostly idle (215 us for 0.22 GB of score rows).
   const int64_t max_cand = (int64_t)max_seq_len - s->window;
-  const double expect = s->top_k + 6.0 * std::sqrt((double)s->top_k * (double)max_cand / 2048.0);
-  if (s->top_k > 0 && !(s->flags & HS_FLAG_BLOCK_SELECT) && max_cand > hs::kSelRegKeys &&
-      (sel_rows < kChipSimds / 4 || expect > 0.75 * hs::kSelRegKeys)) {
+  if (s->top_k > 0 && !(s->flags & HS_FLAG_BLOCK_SELECT) && max_cand > hs::kSelRegKeys) {
     const int64_t ns = (max_cand + hs::kDecSlice - 1) / hs::kDecSlice;
     if (ns <= hs::kMaxDecSlices) p.sel_slices = (int)ns;
   }
@@ -289,6 +286,8 @@ DecodePlan plan_decode_full(const hs_shape* s, int max_seq_len) {
     const size_t seg = (size_t)sel_rows * p.sel_slices;
     p.off_theta = o;
     o = align_up(o + (size_t)sel_rows * 4);
+    p.off_samp = o;
+    o = align_up(o + (size_t)sel_rows * hs::kDecSamples * 4);
     p.off_segcnt = o;
     o = align_up(o + seg * 4);
     p.off_segkey = o;
@@ -788,6 +787,8 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
   float* sigma = s->top_k > 0 ? reinterpret_cast<float*>(w + plan.off_sigma) : nullptr;
   dp.sigma = plan.prob || plan.head_union ? nullptr : sigma;  // those scores are written by their own pass
   dp.sigma_stride = plan.sigma_stride;
+  float* samp = plan.sel_slices > 0 ? reinterpret_cast<float*>(w + plan.off_samp) : nullptr;
+  dp.samp = samp;
   HIP_TRY(timed("decode_full", hst, [&] { return hs::launch_decode_full(dp, hst); }));
   if (plan.splits > 1) {
     hs::CombineParams cp{};
@@ -801,6 +802,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     zp.q = dp.q; zp.kv = dp.kv; zp.seq_lens = seq_lens; zp.lse = lse_buf;
     zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
     zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window; zp.max_len = max_seq_len;
+    zp.samp = samp;
     HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
   }
   if (plan.head_union) {
@@ -809,6 +811,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     zp.q = dp.q; zp.kv = dp.kv; zp.seq_lens = seq_lens; zp.lse = nullptr;
     zp.B = s->batch; zp.Hq = s->q_heads; zp.Hkv = s->kv_heads; zp.window = s->window; zp.scale = dp.scale;
     zp.sigma = sigma; zp.sigma_stride = plan.sigma_stride; zp.max_cand = max_seq_len - s->window; zp.max_len = max_seq_len;
+    zp.samp = samp;
     zp.per_head = 1;
     HIP_TRY(timed("decode_score", hst, [&] { return hs::launch_decode_prob_score(zp, hst); }));
     int32_t* hidx = reinterpret_cast<int32_t*>(w + plan.off_hidx);
@@ -818,6 +821,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     sp.nslices = plan.sel_slices;
     if (plan.sel_slices > 0) {
       sp.theta_key = reinterpret_cast<uint32_t*>(w + plan.off_theta);
+      sp.samp = samp;
       sp.seg_count = reinterpret_cast<uint32_t*>(w + plan.off_segcnt);
       sp.seg_key = reinterpret_cast<uint32_t*>(w + plan.off_segkey);
       sp.seg_idx = reinterpret_cast<int32_t*>(w + plan.off_segidx);
@@ -848,6 +852,7 @@ hs_status hs_decode_step(const hs_shape* s, const void* q, const void* kv_new, v
     sp.nslices = plan.sel_slices;
     if (plan.sel_slices > 0) {
       sp.theta_key = reinterpret_cast<uint32_t*>(w + plan.off_theta);
+      sp.samp = samp;
       sp.seg_count = reinterpret_cast<uint32_t*>(w + plan.off_segcnt);
       sp.seg_key = reinterpret_cast<uint32_t*>(w + plan.off_segkey);
       sp.seg_idx = reinterpret_cast<int32_t*>(w + plan.off_segidx);

@@ -262,10 +262,19 @@ __global__ __launch_bounds__(256) void flash_gather_kernel(DecodeParams P) {
   const int sig_last = imin(cand_end, send - 1);  // last key this split may start a piece at
   int sig_v0 = 0;                                 // first key of the staged segment
   // Writes the staged scores of keys [sig_v0, ve) (relative to sbeg).
+  // Pieces start at multiples of 4 (splits and segments are), so a sample
+  // (every 2^s-th candidate, s >= 2) can only be a piece's first key.
+  float* const samp_row = SIGMA && P.samp ? P.samp + ((int64_t)b * P.Hkv + g) * kDecSamples : nullptr;
+  const int samp_shift = dec_sample_shift(cand_end + 1);
+  const int samp_mask = (1 << samp_shift) - 1;
   auto sig_flush = [&](int ve) {
     for (int i = 4 * lane; i < ve - sig_v0; i += 256) {
       const int j = sbeg + sig_v0 + i;
-      if (j <= sig_last) *reinterpret_cast<f32x4*>(sig_row + j) = *reinterpret_cast<const f32x4*>(&sig_stage[i]);
+      if (j <= sig_last) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sig_stage[i]);
+        *reinterpret_cast<f32x4*>(sig_row + j) = v;
+        if (samp_row && (j & samp_mask) == 0) samp_row[j >> samp_shift] = v[0];
+      }
     }
   };
   // Online-softmax update and O^T += V^T P^T for one 16-key chunk: acc holds

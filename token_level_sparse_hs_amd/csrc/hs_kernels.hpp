@@ -91,18 +91,29 @@ struct SelectDecodeParams {
   int32_t* idx;        // [B][Hkv][top_k]
   // Sliced path (nslices > 0) for rows longer than one block holds in
   // registers: per-row threshold, a filter over row slices of kDecSlice keys
-  // by separate blocks, then one block per row on the survivors.
+  // (one wave each), then one block per row on the survivors.
   int nslices;         // slices per row (covers the longest row)
   uint32_t* theta_key; // [rows] filter threshold (score key; 0 = no filter)
+  const float* samp;   // [rows][kDecSamples] every 2^dec_sample_shift-th score of the row
   uint32_t* seg_count; // [rows][nslices] survivors per slice
-  uint32_t* seg_key;   // [rows][nslices][kDecSlice] survivors' score keys, index order
+  uint32_t* seg_key;   // [rows][nslices][kDecSlice] survivors' scores (fp32 bits), index order
   int32_t* seg_idx;    // [rows][nslices][kDecSlice] survivors' token indices
 };
-// Sliced decode selection: keys per filter block; rows of up to kSelRegKeys
+// Sliced decode selection: keys per filter wave; rows of up to kSelRegKeys
 // candidates are selected directly from registers by one block.
-constexpr int kDecSlice = 16384;
+constexpr int kDecSlice = 4096;
 constexpr int kSelRegKeys = 8192;
-constexpr int kMaxDecSlices = 1024;
+constexpr int kMaxDecSlices = 4096;
+// The kernel that writes a decode score row also writes its samples for the
+// sliced threshold: scores at j = 2^s * i for i < ceil(|C| / 2^s), with s the
+// smallest shift of at least 2 leaving at most kDecSamples of them. A shift
+// of at least 2 puts each sample at the start of an aligned 4-key piece.
+constexpr int kDecSamples = 8192;
+__host__ __device__ __forceinline__ int dec_sample_shift(int ncand) {
+  int s = 2;
+  while (((ncand + (1 << s) - 1) >> s) > kDecSamples) ++s;
+  return s;
+}
 
 // Decode probability-score row: sigma[(b,g)][j] = max over the group's heads
 // of fl(scale * <q_h, k_j>) - lse_h for j in C(p), fp32 dot products in
@@ -119,6 +130,7 @@ struct DecodeScoreParams {
   int max_cand;       // bound on |C(p)| over the batch (grid size)
   int max_len;        // host bound on seq_lens (longer lengths are read as max_len)
   int per_head;       // 1: each head's scaled logit into row b*Hq + h (lse unused)
+  float* samp;        // [rows][kDecSamples] the rows' samples (null: none)
 };
 hipError_t launch_decode_prob_score(const DecodeScoreParams& p, hipStream_t s);
 
@@ -189,6 +201,7 @@ struct DecodeParams {
                             // splits of one (b, g) row and merge in LDS (part unused)
   float* sigma;             // FULL: [B*Hkv][sigma_stride]
   int64_t sigma_stride;
+  float* samp;              // FULL with sigma: [B*Hkv][kDecSamples] samples of the score rows (or null)
   // SPARSE from the FP8 cache copy (kv8 != null; kv unused): rows of
   // [B][Hkv][kv8_cap] tokens, K then V codes, and per-(b, g) scales.
   const uint8_t* kv8;

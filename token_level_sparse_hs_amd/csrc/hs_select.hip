@@ -523,6 +523,146 @@ __device__ RadixResult wave_radix(uint32_t* hist, const uint32_t (&key)[E], int 
   return r;
 }
 
+// Block-wide form of wave_radix over the register keys of all kSelThreads
+// threads (slots e < eslots, wave-uniform; 0 = empty): the bits all keys
+// share are decided from a block min/max, then 8-bit digits, counted into
+// kHistCopies copies per wave (each lane into copy lane % kHistCopies of its
+// wave's set, so lanes with equal digits mostly hit different words), and
+// every wave picks the digit from the summed copies itself. A plain block
+// radix sent all of a row's keys to one or two bins in its first passes
+// (scores share their sign and leading exponent bits), and the LDS atomics
+// of a wave to one word serialise. `hist` holds kBlkHistWords words; the
+// min/max exchange uses sh.wave_tot and sh.cnt.
+constexpr int kBlkHistWords = kSelWaves * kHistCopies * kHistStride;
+
+template <int E>
+__device__ RadixResult block_radix(SelShared& sh, uint32_t* hist, const uint32_t (&key)[E], int eslots,
+                                   uint32_t rank) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kmax = key[e] > kmax ? key[e] : kmax;
+    kmin = (key[e] && key[e] < kmin) ? key[e] : kmin;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)kmax, o, 64), c = (uint32_t)__shfl_xor((int)kmin, o, 64);
+    kmax = a > kmax ? a : kmax;
+    kmin = c < kmin ? c : kmin;
+  }
+  if (lane == 0) {
+    sh.wave_tot[wave] = kmax;
+    sh.cnt[wave] = kmin;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    kmax = sh.wave_tot[w] > kmax ? sh.wave_tot[w] : kmax;
+    kmin = sh.cnt[w] < kmin ? sh.cnt[w] : kmin;
+  }
+  RadixResult r{kmax, 0xffffffffu, rank, false};
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0u) {  // every key equal: the first `rank` in index order
+    __syncthreads();  // the exchange words are read before anyone reuses them
+    return r;
+  }
+  int hi = 31 - __builtin_clz(diff);
+  r.mask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+  r.prefix = kmax & r.mask;
+  uint32_t* my = hist + (wave * kHistCopies + lane % kHistCopies) * kHistStride;
+#pragma unroll 1
+  while (hi >= 0) {
+    const int shift = imax(hi - 7, 0);
+    const uint32_t dmask = (2u << (hi - shift)) - 1u;
+    __syncthreads();  // earlier readers of this LDS (the previous pass, or the caller's) are done
+    for (int i = threadIdx.x; i < kBlkHistWords / 4; i += kSelThreads)
+      reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    const uint32_t lim = hi == 31 ? 0xffffffffu : (2u << hi) - 1u;
+    const uint32_t dump = 256u + (uint32_t)(lane / kHistCopies);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (e < eslots) {  // wave-uniform
+        const uint32_t d = key[e] - r.prefix;
+        atomicAdd(&my[(key[e] != 0u && d <= lim) ? d >> shift : dump], 1u);
+      }
+    }
+    __syncthreads();
+    // lane l owns digits 255 - 4l - q (descending): bins 252 - 4l .. 255 - 4l
+    u32x4 cv = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int cp = 0; cp < kSelWaves * kHistCopies; ++cp)
+      cv += *reinterpret_cast<const u32x4*>(hist + cp * kHistStride + 252 - 4 * lane);
+    const uint32_t c[4] = {cv[3], cv[2], cv[1], cv[0]};
+    const int local = (int)(c[0] + c[1] + c[2] + c[3]);
+    const int incl = wave_incl_scan(local);
+    const uint64_t hit = ballot((uint32_t)incl >= r.need);
+    const int L = __builtin_ctzll(hit);  // first lane reaching the rank
+    uint32_t acc = (uint32_t)(incl - local), dsel = 0u, gt = 0u, eq = 0u;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && acc + c[q] >= r.need) {
+        found = true;
+        dsel = 255u - 4u * (uint32_t)lane - (uint32_t)q;
+        gt = acc;
+        eq = c[q];
+      }
+      acc += c[q];
+    }
+    dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, L);
+    gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+    eq = (uint32_t)__builtin_amdgcn_readlane((int)eq, L);
+    r.prefix |= dsel << shift;
+    r.mask |= dmask << shift;
+    r.need -= gt;
+    if (eq == r.need) {
+      r.take_all = true;
+      break;
+    }
+    hi = shift - 1;
+  }
+  return r;
+}
+
+// Exact top-k (k < n <= E * kSelThreads) of an index-ordered source, as
+// topk_regs_e but with block_radix; `hist` (kBlkHistWords words) may alias
+// the source's key array: every key is in registers before its first clear.
+template <int E, class Src>
+__device__ void topk_regs_blk(SelShared& sh, uint32_t* hist, const Src& src, int n, int k, int32_t* out) {
+  const int run = (n + kSelThreads - 1) / kSelThreads;
+  const int beg = threadIdx.x * run;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (e < run && beg + e < n) ? src.key(beg + e) : 0u;
+  const RadixResult r = block_radix<E>(sh, hist, key, run, (uint32_t)k);
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (!key[e]) continue;
+    const uint32_t km = key[e] & r.mask;
+    ngt += km > r.prefix;
+    neq += km == r.prefix;
+  }
+  const uint32_t excl = block_excl_scan(sh, ngt | (neq << 16));
+  const uint32_t eq_before = excl >> 16;
+  uint32_t pos = (excl & 0xffffu) + (r.take_all ? eq_before : (eq_before < r.need ? eq_before : r.need));
+  uint32_t eq_rank = eq_before;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (!key[e]) continue;
+    const uint32_t km = key[e] & r.mask;
+    bool sel = km > r.prefix;
+    if (km == r.prefix) {
+      sel = r.take_all || eq_rank < r.need;
+      ++eq_rank;
+    }
+    if (sel) out[pos++] = src.index(beg + e);
+  }
+}
+
 constexpr int kWaveE = 80;  // candidates per lane of the wave path (rows of up to 5120)
 
 // One wave per (b, t, g) row: the candidate buffer is read lane-strided
@@ -754,12 +894,14 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecode
 // A decode score row of a long sequence (a million keys at the 1M-token
 // context) is too long for one block to scan at memory speed, and a batch of
 // one sequence has only Hkv such rows. Three launches spread it over the chip:
-//  1. threshold: one block per row takes kDecSamples evenly spaced keys and
+//  1. threshold: one block per row reads the row's S samples (every 2^s-th
+//     key, at most kDecSamples, written beside the score row by the kernel
+//     that produced it, so this reads 32 KB instead of the row) and takes
 //     their m-th largest, m = mu + 6 sqrt(mu) + 1 with mu = k S / n the
 //     expected number of samples among the row's top k, so that the k-th
 //     largest key of the row lies at or above it with overwhelming
 //     probability;
-//  2. filter: one block per (slice of kDecSlice keys, row) keeps the keys at
+//  2. filter: one wave per (slice of kDecSlice keys, row) keeps the keys at
 //     or above the threshold, in index order, with their indices;
 //  3. final: one block per row concatenates the slices' survivors in slice
 //     order (so still in index order) and selects exactly from them. When
@@ -767,8 +909,8 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecode
 //     the block holds, it selects from the whole dense row instead, so the
 //     result never depends on the sampling.
 
-constexpr int kDecSamples = 8192;
 constexpr int kDecCandCap = 16384;  // survivors the final block holds in LDS
+static_assert(kDecCandCap >= kBlkHistWords, "the final block's histograms overlay its key array");
 
 // Exclusive block-wide scan that also returns the block total.
 __device__ __forceinline__ uint32_t block_scan_total(SelShared& sh, uint32_t v, uint32_t* total) {
@@ -799,75 +941,121 @@ __device__ __forceinline__ DecRow dec_row(const SelectDecodeParams& P, int row) 
 
 __global__ __launch_bounds__(kSelThreads) void select_decode_threshold_kernel(SelectDecodeParams P) {
   __shared__ SelShared sh;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBlkHistWords];
   const int row = blockIdx.x;
   const DecRow r = dec_row(P, row);
   if (r.ncand <= kRegCap) return;  // selected directly by the final kernel
-  const double mu = (double)P.top_k * kDecSamples / (double)r.ncand;
+  const int shift = dec_sample_shift(r.ncand);
+  const int nsamp = (r.ncand + (1 << shift) - 1) >> shift;
+  const double mu = (double)P.top_k * nsamp / (double)r.ncand;
   const int m = (int)ceil(mu + 6.0 * sqrt(mu)) + 1;
-  if (m >= kDecSamples) {  // the samples cannot bound the k-th key: no filter
+  if (m >= nsamp) {  // the samples cannot bound the k-th key: no filter
     if (threadIdx.x == 0) P.theta_key[row] = 0u;
     return;
   }
+  // thread t holds samples 4(t + 256e) .. +3: contiguous 16-byte loads
   constexpr int ES = kDecSamples / kSelThreads;
-  const DenseSrc src{r.s};
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(P.samp + (int64_t)row * kDecSamples, 4u * (uint32_t)nsamp);
   uint32_t skey[ES];
 #pragma unroll
-  for (int e = 0; e < ES; ++e) {
-    const int s = threadIdx.x * ES + e;
-    skey[e] = src.key((int)(((int64_t)s * r.ncand) / kDecSamples));
+  for (int e = 0; e < ES / 4; ++e) {
+    const int i = 4 * ((int)threadIdx.x + kSelThreads * e);
+    const u32x4 v = buf_ld16(rs, 4u * (uint32_t)i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) skey[4 * e + q] = i + q < nsamp ? score_key(__uint_as_float(v[q])) : 0u;
   }
-  const RadixResult rr = radix_regs<ES>(sh, skey, (uint32_t)m);
+  const RadixResult rr = block_radix<ES>(sh, hist, skey, ES, (uint32_t)m);
   // keys >= prefix include the m largest samples (take_all leaves the low
   // bits of prefix zero: still a lower bound)
   if (threadIdx.x == 0) P.theta_key[row] = rr.prefix;
 }
 
+// One wave per slice (kDecSlice keys of a row; a block holds four slices of
+// one row). Load j of lane l reads keys 256j + 4l .. +3 of the slice, so
+// every load is one contiguous 1 KB piece of the row, and all 16 are issued
+// up front. Survivors are emitted in index order (per load, then lane, then
+// q; positions from four ballots) as soon as each load lands, while the later
+// ones are still in flight: each slice has its own output segment, so no
+// wave waits for another (a block-wide count exchange before the emission
+// held every resident block in step, loads then emission, and cost 40% of the
+// kernel). They pass through the wave's LDS ring in order and leave in runs
+// of 64 consecutive entries (one coalesced store per array), not as one
+// scattered store per survivor bit position. About 2% of the keys survive.
+constexpr int kRing = 512;  // per-wave LDS ring of the filter's survivors
+
 __global__ __launch_bounds__(kSelThreads) void select_decode_filter_kernel(SelectDecodeParams P) {
-  __shared__ SelShared sh;
-  const int slice = blockIdx.x, row = blockIdx.y;
+  __shared__ uint32_t ring_key[kSelWaves][kRing];
+  __shared__ int32_t ring_idx[kSelWaves][kRing];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = (int)blockIdx.x * kSelWaves + wave, row = blockIdx.y;
+  if (slice >= P.nslices) return;
   const DecRow r = dec_row(P, row);
-  if (r.ncand <= kRegCap) return;
+  if (r.ncand <= kRegCap) return;  // selected directly by the final kernel
   const int i0 = slice * kDecSlice;
   const int n = imin(r.ncand, i0 + kDecSlice) - i0;
   const int64_t seg = (int64_t)row * P.nslices + slice;
   if (n <= 0) {
-    if (threadIdx.x == 0) P.seg_count[seg] = 0u;
+    if (lane == 0) P.seg_count[seg] = 0u;
     return;
   }
   const uint32_t theta = P.theta_key[row];
-  // thread t owns keys [64t, 64t + 64) of the slice: one scan keeps index order
-  constexpr int kPer = kDecSlice / kSelThreads;
-  static_assert(kPer == 64, "16 vector loads per thread");
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(r.s + i0, 4u * (uint32_t)n);  // reads past n return 0
-  u32x4 w[kPer / 4];
+  constexpr int kLoads = kDecSlice / 256;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(r.s + i0, 4u * (uint32_t)n);
+  u32x4 v[kLoads];
 #pragma unroll
-  for (int j = 0; j < kPer / 4; ++j) w[j] = buf_ld16(rs, 4u * (uint32_t)(kPer * threadIdx.x + 4 * j));
-  const int e0 = kPer * threadIdx.x;
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kPer / 4; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) cnt += (e0 + 4 * j + q < n && score_key(__uint_as_float(w[j][q])) >= theta) ? 1u : 0u;
-  uint32_t total;
-  uint32_t pos = block_scan_total(sh, cnt, &total);
+  for (int j = 0; j < kLoads; ++j)  // past the slice's end: range-checked, read as 0 (only a row's last slice)
+    v[j] = buf_ld16(rs, 4u * (uint32_t)(256 * j + 4 * lane));
+  const int lim = n - 4 * lane;  // key 256j + q of this lane lies in the slice iff 256j + q < lim
   uint32_t* okey = P.seg_key + seg * kDecSlice;
   int32_t* oidx = P.seg_idx + seg * kDecSlice;
+  uint32_t* rkey = ring_key[wave];
+  int32_t* ridx = ring_idx[wave];
+  uint32_t tail = 0, head = 0;  // entries appended to / written out of the ring (wave-uniform)
 #pragma unroll
-  for (int j = 0; j < kPer / 4; ++j)
+  for (int j = 0; j < kLoads; ++j) {
+    // survivor bits, branch-free (a short-circuit test per key became a
+    // branch per key, and the branches made the first test wait for every load)
+    uint32_t m4 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      m4 |= ((uint32_t)(256 * j + q < lim) & (uint32_t)(score_key(__uint_as_float(v[j][q])) >= theta)) << q;
+    if (ballot(m4 != 0u) == 0) continue;  // wave-uniform
+    uint32_t pos = tail;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t key = score_key(__uint_as_float(w[j][q]));
-      if (e0 + 4 * j + q < n && key >= theta) {
-        okey[pos] = key;
-        oidx[pos] = i0 + e0 + 4 * j + q;
+      const uint64_t bq = ballot((m4 >> q) & 1u);
+      pos += lane_prefix(bq);
+      tail += (uint32_t)__popcll(bq);
+    }
+    const int e0 = i0 + 256 * j + 4 * lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((m4 >> q) & 1u) {
+        rkey[pos & (kRing - 1)] = v[j][q];  // the score's bits (the final kernel takes their key)
+        ridx[pos & (kRing - 1)] = e0 + q;
         ++pos;
       }
     }
-  if (threadIdx.x == 0) P.seg_count[seg] = total;
+    if (tail - head >= kRing / 2) {  // a load adds at most 256 < kRing / 2 entries: no overrun
+#pragma unroll
+      for (int c = 0; c < kRing / 128; ++c) {
+        const uint32_t i = head + 64u * (uint32_t)c + (uint32_t)lane;
+        okey[i] = rkey[i & (kRing - 1)];
+        oidx[i] = ridx[i & (kRing - 1)];
+      }
+      head += kRing / 2;
+    }
+  }
+  for (uint32_t i = head + (uint32_t)lane; i < tail; i += 64) {
+    okey[i] = rkey[i & (kRing - 1)];
+    oidx[i] = ridx[i & (kRing - 1)];
+  }
+  if (lane == 0) P.seg_count[seg] = tail;
 }
 
 struct DecLds {
-  uint32_t key[kDecCandCap];
+  __attribute__((aligned(16))) uint32_t key[kDecCandCap];
   int32_t idx[kDecCandCap];
   uint32_t off[kMaxDecSlices + 1];
 };
@@ -885,7 +1073,7 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
   }
   const DenseSrc dense{r.s};
   if (r.ncand <= kRegCap) {
-    topk_regs(sh, dense, r.ncand, k, out);
+    topk_regs_blk<kE>(sh, lds.key, dense, r.ncand, k, out);
     return;
   }
   const int ns = (r.ncand + kDecSlice - 1) / kDecSlice;  // <= nslices <= kMaxDecSlices
@@ -914,7 +1102,7 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
       else hi = mid;
     }
     const int64_t src = ((int64_t)row * P.nslices + lo) * kDecSlice + (i - lds.off[lo]);
-    lds.key[i] = P.seg_key[src];
+    lds.key[i] = score_key(__uint_as_float(P.seg_key[src]));
     lds.idx[i] = P.seg_idx[src];
   }
   __syncthreads();
@@ -922,9 +1110,9 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
   if (total == (uint32_t)k) {
     for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = lds.idx[i];
   } else if (total <= (uint32_t)kRegCap) {
-    topk_regs(sh, ls, (int)total, k, out);
+    topk_regs_blk<kE>(sh, lds.key, ls, (int)total, k, out);  // the histograms overlay the keys once in registers
   } else {
-    topk_regs_e<kDecCandCap / kSelThreads>(sh, ls, (int)total, k, out);
+    topk_regs_blk<kDecCandCap / kSelThreads>(sh, lds.key, ls, (int)total, k, out);
   }
 }
 
@@ -954,6 +1142,9 @@ __global__ __launch_bounds__(256) void decode_prob_score_kernel(DecodeScoreParam
   const float lse_col = col < G && !P.per_head ? P.lse[(int64_t)b * P.Hq + g * G + col] : 0.f;
   const uint16_t* slab = P.kv.slab(b, g);
   float* srow = P.sigma + (int64_t)row * P.sigma_stride;
+  // samples for the sliced threshold: scores at multiples of 2^s (jk is a multiple of 4)
+  const int samp_shift = dec_sample_shift(ncand);
+  const int samp_mask = (1 << samp_shift) - 1;
   const int jend = imin(ncand, j0 + kDecScoreWaveKeys);
   for (int c0 = j0; c0 < jend; c0 += 64) {
     // A operand: key c0 + 16ch + col, dims 32s + 8kg .. +8 (rows past the
@@ -976,7 +1167,9 @@ __global__ __launch_bounds__(256) void decode_prob_score_kernel(DecodeScoreParam
       const int jk = c0 + 16 * ch + 4 * kg;
       if (P.per_head) {  // each head's own scaled logit, its own row
         if (col < G) {
-          float* hrow = P.sigma + ((int64_t)b * P.Hq + g * G + col) * P.sigma_stride;
+          const int64_t hr = (int64_t)b * P.Hq + g * G + col;
+          float* hrow = P.sigma + hr * P.sigma_stride;
+          if (P.samp && jk < ncand && (jk & samp_mask) == 0) P.samp[hr * kDecSamples + (jk >> samp_shift)] = acc[0] * P.scale;
           if (jk + 3 < ncand) {
             *reinterpret_cast<f32x4*>(hrow + jk) =
                 f32x4{acc[0] * P.scale, acc[1] * P.scale, acc[2] * P.scale, acc[3] * P.scale};
@@ -992,6 +1185,7 @@ __global__ __launch_bounds__(256) void decode_prob_score_kernel(DecodeScoreParam
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = group_max<G>(col < G ? fmaf(acc[i], P.scale, -lse_col) : kNegInf);
       if (col == 0) {
+        if (P.samp && jk < ncand && (jk & samp_mask) == 0) P.samp[(int64_t)row * kDecSamples + (jk >> samp_shift)] = v[0];
         if (jk + 3 < ncand) {
           *reinterpret_cast<f32x4*>(srow + jk) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
@@ -1288,7 +1482,8 @@ hipError_t launch_select_decode(const SelectDecodeParams& p, int rows, hipStream
   select_decode_threshold_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  select_decode_filter_kernel<<<dim3((unsigned)p.nslices, (unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
+  select_decode_filter_kernel<<<dim3((unsigned)((p.nslices + kSelWaves - 1) / kSelWaves), (unsigned)rows),
+                                dim3(kSelThreads), 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   select_decode_final_kernel<<<dim3((unsigned)rows), dim3(kSelThreads), 0, s>>>(p);
