@@ -3,6 +3,7 @@
 // enqueued; the library allocates no device memory and never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -194,7 +195,9 @@ PrefillPlan plan_prefill(const hs_shape* s) {
   }
   p.cap = (int)std::min<int64_t>(round_up(3 * (int64_t)s->top_k + 256, 64), std::max<int64_t>(max_cand, 1));
   p.sample = max_cand > p.cap;
-  p.stride = std::max(1, s->top_k / 64);
+  // about 64 expected samples among a row's top k (stride k/64), but no more
+  // than 16384 samples per row: the threshold block holds that many in registers
+  p.stride = (int)std::max<int64_t>({1, s->top_k / 64, (max_cand + 16383) / 16384});
   p.max_samples = p.sample ? (int)round_up((max_cand + p.stride - 1) / p.stride, 64) : 0;
   size_t o = 0;
   p.off_theta = o;

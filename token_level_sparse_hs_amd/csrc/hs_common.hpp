@@ -254,11 +254,16 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {  // set bits be
 
 // Monotone map of a finite float to uint32 (larger float -> larger key), with
 // -0.0 mapped like +0.0 so that the two zeros tie.
+// Branch-free (selects and bit operations only): under a condition, a branch
+// here made the compiler wait for every outstanding load before each key.
 __device__ __forceinline__ uint32_t score_key(float x) {
   uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = u == 0x80000000u ? 0u : u;
+  const uint32_t neg = (uint32_t)((int32_t)u >> 31);  // all ones for a negative score
+  return u ^ (neg | 0x80000000u);
 }
+// score_key(x) where `valid`, else 0 (the empty key).
+__device__ __forceinline__ uint32_t score_key_if(float x, bool valid) { return score_key(x) & (0u - (uint32_t)valid); }
 __device__ __forceinline__ float key_to_score(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __uint_as_float(u);

@@ -245,47 +245,166 @@ struct RadixResult {
   bool take_all;    // every element equal to prefix (under mask) is selected
 };
 
-// Radix search over register-held keys (0 = empty slot) for the element of
-// rank `rank` (1-based, largest first). Stops early once a whole bucket is
-// needed.
+constexpr int kHistCopies = 8;
+constexpr int kHistStride = 256 + 64 / kHistCopies;  // words per copy: bins + dump slots
+
+// Block-wide form of wave_radix over the register keys of all kSelThreads
+// threads (slots e < eslots, wave-uniform; 0 = empty): the bits all keys
+// share are decided from a block min/max, then 8-bit digits, counted into
+// kBlkCopies copies per wave (each lane into copy lane % kBlkCopies of its
+// wave's set, so lanes with equal digits mostly hit different words), and
+// every wave picks the digit from the summed copies itself. A plain block
+// radix sent all of a row's keys to one or two bins in its first passes
+// (scores share their sign and leading exponent bits), and the LDS atomics
+// of a wave to one word serialise. `hist` holds kBlkHistWords words; the
+// min/max exchange uses sh.wave_tot and sh.cnt.
+constexpr int kBlkCopies = 4;                      // histogram copies per wave
+constexpr int kBlkStride = 256 + 64 / kBlkCopies;  // words per copy: bins + dump slots
+constexpr int kBlkHistWords = kSelWaves * kBlkCopies * kBlkStride;
+
 template <int E>
-__device__ RadixResult radix_regs(SelShared& sh, const uint32_t (&key)[E], uint32_t rank) {
+__device__ RadixResult block_radix(SelShared& sh, uint32_t* hist, const uint32_t (&key)[E], int eslots,
+                                   uint32_t rank) {
+  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  RadixResult r{0u, 0u, rank, false};
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    clear_hist(sh);
-    __syncthreads();
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] && (key[e] & r.mask) == r.prefix) atomicAdd(&sh.hist[wave][(key[e] >> shift) & 255u], 1u);
+  for (int e = 0; e < E; ++e) {
+    kmax = key[e] > kmax ? key[e] : kmax;
+    kmin = (key[e] && key[e] < kmin) ? key[e] : kmin;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)kmax, o, 64), c = (uint32_t)__shfl_xor((int)kmin, o, 64);
+    kmax = a > kmax ? a : kmax;
+    kmin = c < kmin ? c : kmin;
+  }
+  if (lane == 0) {
+    sh.wave_tot[wave] = kmax;
+    sh.cnt[wave] = kmin;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    kmax = sh.wave_tot[w] > kmax ? sh.wave_tot[w] : kmax;
+    kmin = sh.cnt[w] < kmin ? sh.cnt[w] : kmin;
+  }
+  RadixResult r{kmax, 0xffffffffu, rank, false};
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0u) {  // every key equal: the first `rank` in index order
+    __syncthreads();  // the exchange words are read before anyone reuses them
+    return r;
+  }
+  int hi = 31 - __builtin_clz(diff);
+  r.mask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+  r.prefix = kmax & r.mask;
+  uint32_t* my = hist + (wave * kBlkCopies + lane % kBlkCopies) * kBlkStride;
+#pragma unroll 1
+  while (hi >= 0) {
+    const int shift = imax(hi - 7, 0);
+    const uint32_t dmask = (2u << (hi - shift)) - 1u;
+    __syncthreads();  // earlier readers of this LDS (the previous pass, or the caller's) are done
+    for (int i = threadIdx.x; i < kBlkHistWords / 4; i += kSelThreads)
+      reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    pick_digit(sh, true, r.need);
+    const uint32_t lim = hi == 31 ? 0xffffffffu : (2u << hi) - 1u;
+    const uint32_t dump = 256u + (uint32_t)(lane / kBlkCopies);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (e < eslots) {  // wave-uniform
+        const uint32_t d = key[e] - r.prefix;
+        atomicAdd(&my[(key[e] != 0u && d <= lim) ? d >> shift : dump], 1u);
+      }
+    }
     __syncthreads();
-    r.prefix |= sh.found_digit << shift;
-    r.mask |= 0xffu << shift;
-    r.need -= sh.found_gt;
-    if (sh.found_eq == r.need) {
+    // lane l owns digits 255 - 4l - q (descending): bins 252 - 4l .. 255 - 4l
+    u32x4 cv = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int cp = 0; cp < kSelWaves * kBlkCopies; ++cp)
+      cv += *reinterpret_cast<const u32x4*>(hist + cp * kBlkStride + 252 - 4 * lane);
+    const uint32_t c[4] = {cv[3], cv[2], cv[1], cv[0]};
+    const int local = (int)(c[0] + c[1] + c[2] + c[3]);
+    const int incl = wave_incl_scan(local);
+    const uint64_t hit = ballot((uint32_t)incl >= r.need);
+    const int L = __builtin_ctzll(hit);  // first lane reaching the rank
+    uint32_t acc = (uint32_t)(incl - local), dsel = 0u, gt = 0u, eq = 0u;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && acc + c[q] >= r.need) {
+        found = true;
+        dsel = 255u - 4u * (uint32_t)lane - (uint32_t)q;
+        gt = acc;
+        eq = c[q];
+      }
+      acc += c[q];
+    }
+    dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, L);
+    gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+    eq = (uint32_t)__builtin_amdgcn_readlane((int)eq, L);
+    r.prefix |= dsel << shift;
+    r.mask |= dmask << shift;
+    r.need -= gt;
+    if (eq == r.need) {
       r.take_all = true;
       break;
     }
+    hi = shift - 1;
   }
-  __syncthreads();
+  __syncthreads();  // every wave has read the histograms: callers may reuse that LDS
   return r;
+}
+
+// The four largest of a thread's register keys (descending; 0 = empty), by
+// insertion with min/max pairs. A sampled threshold only needs a lower bound
+// on the m-th largest sample, and the m-th largest of any subset is one: the
+// m-th largest of the union of every thread's top four equals it unless some
+// thread holds five of the top m (for m = 113 of 16384 samples, 64 per
+// thread, about one row in 40), and is a little lower then. The radix over
+// that union (all from the upper tail, so the bits they share are skipped)
+// avoids most LDS atomics; over all samples, which span both signs, the
+// first digit sends nearly every lane to a few bins.
+template <int E>
+__device__ __forceinline__ void top4_regs(const uint32_t (&key)[E], uint32_t (&t)[4]) {
+  t[0] = t[1] = t[2] = t[3] = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t x = key[e];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint32_t hi = t[i] > x ? t[i] : x, lo = t[i] > x ? x : t[i];
+      t[i] = hi;
+      x = lo;
+    }
+    t[3] = t[3] > x ? t[3] : x;
+  }
 }
 
 // Exact top-k (k < n <= E * kSelThreads) of an index-ordered source; writes
 // the k selected indices ascending to out. Each thread holds a contiguous run
 // of the source in E registers.
 template <int E, class Src>
-__device__ void topk_regs_e(SelShared& sh, const Src& src, int n, int k, int32_t* out) {
-  const int run = (n + kSelThreads - 1) / kSelThreads;
+__device__ void topk_regs_e(SelShared& sh, uint32_t* hist, const Src& src, int n, int k, int32_t* out) {
+  const int run = __builtin_amdgcn_readfirstlane((n + kSelThreads - 1) / kSelThreads);  // block-uniform
   const int beg = threadIdx.x * run;
+  // Keys in groups of 8 slots (block-uniform test), each group's reads issued
+  // together at clamped in-range positions and masked afterwards: a read
+  // under a per-element condition made the compiler wait for each in turn.
+  static_assert(E % 8 == 0, "slots in groups of 8");
   uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (e < run && beg + e < n) ? src.key(beg + e) : 0u;
-  const RadixResult r = radix_regs<E>(sh, key, (uint32_t)k);
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    if (e0 < run) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) key[e0 + u] = src.key(imin(beg + e0 + u, n - 1));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) key[e0 + u] = 0u;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] &= 0u - (uint32_t)(e < run && beg + e < n);
+  const RadixResult r = block_radix<E>(sh, hist, key, run, (uint32_t)k);
   uint32_t ngt = 0, neq = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -298,22 +417,33 @@ __device__ void topk_regs_e(SelShared& sh, const Src& src, int n, int k, int32_t
   const uint32_t eq_before = excl >> 16;
   uint32_t pos = (excl & 0xffffu) + (r.take_all ? eq_before : (eq_before < r.need ? eq_before : r.need));
   uint32_t eq_rank = eq_before;
+  // indices read in groups of 8 as the keys were (a read per selected
+  // element, under its condition, waited for each in turn)
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (!key[e]) continue;
-    const uint32_t km = key[e] & r.mask;
-    bool sel = km > r.prefix;
-    if (km == r.prefix) {
-      sel = r.take_all || eq_rank < r.need;
-      ++eq_rank;
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    if (e0 < run) {
+      int32_t jv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) jv[u] = src.index(imin(beg + e0 + u, n - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t kk = key[e0 + u];
+        if (!kk) continue;
+        const uint32_t km = kk & r.mask;
+        bool sel = km > r.prefix;
+        if (km == r.prefix) {
+          sel = r.take_all || eq_rank < r.need;
+          ++eq_rank;
+        }
+        if (sel) out[pos++] = jv[u];
+      }
     }
-    if (sel) out[pos++] = src.index(beg + e);
   }
 }
 
 template <class Src>
-__device__ void topk_regs(SelShared& sh, const Src& src, int n, int k, int32_t* out) {
-  topk_regs_e<kE>(sh, src, n, k, out);
+__device__ void topk_regs(SelShared& sh, uint32_t* hist, const Src& src, int n, int k, int32_t* out) {
+  topk_regs_e<kE>(sh, hist, src, n, k, out);
 }
 
 struct LdsSrc {
@@ -328,6 +458,7 @@ struct LdsSrc {
 template <class Src>
 __device__ bool topk_filtered(SelShared& sh, uint32_t* lkey, int32_t* lidx, const Src& src, int n, int k,
                               int32_t* out) {
+  uint32_t* const hist = lkey;  // the histograms overlay the filter's LDS while it is not in use
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const double mu = (double)k * kSamples / (double)n;
   const int m = (int)ceil(mu + 6.0 * sqrt(mu)) + 1;
@@ -339,7 +470,7 @@ __device__ bool topk_filtered(SelShared& sh, uint32_t* lkey, int32_t* lidx, cons
     const int s = threadIdx.x * ES + e;
     skey[e] = src.key((int)(((int64_t)s * n) / kSamples));
   }
-  const RadixResult r = radix_regs<ES>(sh, skey, (uint32_t)m);
+  const RadixResult r = block_radix<ES>(sh, hist, skey, ES, (uint32_t)m);
   const uint32_t theta = r.prefix;  // keys >= theta include the m largest samples
   // Each wave filters a contiguous quarter of the row into its LDS region.
   constexpr int kRegion = kRegCap / kSelWaves;
@@ -404,17 +535,19 @@ __device__ bool topk_filtered(SelShared& sh, uint32_t* lkey, int32_t* lidx, cons
     for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = lidx[i];
     return true;
   }
-  topk_regs(sh, LdsSrc{lkey, lidx}, (int)total, k, out);
+  topk_regs(sh, hist, LdsSrc{lkey, lidx}, (int)total, k, out);
   return true;
 }
 
 // ---------------------------------------------------------------- kernels
 
 // Dispatch by row length: registers, LDS filter (BIG kernels only), stream.
+// `hist` (kBlkHistWords words) may be lkey in BIG kernels.
 template <bool BIG, class Src>
-__device__ void topk_any(SelShared& sh, uint32_t* lkey, int32_t* lidx, const Src& src, int n, int k, int32_t* out) {
+__device__ void topk_any(SelShared& sh, uint32_t* hist, uint32_t* lkey, int32_t* lidx, const Src& src, int n, int k,
+                         int32_t* out) {
   if (n <= kRegCap) {
-    topk_regs(sh, src, n, k, out);
+    topk_regs(sh, hist, src, n, k, out);
     return;
   }
   if constexpr (BIG) {
@@ -425,7 +558,7 @@ __device__ void topk_any(SelShared& sh, uint32_t* lkey, int32_t* lidx, const Src
 
 template <bool BIG>
 struct SelLds {
-  uint32_t key[BIG ? kRegCap : 1];
+  __attribute__((aligned(16))) uint32_t key[BIG ? kRegCap : 1];
   int32_t idx[BIG ? kRegCap : 1];
 };
 
@@ -442,8 +575,6 @@ struct SelLds {
 // each with 256 digit bins and one dump slot per lane of the copy for the
 // keys outside the current prefix, so every lane adds unconditionally (a
 // wave's LDS operations execute in order).
-constexpr int kHistCopies = 8;
-constexpr int kHistStride = 256 + 64 / kHistCopies;  // words per copy: bins + dump slots
 
 template <int E>
 __device__ RadixResult wave_radix(uint32_t* hist, const uint32_t (&key)[E], int n, uint32_t rank) {
@@ -521,146 +652,6 @@ __device__ RadixResult wave_radix(uint32_t* hist, const uint32_t (&key)[E], int 
     hi = shift - 1;
   }
   return r;
-}
-
-// Block-wide form of wave_radix over the register keys of all kSelThreads
-// threads (slots e < eslots, wave-uniform; 0 = empty): the bits all keys
-// share are decided from a block min/max, then 8-bit digits, counted into
-// kHistCopies copies per wave (each lane into copy lane % kHistCopies of its
-// wave's set, so lanes with equal digits mostly hit different words), and
-// every wave picks the digit from the summed copies itself. A plain block
-// radix sent all of a row's keys to one or two bins in its first passes
-// (scores share their sign and leading exponent bits), and the LDS atomics
-// of a wave to one word serialise. `hist` holds kBlkHistWords words; the
-// min/max exchange uses sh.wave_tot and sh.cnt.
-constexpr int kBlkHistWords = kSelWaves * kHistCopies * kHistStride;
-
-template <int E>
-__device__ RadixResult block_radix(SelShared& sh, uint32_t* hist, const uint32_t (&key)[E], int eslots,
-                                   uint32_t rank) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  uint32_t kmax = 0u, kmin = 0xffffffffu;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    kmax = key[e] > kmax ? key[e] : kmax;
-    kmin = (key[e] && key[e] < kmin) ? key[e] : kmin;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t a = (uint32_t)__shfl_xor((int)kmax, o, 64), c = (uint32_t)__shfl_xor((int)kmin, o, 64);
-    kmax = a > kmax ? a : kmax;
-    kmin = c < kmin ? c : kmin;
-  }
-  if (lane == 0) {
-    sh.wave_tot[wave] = kmax;
-    sh.cnt[wave] = kmin;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    kmax = sh.wave_tot[w] > kmax ? sh.wave_tot[w] : kmax;
-    kmin = sh.cnt[w] < kmin ? sh.cnt[w] : kmin;
-  }
-  RadixResult r{kmax, 0xffffffffu, rank, false};
-  const uint32_t diff = kmax ^ kmin;
-  if (diff == 0u) {  // every key equal: the first `rank` in index order
-    __syncthreads();  // the exchange words are read before anyone reuses them
-    return r;
-  }
-  int hi = 31 - __builtin_clz(diff);
-  r.mask = hi == 31 ? 0u : ~((2u << hi) - 1u);
-  r.prefix = kmax & r.mask;
-  uint32_t* my = hist + (wave * kHistCopies + lane % kHistCopies) * kHistStride;
-#pragma unroll 1
-  while (hi >= 0) {
-    const int shift = imax(hi - 7, 0);
-    const uint32_t dmask = (2u << (hi - shift)) - 1u;
-    __syncthreads();  // earlier readers of this LDS (the previous pass, or the caller's) are done
-    for (int i = threadIdx.x; i < kBlkHistWords / 4; i += kSelThreads)
-      reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    const uint32_t lim = hi == 31 ? 0xffffffffu : (2u << hi) - 1u;
-    const uint32_t dump = 256u + (uint32_t)(lane / kHistCopies);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (e < eslots) {  // wave-uniform
-        const uint32_t d = key[e] - r.prefix;
-        atomicAdd(&my[(key[e] != 0u && d <= lim) ? d >> shift : dump], 1u);
-      }
-    }
-    __syncthreads();
-    // lane l owns digits 255 - 4l - q (descending): bins 252 - 4l .. 255 - 4l
-    u32x4 cv = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int cp = 0; cp < kSelWaves * kHistCopies; ++cp)
-      cv += *reinterpret_cast<const u32x4*>(hist + cp * kHistStride + 252 - 4 * lane);
-    const uint32_t c[4] = {cv[3], cv[2], cv[1], cv[0]};
-    const int local = (int)(c[0] + c[1] + c[2] + c[3]);
-    const int incl = wave_incl_scan(local);
-    const uint64_t hit = ballot((uint32_t)incl >= r.need);
-    const int L = __builtin_ctzll(hit);  // first lane reaching the rank
-    uint32_t acc = (uint32_t)(incl - local), dsel = 0u, gt = 0u, eq = 0u;
-    bool found = false;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (!found && acc + c[q] >= r.need) {
-        found = true;
-        dsel = 255u - 4u * (uint32_t)lane - (uint32_t)q;
-        gt = acc;
-        eq = c[q];
-      }
-      acc += c[q];
-    }
-    dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, L);
-    gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
-    eq = (uint32_t)__builtin_amdgcn_readlane((int)eq, L);
-    r.prefix |= dsel << shift;
-    r.mask |= dmask << shift;
-    r.need -= gt;
-    if (eq == r.need) {
-      r.take_all = true;
-      break;
-    }
-    hi = shift - 1;
-  }
-  return r;
-}
-
-// Exact top-k (k < n <= E * kSelThreads) of an index-ordered source, as
-// topk_regs_e but with block_radix; `hist` (kBlkHistWords words) may alias
-// the source's key array: every key is in registers before its first clear.
-template <int E, class Src>
-__device__ void topk_regs_blk(SelShared& sh, uint32_t* hist, const Src& src, int n, int k, int32_t* out) {
-  const int run = (n + kSelThreads - 1) / kSelThreads;
-  const int beg = threadIdx.x * run;
-  uint32_t key[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (e < run && beg + e < n) ? src.key(beg + e) : 0u;
-  const RadixResult r = block_radix<E>(sh, hist, key, run, (uint32_t)k);
-  uint32_t ngt = 0, neq = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (!key[e]) continue;
-    const uint32_t km = key[e] & r.mask;
-    ngt += km > r.prefix;
-    neq += km == r.prefix;
-  }
-  const uint32_t excl = block_excl_scan(sh, ngt | (neq << 16));
-  const uint32_t eq_before = excl >> 16;
-  uint32_t pos = (excl & 0xffffu) + (r.take_all ? eq_before : (eq_before < r.need ? eq_before : r.need));
-  uint32_t eq_rank = eq_before;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (!key[e]) continue;
-    const uint32_t km = key[e] & r.mask;
-    bool sel = km > r.prefix;
-    if (km == r.prefix) {
-      sel = r.take_all || eq_rank < r.need;
-      ++eq_rank;
-    }
-    if (sel) out[pos++] = src.index(beg + e);
-  }
 }
 
 constexpr int kWaveE = 80;  // candidates per lane of the wave path (rows of up to 5120)
@@ -741,7 +732,8 @@ __global__ __launch_bounds__(256, 3) void select_prefill_wave_kernel(SelectParam
 // path queued): buffer path when the candidate count proves the buffer holds
 // the top k, exact rescan otherwise.
 template <bool BIG>
-__device__ void select_prefill_row(const SelectParams& P, int64_t row, SelShared& sh, SelLds<BIG>& lds, float* qs) {
+__device__ void select_prefill_row(const SelectParams& P, int64_t row, SelShared& sh, uint32_t* hist, SelLds<BIG>& lds,
+                                   float* qs) {
   const int g = (int)(row % P.Hkv);
   const int64_t bt = row / P.Hkv;
   const int t = (int)(bt % P.n_q);
@@ -761,7 +753,7 @@ __device__ void select_prefill_row(const SelectParams& P, int64_t row, SelShared
       for (int i = threadIdx.x; i < cnt; i += kSelThreads) out[i] = src.index(i);
       return;
     }
-    topk_any<BIG>(sh, lds.key, lds.idx, src, cnt, P.top_k, out);
+    topk_any<BIG>(sh, hist, lds.key, lds.idx, src, cnt, P.top_k, out);
     return;
   }
   // Exact rescan of every candidate.
@@ -776,7 +768,7 @@ __device__ void select_prefill_row(const SelectParams& P, int64_t row, SelShared
   if (P.lse && threadIdx.x < G) ls[threadIdx.x] = P.lse[((int64_t)b * P.Hq + g * G + threadIdx.x) * P.n_q + t];
   __syncthreads();
   RescanSrc src{qs, P.kv.slab(b, g), P.kv.st, G, P.scale, P.lse ? ls : nullptr};
-  topk_any<BIG>(sh, lds.key, lds.idx, src, ncand, P.top_k, out);
+  topk_any<BIG>(sh, hist, lds.key, lds.idx, src, ncand, P.top_k, out);
   if (threadIdx.x == 0 && P.rescan_count) atomicAdd(P.rescan_count, 1u);
 }
 
@@ -785,10 +777,12 @@ template <bool BIG>
 __global__ __launch_bounds__(kSelThreads) void select_prefill_deferred_kernel(SelectParams P) {
   __shared__ SelShared sh;
   __shared__ SelLds<BIG> lds;
+  __shared__ __attribute__((aligned(16))) uint32_t hist_own[BIG ? 4 : kBlkHistWords];
   __shared__ float qs[8 * kHeadDim + 8];
+  uint32_t* const hist = BIG ? lds.key : hist_own;  // BIG: the histograms overlay the key array
   const uint32_t n = *reinterpret_cast<volatile const uint32_t*>(P.defer_count);
   for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
-    select_prefill_row<BIG>(P, P.defer_rows[li], sh, lds, qs);
+    select_prefill_row<BIG>(P, P.defer_rows[li], sh, hist, lds, qs);
     __syncthreads();
   }
 }
@@ -801,6 +795,7 @@ __global__ __launch_bounds__(kSelThreads) void select_prefill_deferred_kernel(Se
 // the wave selection path, when samples exist) get theta = -inf.
 __global__ __launch_bounds__(kSelThreads) void threshold_kernel(ThresholdParams P) {
   __shared__ SelShared sh;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBlkHistWords];
   const int64_t row = blockIdx.x;
   if (row == 0 && threadIdx.x == 0 && P.defer_count) P.defer_count[0] = P.defer_count[1] = 0u;
   const int64_t bt = row / P.Hkv;
@@ -821,13 +816,29 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(ThresholdParams 
     return;
   }
   DenseSrc src{P.samples + row * (int64_t)P.max_samples};
-  if (nsamp <= kRegCap) {
-    const int E = (nsamp + kSelThreads - 1) / kSelThreads;
-    const int beg = threadIdx.x * E;
-    uint32_t key[kE];
+  constexpr int kThrE = 64;  // samples per thread in registers: rows of up to 16384 samples
+  if (nsamp <= kThrE * kSelThreads) {
+    // thread t holds samples 4(t + 256e) .. +3: 16-byte loads, coalesced
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(src.s, 4u * (uint32_t)nsamp);
+    const int slots = (nsamp + 4 * kSelThreads - 1) / (4 * kSelThreads);  // 16-byte loads holding samples
+    // all loads first and unconditionally (past the row: range-checked, read as 0), then the keys
+    u32x4 v[kThrE / 4];
 #pragma unroll
-    for (int e = 0; e < kE; ++e) key[e] = (e < E && beg + e < nsamp) ? src.key(beg + e) : 0u;
-    const RadixResult r = radix_regs<kE>(sh, key, (uint32_t)m);
+    for (int e = 0; e < kThrE / 4; ++e) v[e] = buf_ld16(rs, 16u * (uint32_t)((int)threadIdx.x + kSelThreads * e));
+    uint32_t key[kThrE];
+#pragma unroll
+    for (int e = 0; e < kThrE / 4; ++e)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        key[4 * e + q] = score_key_if(__uint_as_float(v[e][q]), 4 * ((int)threadIdx.x + kSelThreads * e) + q < nsamp);
+    RadixResult r;
+    if (m <= 4 * kSelThreads) {
+      uint32_t t4[4];
+      top4_regs<kThrE>(key, t4);
+      r = block_radix<4>(sh, hist, t4, 4, (uint32_t)m);
+    } else {
+      r = block_radix<kThrE>(sh, hist, key, 4 * slots, (uint32_t)m);
+    }
     // take_all leaves the low bits open: prefix is then a lower bound
     if (threadIdx.x == 0) P.theta[row] = key_to_score(r.prefix);
   } else {
@@ -886,7 +897,7 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecode
     return;
   }
   DenseSrc src{P.sigma + (int64_t)row * P.sigma_stride};
-  topk_any<true>(sh, lds.key, lds.idx, src, ncand, P.top_k, out);
+  topk_any<true>(sh, lds.key, lds.key, lds.idx, src, ncand, P.top_k, out);
 }
 
 // ---------------------------------------------------------------- decode, long rows
@@ -956,15 +967,23 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_threshold_kernel(Se
   // thread t holds samples 4(t + 256e) .. +3: contiguous 16-byte loads
   constexpr int ES = kDecSamples / kSelThreads;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc_sized(P.samp + (int64_t)row * kDecSamples, 4u * (uint32_t)nsamp);
+  u32x4 v[ES / 4];  // all loads first (past the samples: range-checked, read as 0), then the keys
+#pragma unroll
+  for (int e = 0; e < ES / 4; ++e) v[e] = buf_ld16(rs, 16u * (uint32_t)((int)threadIdx.x + kSelThreads * e));
   uint32_t skey[ES];
 #pragma unroll
-  for (int e = 0; e < ES / 4; ++e) {
-    const int i = 4 * ((int)threadIdx.x + kSelThreads * e);
-    const u32x4 v = buf_ld16(rs, 4u * (uint32_t)i);
+  for (int e = 0; e < ES / 4; ++e)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) skey[4 * e + q] = i + q < nsamp ? score_key(__uint_as_float(v[q])) : 0u;
+    for (int q = 0; q < 4; ++q)
+      skey[4 * e + q] = score_key_if(__uint_as_float(v[e][q]), 4 * ((int)threadIdx.x + kSelThreads * e) + q < nsamp);
+  RadixResult rr;
+  if (m <= 4 * kSelThreads) {  // the union of per-thread top fours (a lower bound, usually exact)
+    uint32_t t4[4];
+    top4_regs<ES>(skey, t4);
+    rr = block_radix<4>(sh, hist, t4, 4, (uint32_t)m);
+  } else {
+    rr = block_radix<ES>(sh, hist, skey, ES, (uint32_t)m);
   }
-  const RadixResult rr = block_radix<ES>(sh, hist, skey, ES, (uint32_t)m);
   // keys >= prefix include the m largest samples (take_all leaves the low
   // bits of prefix zero: still a lower bound)
   if (threadIdx.x == 0) P.theta_key[row] = rr.prefix;
@@ -1073,7 +1092,7 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
   }
   const DenseSrc dense{r.s};
   if (r.ncand <= kRegCap) {
-    topk_regs_blk<kE>(sh, lds.key, dense, r.ncand, k, out);
+    topk_regs_e<kE>(sh, lds.key, dense, r.ncand, k, out);
     return;
   }
   const int ns = (r.ncand + kDecSlice - 1) / kDecSlice;  // <= nslices <= kMaxDecSlices
@@ -1094,25 +1113,42 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
     topk_stream(sh, dense, r.ncand, k, out);
     return;
   }
-  for (uint32_t i = threadIdx.x; i < total; i += kSelThreads) {
-    int lo = 0, hi = ns;  // the last slice whose offset is <= i
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (lds.off[mid] <= i) lo = mid;
-      else hi = mid;
+  // survivors into LDS in batches of 8 per thread: the batch's reads are
+  // issued together (positions past the end re-read the last survivor)
+  constexpr int kCopyBatch = 8;
+  for (uint32_t i0 = 0; i0 < total; i0 += kCopyBatch * kSelThreads) {
+    uint32_t kk[kCopyBatch];
+    int32_t jj[kCopyBatch];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const uint32_t i = imin((int)(i0 + u * kSelThreads + threadIdx.x), (int)total - 1);
+      int lo = 0, hi = ns;  // the last slice whose offset is <= i
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (lds.off[mid] <= i) lo = mid;
+        else hi = mid;
+      }
+      const int64_t src = ((int64_t)row * P.nslices + lo) * kDecSlice + (i - lds.off[lo]);
+      kk[u] = P.seg_key[src];
+      jj[u] = P.seg_idx[src];
     }
-    const int64_t src = ((int64_t)row * P.nslices + lo) * kDecSlice + (i - lds.off[lo]);
-    lds.key[i] = score_key(__uint_as_float(P.seg_key[src]));
-    lds.idx[i] = P.seg_idx[src];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const uint32_t i = i0 + u * kSelThreads + threadIdx.x;
+      if (i < total) {
+        lds.key[i] = score_key(__uint_as_float(kk[u]));
+        lds.idx[i] = jj[u];
+      }
+    }
   }
   __syncthreads();
   const LdsSrc ls{lds.key, lds.idx};
   if (total == (uint32_t)k) {
     for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = lds.idx[i];
   } else if (total <= (uint32_t)kRegCap) {
-    topk_regs_blk<kE>(sh, lds.key, ls, (int)total, k, out);  // the histograms overlay the keys once in registers
+    topk_regs_e<kE>(sh, lds.key, ls, (int)total, k, out);  // the histograms overlay the keys once in registers
   } else {
-    topk_regs_blk<kDecCandCap / kSelThreads>(sh, lds.key, ls, (int)total, k, out);
+    topk_regs_e<kDecCandCap / kSelThreads>(sh, lds.key, ls, (int)total, k, out);
   }
 }
 
@@ -1297,7 +1333,7 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks_kernel(BlockSelectP
   if (br.nblk <= br.nb) {
     for (int i = threadIdx.x; i < br.nblk; i += kSelThreads) chosen[i] = i;
   } else {
-    topk_any<true>(sh, lds.key, lds.idx, DenseSrc{P.blk_score + row * P.blk_stride}, br.nblk, br.nb, chosen);
+    topk_any<true>(sh, lds.key, lds.key, lds.idx, DenseSrc{P.blk_score + row * P.blk_stride}, br.nblk, br.nb, chosen);
     nsel = br.nb;
   }
   __syncthreads();
