@@ -112,6 +112,15 @@ def test_large_k_buffer_path():
     run(1, n, n, 8, 1, 3000, 64, seed=800, rows=rows)
 
 
+def test_large_k_wave128_rows():
+    """k > 2560: sampled rows keep about 1.77 k > 5120 candidates, which the
+    one-wave selection takes with 128 register slots per lane (rows of up to
+    8192) instead of queueing them for the block-wide path."""
+    n = 16000
+    rows = [9300, 10000, 11111, 12500, 14000, 15000, 15999]
+    run(1, n, n, 8, 1, 3000, 64, seed=810, rows=rows)
+
+
 def test_rescan_streaming_long_rows():
     """Exact rescan of rows longer than the register capacity."""
     n = 9500

@@ -654,7 +654,8 @@ __device__ RadixResult wave_radix(uint32_t* hist, const uint32_t (&key)[E], int 
   return r;
 }
 
-constexpr int kWaveE = 80;  // candidates per lane of the wave path (rows of up to 5120)
+constexpr int kWaveE = 80;       // candidates per lane of the wave path (rows of up to 5120)
+constexpr int kWaveEBig = 128;   // the same for calls whose rows expect more (rows of up to 8192)
 
 // One wave per (b, t, g) row: the candidate buffer is read lane-strided
 // (coalesced) into registers, the k-th key is found by wave_radix, and the
@@ -662,7 +663,8 @@ constexpr int kWaveE = 80;  // candidates per lane of the wave path (rows of up 
 // register slot (ties at the k-th key are taken in token order). Rows the
 // wave path cannot take (forced rescan, a count outside [k, cap], or more
 // candidates than it holds) are queued for the block-wide path.
-__global__ __launch_bounds__(256, 3) void select_prefill_wave_kernel(SelectParams P, int64_t rows) {
+template <int E>  // register slots per lane: rows of up to 64 * E candidates
+__global__ __launch_bounds__(256, E > kWaveE ? 2 : 3) void select_prefill_wave_kernel(SelectParams P, int64_t rows) {
   __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kHistCopies * kHistStride];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -680,7 +682,7 @@ __global__ __launch_bounds__(256, 3) void select_prefill_wave_kernel(SelectParam
     return;
   }
   const int cnt = uniform(P.counts[row]);
-  if (P.force_rescan || cnt < k || cnt > P.cap || cnt > 64 * kWaveE) {
+  if (P.force_rescan || cnt < k || cnt > P.cap || cnt > 64 * E) {
     if (lane == 0) P.defer_rows[atomicAdd(P.defer_count, 1u)] = (int32_t)row;
     return;
   }
@@ -693,19 +695,19 @@ __global__ __launch_bounds__(256, 3) void select_prefill_wave_kernel(SelectParam
     for (int i = lane; i < k; i += 64) out[i] = P.buf_j[row * (int64_t)P.cap + i];
     return;
   }
-  uint32_t key[kWaveE];
+  uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < kWaveE; ++e) {  // slots past the count: no load issued (wave-uniform branch)
+  for (int e = 0; e < E; ++e) {  // slots past the count: no load issued (wave-uniform branch)
     key[e] = 0u;
     if (64 * e < cnt) key[e] = buf_ld4(rs_s, 4u * (uint32_t)lane + 256u * (uint32_t)e);
   }
 #pragma unroll
-  for (int e = 0; e < kWaveE; ++e) key[e] = 64 * e + lane < cnt ? score_key(__uint_as_float(key[e])) : 0u;
-  const RadixResult r = wave_radix<kWaveE>(hist_all[wave], key, cnt, (uint32_t)k);
+  for (int e = 0; e < E; ++e) key[e] = 64 * e + lane < cnt ? score_key(__uint_as_float(key[e])) : 0u;
+  const RadixResult r = wave_radix<E>(hist_all[wave], key, cnt, (uint32_t)k);
   uint32_t out_run = 0, eq_run = 0;
   constexpr int kGroup = 8;  // index loads in flight per step (bounds register use)
 #pragma unroll
-  for (int e0 = 0; e0 < kWaveE; e0 += kGroup) {
+  for (int e0 = 0; e0 < E; e0 += kGroup) {
     if (64 * e0 >= cnt) continue;  // (not break: the loop stays fully unrolled)
     uint32_t j[kGroup];
 #pragma unroll
@@ -1488,7 +1490,13 @@ hipError_t launch_block_max(const BlockMaxParams& p, hipStream_t s) {
 }
 
 hipError_t launch_select_prefill(const SelectParams& p, int64_t rows, hipStream_t s) {
-  select_prefill_wave_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
+  // Sampled rows keep about 1.77 k candidates: past what 80 slots per lane
+  // hold from k ~ 2600 on (k = 4096 at the 1M context: ~7300), where every
+  // row would otherwise go to the block-wide path.
+  if (p.top_k > 2560)
+    select_prefill_wave_kernel<kWaveEBig><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
+  else
+    select_prefill_wave_kernel<kWaveE><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)std::min<int64_t>(rows, 1024);
