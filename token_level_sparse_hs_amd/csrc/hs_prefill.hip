@@ -442,17 +442,34 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     } else if (sel_tile) {
       const float* ws = sig[wave];
       const int j = key0 + lane;
+      // The candidate test is one compare: past a token's last candidate key
+      // the lane compares against +inf (its score is finite, or -inf where
+      // causally masked), so the ballot is the compare's own lane mask. Tiles
+      // wholly inside every token's candidate range (all but those at the
+      // window's edge) skip the limit.
+      auto compact = [&](auto all_cand_c) __attribute__((always_inline)) {
+        constexpr bool kAllCand = decltype(all_cand_c)::value;
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        const float v = ws[u * 64 + lane] * P.scale;
-        const bool pass = j <= off + wt0 + u - P.window && v >= theta[u];
-        const uint64_t m = ballot(pass);
-        const uint32_t off = pass ? 4u * ((uint32_t)cnt[u] + lane_prefix(m)) : kDropOffset;
-        const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap;  // wave-uniform row base
-        buf_st4(make_rsrc_sized(P.buf_sigma + rb, 4u * (uint32_t)P.cap), off, __float_as_uint(v));
-        buf_st4(make_rsrc_sized(P.buf_j + rb, 4u * (uint32_t)P.cap), off, (uint32_t)j);
-        cnt[u] = uniform(cnt[u] + __popcll(m));
-      }
+        for (int u = 0; u < TPW; ++u) {
+          const float v = ws[u * 64 + lane] * P.scale;
+          const float th = kAllCand || j <= off + wt0 + u - P.window ? theta[u] : kPosInf;
+          const bool pass = v >= th;
+          const uint64_t m = ballot(pass);
+          const uint32_t so = pass ? 4u * lane_prefix(m) : kDropOffset;
+          // the row's next free entry and the room left, in the (scalar)
+          // descriptors: entries past the buffer's capacity fail the range check
+          const int c = uniform(cnt[u]);
+          const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap + c;
+          const uint32_t room = 4u * (uint32_t)imax(0, P.cap - c);
+          buf_st4(make_rsrc_sized(P.buf_sigma + rb, room), so, __float_as_uint(v));
+          buf_st4(make_rsrc_sized(P.buf_j + rb, room), so, (uint32_t)j);
+          cnt[u] = uniform(c + __popcll(m));
+        }
+      };
+      if (uniform(key0 + 63 <= off + wt0 - P.window ? 1 : 0))  // a scalar branch
+        compact(std::true_type{});
+      else
+        compact(std::false_type{});
     }
   };
 
