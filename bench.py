@@ -338,14 +338,19 @@ def cpu_baseline(c, args, w, case, dec_data):
     t_row = rows_time([w.n_q - 1])
     R = int(max(2, min(256, args.cpu_seconds / max(t_row, 1e-4))))
     rows = sorted(set(int(x) for x in np.linspace(0, w.n_q - 1, R)))
-    t = rows_time(rows)
+    t_rows = rows_time(rows)
     st = dec_data[0]
     t0 = time.perf_counter()
     orc.decode_step(st["q_full"][0].float().cpu().numpy(), [x[0].float().cpu().numpy() for x in st["q_sparse"]],
                     st["kv_new"][0].float().cpu().numpy(), K, V, n + 1, w.top_k, w.window, scale)
-    t += time.perf_counter() - t0
+    t_dec = time.perf_counter() - t0
+    t = t_rows + t_dec
+    # the whole step at the sample's per-row and per-decode-step cost (the
+    # chunk's rows all attend over about a million keys, so they cost alike)
+    full = t_rows / len(rows) * w.n_q + t_dec * w.decode_steps
     return {"value": round((len(rows) + 1) / t, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "cpu": cpu_model(), "host_cpus": os.cpu_count(),
+            "step_s_extrapolated": round(full, 1),
             "sample": f"{len(rows)} query rows evenly spaced over the {w.n_q}-row chunk of the 1M-token workload "
                       f"(full layer + selection + {len(qs)} sparse layers each) and 1 decode step "
                       f"(full layer + selection + {len(qs)} sparse layers), {t:.1f} s of CPU time"}
