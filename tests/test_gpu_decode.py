@@ -117,6 +117,34 @@ def test_decode_sampled_threshold_overshoot():
     assert sum(int(j) in planted for j in ref["idx"][0]) > k // 2
 
 
+@pytest.mark.parametrize("tail", [1, 2, 3])
+def test_decode_filter_ragged_tail_keeps_last_keys(tail):
+    """The sliced selection reads score rows in 16-byte pieces; when |C(p)| is
+    not a multiple of 4 the last piece runs past the row's range. Keys planted
+    at the row's last `tail` candidates, aimed at the queries, are the top of
+    the row and must all be selected (and the rest must match the oracle)."""
+    W, k, Hq, Hkv = 64, 256, 4, 1
+    ncand = 20000 + tail
+    L = ncand + W - 1  # after the append, p = L and |C(p)| = L - W + 1 = ncand
+    print(f"[case] decode ragged tail ncand={ncand}", flush=True)
+    kv = torch.zeros((1, Hkv, L + 1, 2, 128), dtype=torch.bfloat16, device=DEV)
+    kv[0, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 91 + tail, DEV)
+    q = synth.randn_bf16((1, Hq, 128), 92 + tail, DEV)
+    u = q[0].float().sum(0)
+    u = u / u.norm() * (128 ** 0.5)
+    planted = list(range(ncand - tail, ncand))
+    kv[0, 0, planted, 0] = (2.0 * u).to(torch.bfloat16)
+    kv_new = synth.randn_bf16((1, Hkv, 2, 128), 93 + tail, DEV)
+    seq_lens = torch.tensor([L + 1], dtype=torch.int32, device=DEV)
+    o, lse, idx = hs.decode_step(q, kv_new, kv, seq_lens, L + 1, top_k=k, window=W)
+    torch.cuda.synchronize()
+    Ks, Vs = kv[0, :, :, 0].float().cpu().numpy(), kv[0, :, :, 1].float().cpu().numpy()
+    ref = orc.decode_step(f32(q[0]), [], f32(kv_new[0]), Ks, Vs, L + 1, k, W, orc.default_scale(128))
+    got = idx.cpu().numpy()[0, 0]
+    check_idx_row(got, ref["idx"][0], ref["sigma"][0], ref["tau"][0], L, W, k, where="ragged tail")
+    assert set(planted) <= set(int(j) for j in got), "a planted last candidate was not selected"
+
+
 def test_decode_streaming_select():
     """k close to the row length defeats the sample filter: streaming select."""
     run_decode([9000], 1, 4, 1, 8000, 16, seed=14, n_sparse=1)

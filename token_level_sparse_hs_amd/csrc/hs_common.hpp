@@ -214,7 +214,9 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
 // Buffer over [base, base + bytes): a store at an offset at or past `bytes`
 // is discarded and a load there returns 0 (hardware range check), so lanes
 // that must not access memory still execute the instruction (no divergent
-// branch around it).
+// branch around it). The check is per 4-byte element: a 16-byte load that
+// runs past `bytes` returns its elements below `bytes` and 0 for the rest
+// (the decode selection's ragged-tail test relies on it).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_sized(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
