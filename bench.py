@@ -100,12 +100,18 @@ def mfma_roof(flops, us, kernel):
 # ---------------------------------------------------------------- traffic
 
 def device_source_hash():
-    """sha256 over the kernel sources (the HIP files and the headers they include)."""
+    """sha256 over the kernel sources (the HIP files and the headers they
+    include), comments and blank lines removed: a comment edit leaves the
+    code, and so the counters taken on it, unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "token_level_sparse_hs_amd", "csrc")
     for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        text = open(p).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
         h.update(os.path.basename(p).encode())
-        h.update(open(p, "rb").read())
+        h.update(code.encode())
     return h.hexdigest()
 
 
