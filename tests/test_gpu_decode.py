@@ -87,7 +87,7 @@ def test_decode_long_rows_filtered_select():
 
 def test_decode_sampled_threshold_overshoot():
     """Long rows are filtered by the m-th largest of their samples: every
-    2^s-th candidate score, s >= 2 the smallest shift leaving at most 8192
+    2^s-th candidate score, s >= 2 the smallest shift leaving at most 16384
     of them. Keys placed exactly at the sampled positions and aimed at the
     queries push that threshold above the row's k-th score, so fewer than k
     keys survive the filter: the selection must fall back to the whole row
@@ -101,7 +101,7 @@ def test_decode_sampled_threshold_overshoot():
     u = u / u.norm() * (128 ** 0.5)
     ncand = L - W + 1  # candidates of the row after the append (p = L)
     shift = 2
-    while -(-ncand // (1 << shift)) > 8192:
+    while -(-ncand // (1 << shift)) > 16384:
         shift += 1
     pos = torch.arange(0, ncand, 1 << shift, device=DEV)
     noise = synth.randn_bf16((len(pos), 128), 83, DEV).float()

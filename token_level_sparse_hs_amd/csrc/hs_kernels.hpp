@@ -108,7 +108,7 @@ constexpr int kMaxDecSlices = 4096;
 // sliced threshold: scores at j = 2^s * i for i < ceil(|C| / 2^s), with s the
 // smallest shift of at least 2 leaving at most kDecSamples of them. A shift
 // of at least 2 puts each sample at the start of an aligned 4-key piece.
-constexpr int kDecSamples = 8192;
+constexpr int kDecSamples = 16384;
 __host__ __device__ __forceinline__ int dec_sample_shift(int ncand) {
   int s = 2;
   while (((ncand + (1 << s) - 1) >> s) > kDecSamples) ++s;

@@ -909,7 +909,7 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_kernel(SelectDecode
 // one sequence has only Hkv such rows. Three launches spread it over the chip:
 //  1. threshold: one block per row reads the row's S samples (every 2^s-th
 //     key, at most kDecSamples, written beside the score row by the kernel
-//     that produced it, so this reads 32 KB instead of the row) and takes
+//     that produced it, so this reads 64 KB instead of the row) and takes
 //     their m-th largest, m = mu + 6 sqrt(mu) + 1 with mu = k S / n the
 //     expected number of samples among the row's top k, so that the k-th
 //     largest key of the row lies at or above it with overwhelming
