@@ -1115,29 +1115,51 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
     topk_stream(sh, dense, r.ncand, k, out);
     return;
   }
-  // survivors into LDS in batches of 8 per thread: the batch's reads are
-  // issued together (positions past the end re-read the last survivor)
-  constexpr int kCopyBatch = 8;
-  for (uint32_t i0 = 0; i0 < total; i0 += kCopyBatch * kSelThreads) {
-    uint32_t kk[kCopyBatch];
-    int32_t jj[kCopyBatch];
+  // Survivors into LDS: thread t copies the contiguous run [t*run, t*run +
+  // run) of the concatenation (the run the register selection below reads
+  // back). One binary search over the slice offsets finds the run's first
+  // slice; a walk then crosses slice boundaries in order, and every read of
+  // a group is issued before the first is used. (A binary search per element
+  // chained about nine dependent LDS reads per survivor: most of this
+  // kernel's time at the 1M context.)
+  const int run = uniform((int)((total + kSelThreads - 1) / kSelThreads));
+  const int beg = (int)threadIdx.x * run;
+  int sl = 0;  // the last slice whose offset is <= the run's first position
+  {
+    const uint32_t b0 = (uint32_t)imin(beg, (int)total - 1);
+    int hi = ns;
+    while (hi - sl > 1) {
+      const int mid = (sl + hi) >> 1;
+      if (lds.off[mid] <= b0) sl = mid;
+      else hi = mid;
+    }
+  }
+  uint32_t sbase = lds.off[sl], next = lds.off[sl + 1];  // the slice's first position, the next slice's
+  const int64_t seg0 = (int64_t)row * P.nslices * kDecSlice;
+  constexpr int kCopyGroup = 16;
+  for (int e0 = 0; e0 < run; e0 += kCopyGroup) {
+    uint32_t src[kCopyGroup];
 #pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      const uint32_t i = imin((int)(i0 + u * kSelThreads + threadIdx.x), (int)total - 1);
-      int lo = 0, hi = ns;  // the last slice whose offset is <= i
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (lds.off[mid] <= i) lo = mid;
-        else hi = mid;
+    for (int u = 0; u < kCopyGroup; ++u) {
+      const uint32_t i = (uint32_t)imin(beg + e0 + u, (int)total - 1);  // past the run: re-read the last
+      while (i >= next) {  // into the following slice (empty slices skipped; off[ns] = total ends it)
+        ++sl;
+        sbase = next;
+        next = lds.off[sl + 1];
       }
-      const int64_t src = ((int64_t)row * P.nslices + lo) * kDecSlice + (i - lds.off[lo]);
-      kk[u] = P.seg_key[src];
-      jj[u] = P.seg_idx[src];
+      src[u] = (uint32_t)sl * kDecSlice + (i - sbase);
+    }
+    uint32_t kk[kCopyGroup];
+    int32_t jj[kCopyGroup];
+#pragma unroll
+    for (int u = 0; u < kCopyGroup; ++u) {
+      kk[u] = P.seg_key[seg0 + src[u]];
+      jj[u] = P.seg_idx[seg0 + src[u]];
     }
 #pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      const uint32_t i = i0 + u * kSelThreads + threadIdx.x;
-      if (i < total) {
+    for (int u = 0; u < kCopyGroup; ++u) {
+      const int i = beg + e0 + u;
+      if (e0 + u < run && i < (int)total) {
         lds.key[i] = score_key(__uint_as_float(kk[u]));
         lds.idx[i] = jj[u];
       }
