@@ -188,17 +188,85 @@ __device__ __forceinline__ void stage_group_max(const f32x16* acc, float* sig, f
   }
 }
 
+// The group maximum of stage_group_max in pieces, so that its steps can sit
+// between matrix instructions. gm_fold8 folds lane^8 for values [I0, I0+N)
+// into r, gm_fold4 lane^4 into r2, gm_fold2 lane^2 (G = 8); gm_store writes
+// the wave's rows of sig. Within a piece all first-form steps precede the
+// second-form ones, so no step reads a register written right before it;
+// callers keep each piece's sources at least one chunk (an MFMA, its operand
+// reads and a piece) behind their writes.
+template <int I0, int N>
+__device__ __forceinline__ void gm_fold8(const f32x16* acc, float* r, float dep) {
+#pragma unroll
+  for (int i = I0; i < I0 + N; ++i) HS_DPP_MAX_DEF(r[i], acc[1][i], 8, 0xc, dep);
+#pragma unroll
+  for (int i = I0; i < I0 + N; ++i) HS_DPP_MAX_UPD(r[i], acc[0][i], 8, 0x3, dep);
+}
+template <int I0, int N>
+__device__ __forceinline__ void gm_fold4(const float* r, float* r2, float dep) {
+#pragma unroll
+  for (int i = I0; i < I0 + N; ++i) HS_DPP_MAX_DEF(r2[i], r[8 + i], 4, 0xa, dep);
+#pragma unroll
+  for (int i = I0; i < I0 + N; ++i) HS_DPP_MAX_UPD(r2[i], r[i], 12, 0x5, dep);
+}
+__device__ __forceinline__ void gm_fold2(float* r2) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    asm volatile("v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(r2[i]));
+}
+// Row layout as in stage_group_max. For G = 8 the lanes q and q^2 hold equal
+// values for the same sig entries after gm_fold2, so every lane writes (the
+// duplicate writes store the same bytes) and no branch splits the schedule.
 template <int G>
+__device__ __forceinline__ void gm_store(const f32x16* acc, const float* r, const float* r2, float* sig) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, q = lane & 15;
+  if constexpr (G == 1) {
+    float* row = sig + (lane & 31) * 64;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(row + 32 * c + 8 * q4 + 4 * h) =
+            f32x4{acc[c][4 * q4], acc[c][4 * q4 + 1], acc[c][4 * q4 + 2], acc[c][4 * q4 + 3]};
+  } else {
+    const int c = (q >> 3) & 1;
+    float* trow = sig + tok_of<G>(lane & 31) * 64 + 32 * c + 4 * h;
+    if constexpr (G == 2) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(trow + 8 * q4) = f32x4{r[4 * q4], r[4 * q4 + 1], r[4 * q4 + 2], r[4 * q4 + 3]};
+    } else {
+      const int ih = (q >> 2) & 1;
+      *reinterpret_cast<f32x4*>(trow + 16 * ih) = f32x4{r2[0], r2[1], r2[2], r2[3]};
+      *reinterpret_cast<f32x4*>(trow + 16 * ih + 8) = f32x4{r2[4], r2[5], r2[6], r2[7]};
+    }
+  }
+}
+
+// SEL: 0 no selection, 1 token-level candidates, 2 block-level maxima.
+//
+// Software pipeline over 64-key tiles (one wave's view of tile i):
+//   A: S_i = K_i Q^T (16 MFMAs) beside the candidate compaction of tile
+//      i-1 (from the group maxima staged in LDS);
+//   B: causal mask and row maximum of S_i, then O += V_{i-1}^T P_{i-1}^T
+//      (16 MFMAs) beside the group maximum of S_i and P_i = exp2(...),
+//      summed and packed to bf16.
+// Each wave thus keeps its matrix pipe busy with vector work of its own
+// instead of relying on the other wave of its SIMD. V tiles are consumed one
+// tile after their K tiles: at tile i, K_{i+1} and V_i are fetched (into the
+// stages that K_{i-1} and V_{i-2} left), and one barrier per tile orders
+// everything. Rows whose maximum rises past the deferred-rescale slack finish
+// O += V_{i-1}^T P_{i-1}^T first, rescale, and let B add a zero P.
+template <int G, int SEL>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   constexpr int TPW = 32 / G;
   constexpr int TPB = 4 * TPW;
-  // K and V tiles of 64 keys, two stages, unpadded 256-byte rows written by
-  // direct global->LDS loads. 16-byte chunks are XOR-permuted within a row
+  // K and V tiles of 64 keys, two stages each, unpadded 256-byte rows written
+  // by direct global->LDS loads. 16-byte chunks are XOR-permuted within a row
   // so that both operand read patterns hit distinct banks: chunk c of K row r
   // sits at c ^ (r % 16) (16 rows read the same chunk), chunk c of V row r at
   // c ^ 4(r % 4) (the transpose reads take 4 rows x 64 bytes at a time).
-  // (one array per stage: distinct objects, so that reads of one stage are
-  // not made to wait for loads in flight into the other)
   __shared__ __attribute__((aligned(1024))) uint8_t kv_st0[2][kTileB];
   __shared__ __attribute__((aligned(1024))) uint8_t kv_st1[2][kTileB];
   __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
@@ -236,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   int cnt[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    const bool ok = P.select == 1 && wt0 + u < P.n_q;
+    const bool ok = SEL == 1 && wt0 + u < P.n_q;
     theta[u] = ok ? __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, P.theta[row0 + (int64_t)u * P.Hkv])))
                   : kPosInf;
     cnt[u] = 0;
@@ -257,7 +325,6 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   const uint16_t* slab = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<int64_t>(P.kv.slab(b, g))));
   const uint32_t rowb = 2u * (uint32_t)P.kv.st;
   const uint32_t span = (uint32_t)(P.n_kv - 1) * rowb + 2u * kHeadDim;  // bytes up to the last valid row's end
-  // Buffer descriptors (raw, range-checked) in scalar registers.
   const u32x4 krs = rsrc_words(slab, span);
   const u32x4 vrs = rsrc_words(slab + P.kv.voff, span);
   uint32_t dk[4], dv[4];
@@ -268,18 +335,21 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     dv[i] = r * rowb + 16u * ((lane & 15) ^ (4u * (r & 3)));
   }
   // The loads are issued from inline assembly, so the compiler does not
-  // treat them as LDS writes in flight (it would otherwise wait for all of
-  // them before every LDS access, the next tile's included); the tile wait
-  // and the barrier below order them explicitly.
-  auto fetch = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+  // treat them as LDS writes in flight; the tile wait and the barrier order
+  // them explicitly.
+  auto fetch_k = [&](int kt, auto stage_c) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
     const uint32_t soff = (uint32_t)uniform(kt * 64) * rowb;
-    const uint32_t base = lds_addr(S ? kv_st1 : kv_st0) + (uint32_t)(16 * wave) * kRowB;
+    const uint32_t base = lds_addr(S ? kv_st1[0] : kv_st0[0]) + (uint32_t)(16 * wave) * kRowB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lds_dma16(base + 4u * i * kRowB, dk[i], krs, soff);
-      lds_dma16(base + kTileB + 4u * i * kRowB, dv[i], vrs, soff);
-    }
+    for (int i = 0; i < 4; ++i) lds_dma16(base + 4u * i * kRowB, dk[i], krs, soff);
+  };
+  auto fetch_v = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
+    const uint32_t soff = (uint32_t)uniform(kt * 64) * rowb;
+    const uint32_t base = lds_addr(S ? kv_st1[1] : kv_st0[1]) + (uint32_t)(16 * wave) * kRowB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(base + 4u * i * kRowB, dv[i], vrs, soff);
   };
   // Operand read offsets within a tile. K (S^T = K Q^T, A operand): lane
   // (n, h) reads dims 16s + 8h .. +8 of key n (+32 for the second MFMA block).
@@ -293,57 +363,157 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     vad[bk] = (((lane & 15) >> 2) + 4 * h) * kRowB +
               16u * (4u * (bk ^ ((lane >> 2) & 3)) + 2u * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8u * (lane & 1);
 
-  // Candidate stores of the last tile still in flight: the wait for a tile's
-  // loads then allows that many later operations to remain outstanding
-  // (vector memory operations complete in order).
-  constexpr int kStores = 2 * TPW;
-  bool stores_pending = false;
+  // bf16 P of the last two tiles (B operands of O^T += V^T P^T), in turn.
+  u32x4 pbA[4], pbB[4];
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) pbA[s2] = pbB[s2] = u32x4{0u, 0u, 0u, 0u};
+
+  // Stores per tile of the compaction; the wait for a tile's loads lets them
+  // remain outstanding (vector memory operations complete in order).
+  constexpr int kStores = SEL == 1 ? 2 * TPW : 0;
+  constexpr int kTileWait = kStores < 63 ? kStores : 63;
+
+  // O^T += V^T P^T for one tile: MFMA m = 4 s2 + bk, A operand from two
+  // transpose reads (issued two products ahead), B = pb[s2]. FILL(m) places
+  // vector work of the caller after product m; each product and its work
+  // form one scheduling chunk.
+  auto pv = [&](const uint8_t* Vb, const u32x4* pb, auto&& fill) __attribute__((always_inline)) {
+    u32x2 vf[3][2];
+    auto vread = [&](int m, u32x2* dst) __attribute__((always_inline)) {
+      const int s2 = m >> 2, bk = m & 3;
+      const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1);
+      dst[0] = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + kb * kRowB + vad[bk]));
+      dst[1] = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + (kb + 8) * kRowB + vad[bk]));
+    };
+    vread(0, vf[0]);
+    vread(1, vf[1]);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      if (m + 2 < 16) vread(m + 2, vf[(m + 2) % 3]);
+      const int s2 = m >> 2, bk = m & 3;
+      const u32x4 w = {vf[m % 3][0][0], vf[m % 3][0][1], vf[m % 3][1][0], vf[m % 3][1][1]};
+      oacc[bk] = mfma32x32x16(as_bf16x8(w), as_bf16x8(pb[s2]), oacc[bk]);
+      fill(m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Candidate compaction of the tile at key0p for row u (token-level
+  // selection): every candidate key whose score reaches the row's threshold
+  // is appended, in ascending key order, to the row's buffer. Past a token's
+  // last candidate key (and for tiles without candidates: lim = -1) the lane
+  // compares against +inf, so the ballot is the compare's own lane mask.
+  // Exactly two range-checked stores: failing lanes and positions past the
+  // buffer's capacity aim beyond the row and are dropped.
+  auto compact_row = [&](int u, float sv, int key0p, int lim) __attribute__((always_inline)) {
+    const float v = sv * P.scale;
+    const float th = lane <= lim ? theta[u] : kPosInf;
+    const bool pass = v >= th;
+    const uint64_t m = ballot(pass);
+    const uint32_t so = pass ? 4u * lane_prefix(m) : kDropOffset;
+    const int c = uniform(cnt[u]);
+    const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap + c;
+    const uint32_t room = 4u * (uint32_t)imax(0, P.cap - c);
+    buf_st4(make_rsrc_sized(P.buf_sigma + rb, room), so, __float_as_uint(v));
+    buf_st4(make_rsrc_sized(P.buf_j + rb, room), so, (uint32_t)(key0p + lane));
+    cnt[u] = uniform(c + __popcll(m));
+  };
+  // Block-level selection of the tile at key0p: the best scaled score among
+  // the tile's candidates of each row (the tile is one 64-key block). Row
+  // u's 64 scores are spread over 64 / TPW consecutive lanes, TPW scores
+  // each, then reduced across those lanes (DPP within a 16-lane row).
+  auto block_max = [&](int key0p) __attribute__((always_inline)) {
+    constexpr int LPR = 64 / TPW;
+    const int u = lane / LPR, c0 = (lane % LPR) * TPW;
+    const int lim = off + wt0 + u - P.window - key0p;  // last candidate, tile-relative
+    const float* ws = sig[wave] + u * 64 + c0;
+    float v = kNegInf;
+#pragma unroll
+    for (int i = 0; i < TPW; i += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ws + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v = c0 + i + e <= lim ? fmaxf(v, x[e]) : v;
+    }
+    if constexpr (LPR >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+    if constexpr (LPR >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+    if constexpr (LPR >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    if constexpr (LPR >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+    if (lane % LPR == 0 && wt0 + u < P.n_q)
+      P.blk_score[(row0 + (int64_t)u * P.Hkv) * P.blk_stride + (key0p >> 6)] = v * P.scale;
+  };
+  // Selection of a finished tile (its group maxima in sig): the compaction
+  // rows go into chunks 2..7 of the caller's schedule (chunk < 0: all).
+  float sv[TPW];
+  auto select_part = [&](int key0p, bool live, int chunk) __attribute__((always_inline)) {
+    if constexpr (SEL == 1) {
+      // up to 8 rows: their scores are read two chunks ahead of their use
+      if (TPW <= 8 && chunk <= 0) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) sv[u] = sig[wave][u * 64 + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        if (chunk < 0 || chunk == 2 + (u * 6) / TPW)
+          compact_row(u, TPW <= 8 ? sv[u] : sig[wave][u * 64 + lane], key0p,
+                      live ? off + wt0 + u - P.window - key0p : -1);
+    } else if constexpr (SEL == 2) {
+      if ((chunk < 0 || chunk == 2) && live) block_max(key0p);
+    }
+  };
+
+  fetch_k(0, std::integral_constant<int, 0>{});
+  // V stage 1 is read (times a zero P) before its first tile arrives, and
+  // the first tile's selection step reads the group maxima of a tile that
+  // does not exist (with no candidates, but finite scores are assumed)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) st16(&kv_st1[1][(tid + 256 * e) * 16], u32x4{0u, 0u, 0u, 0u});
+  if constexpr (SEL != 0) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) sig[wave][u * 64 + lane] = kNegInf;
+  }
+  lds_wait();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   auto tile = [&](int kt, auto stage_c) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
-    const int key0 = kt * 64;
-    if (stores_pending)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStores < 63 ? kStores : 63));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // every wave's part of tile kt has landed, and every wave is done with
-    // tile kt-1, whose stage the next loads overwrite
+    u32x4* pb_prev = S ? pbA : pbB;
+    u32x4* pb_cur = S ? pbB : pbA;
+    const int key0 = kt * 64, key0p = key0 - 64;
+    const bool sel_prev = SEL != 0 && wave_live && kt > 0 && key0p <= p_whi - P.window;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileWait));
+    // every wave's part of K_kt and V_{kt-1} has landed, and every wave is
+    // done with K_{kt-1} and V_{kt-2}, whose stages the next loads overwrite
     asm volatile("s_barrier" ::: "memory");
-    if (kt + 1 < ntiles) fetch(kt + 1, std::integral_constant<int, 1 - S>{});
-    const bool sel_tile = P.select && wave_live && key0 <= p_whi - P.window;
-    stores_pending = sel_tile && P.select == 1;  // exactly kStores stores follow (block level: wait for all)
-    if (!(wave_live && key0 <= p_whi)) return;
+    if (kt + 1 < ntiles) fetch_k(kt + 1, std::integral_constant<int, 1 - S>{});
+    fetch_v(kt, std::integral_constant<int, S>{});
     const uint8_t* Kb = S ? kv_st1[0] : kv_st0[0];
-    const uint8_t* Vb = S ? kv_st1[1] : kv_st0[1];
-    // the two key blocks' products interleaved: independent accumulators
-    // keep the matrix pipe fed without waiting on the previous result
+    const uint8_t* Vp = S ? kv_st0[1] : kv_st1[1];  // V_{kt-1}
+
+    // ---- A: S^T = K Q^T beside the previous tile's selection
     f32x16 acc[2] = {};
     __builtin_amdgcn_s_setprio(1);
-    // K operands read two steps ahead of their products (a three-slot
-    // ring), so the LDS latency hides behind the matrix pipe
-    u32x4 kf[3][2];
+    {
+      u32x4 kf[3][2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) kf[s2][c] = ld16(Kb + c * 32 * kRowB + kad[s2]);
+        for (int c = 0; c < 2; ++c) kf[s2][c] = ld16(Kb + c * 32 * kRowB + kad[s2]);
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      if (s2 + 2 < 8)
+      for (int s2 = 0; s2 < 8; ++s2) {
+        if (s2 + 2 < 8)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) kf[(s2 + 2) % 3][c] = ld16(Kb + c * 32 * kRowB + kad[s2 + 2]);
+          for (int c = 0; c < 2; ++c) kf[(s2 + 2) % 3][c] = ld16(Kb + c * 32 * kRowB + kad[s2 + 2]);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) acc[c] = mfma32x32x16(as_bf16x8(kf[s2 % 3][c]), qb[s2], acc[c]);
-    }
-    // keep that order: the scheduler would otherwise pull each read down
-    // to its product to save registers
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      if (s2 + 2 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        for (int c = 0; c < 2; ++c) acc[c] = mfma32x32x16(as_bf16x8(kf[s2 % 3][c]), qb[s2], acc[c]);
+        select_part(key0p, sel_prev, s2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     mfma_settle<kSettle32>(acc[0], acc[1]);
     __builtin_amdgcn_s_setprio(0);
+
+    // ---- B: mask, row maximum, rescale; then O += V_{kt-1}^T P_{kt-1}^T
+    // beside the group maximum and P of this tile
     if (key0 + 63 > p_wlo) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -356,20 +526,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       // assembly: two wait states after their vector writes
       asm volatile("s_nop 1" : "+v"(acc[0]), "+v"(acc[1]));
     }
-    // online softmax (exp2 domain); O is rescaled only when some row's
-    // running maximum moved
     float mx = kNegInf;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[c][i]);
-    // Selection, part 1: the group maxima of the tile's candidate keys go
-    // to the wave's LDS rows now, while the raw scores are still in place.
-    if (sel_tile) stage_group_max<G>(acc, sig[wave], mx);
+    const float dep = mx;
     mx = xor32_max(mx);
     // deferred rescaling (see the gather kernel): P <= 2^kRescaleLog2
     const float m_cand = mx * cexp;
     if (ballot(m_cand > m_run + kRescaleLog2)) {
+      pv(Vp, pb_prev, [](int) {});
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) pb_prev[s2] = u32x4{0u, 0u, 0u, 0u};
+      mfma_settle4<kSettle32>(oacc);
       const float m_new = fmaxf(m_run, m_cand);
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == kNegInf ? 0.f : m_new));
       l_run *= alpha;
@@ -380,101 +550,51 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       m_run = m_new;
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(acc[c][i], cexp, -m_use));
-        acc[c][i] = pv;
-        psum += pv;
-      }
-    l_run += psum;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const int c = s2 >> 1, base = 8 * (s2 & 1);
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[c][base + 2 * e], acc[c][base + 2 * e + 1]);
-      pb[s2] = as_bf16x8(w);
-    }
-    // O^T += V^T P^T: the A operand (dims 32bk + l%32, keys kb + 0..3 and
-    // kb + 8 + 0..3 of the permuted k order) from two transpose reads.
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-#pragma unroll
-      for (int bk = 0; bk < 4; ++bk) {  // four independent accumulators in turn
-        const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1);
-        const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + kb * kRowB + vad[bk]));
-        const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + (kb + 8) * kRowB + vad[bk]));
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[bk] = mfma32x32x16(as_bf16x8(w), pb[s2], oacc[bk]);
-      }
-    }
-    // Selection, part 2, once the PV products are issued (it does not
-    // depend on them): every candidate key whose score reaches the row's
-    // threshold is appended, in ascending key order, to the row's buffer.
-    // Exactly kStores range-checked stores per tile: failing lanes and
-    // positions past the buffer's capacity aim beyond the row and are dropped.
-    if (sel_tile && P.select == 2) {
-      // block level: the best scaled score among the tile's candidates of
-      // each row (the tile is one 64-key block). Row u's 64 scores are spread
-      // over 64 / TPW consecutive lanes, TPW scores each, then reduced
-      // across those lanes (DPP within a 16-lane row).
-      constexpr int LPR = 64 / TPW;
-      const int u = lane / LPR, c0 = (lane % LPR) * TPW;
-      const int lim = off + wt0 + u - P.window - key0;  // last candidate, tile-relative
-      const float* ws = sig[wave] + u * 64 + c0;
-      float v = kNegInf;
-#pragma unroll
-      for (int i = 0; i < TPW; i += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(ws + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v = c0 + i + e <= lim ? fmaxf(v, x[e]) : v;
-      }
-      if constexpr (LPR >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
-      if constexpr (LPR >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
-      if constexpr (LPR >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-      if constexpr (LPR >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-      if (lane % LPR == 0 && wt0 + u < P.n_q)
-        P.blk_score[(row0 + (int64_t)u * P.Hkv) * P.blk_stride + (key0 >> 6)] = v * P.scale;
-    } else if (sel_tile) {
-      const float* ws = sig[wave];
-      const int j = key0 + lane;
-      // The candidate test is one compare: past a token's last candidate key
-      // the lane compares against +inf (its score is finite, or -inf where
-      // causally masked), so the ballot is the compare's own lane mask. Tiles
-      // wholly inside every token's candidate range (all but those at the
-      // window's edge) skip the limit.
-      auto compact = [&](auto all_cand_c) __attribute__((always_inline)) {
-        constexpr bool kAllCand = decltype(all_cand_c)::value;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const float v = ws[u * 64 + lane] * P.scale;
-          const float th = kAllCand || j <= off + wt0 + u - P.window ? theta[u] : kPosInf;
-          const bool pass = v >= th;
-          const uint64_t m = ballot(pass);
-          const uint32_t so = pass ? 4u * lane_prefix(m) : kDropOffset;
-          // the row's next free entry and the room left, in the (scalar)
-          // descriptors: entries past the buffer's capacity fail the range check
-          const int c = uniform(cnt[u]);
-          const int64_t rb = (row0 + (int64_t)u * P.Hkv) * P.cap + c;
-          const uint32_t room = 4u * (uint32_t)imax(0, P.cap - c);
-          buf_st4(make_rsrc_sized(P.buf_sigma + rb, room), so, __float_as_uint(v));
-          buf_st4(make_rsrc_sized(P.buf_j + rb, room), so, (uint32_t)j);
-          cnt[u] = uniform(c + __popcll(m));
+    float r[16], r2[8];
+    float ps[2] = {0.f, 0.f};
+    pv(Vp, pb_prev, [&](int m) __attribute__((always_inline)) {
+      if constexpr (SEL != 0) {
+        if constexpr (G == 1) {
+          if (m == 0) gm_store<G>(acc, r, r2, sig[wave]);
+        } else {
+          if (m == 0) gm_fold8<0, 4>(acc, r, dep);
+          if (m == 1) gm_fold8<4, 4>(acc, r, dep);
+          if (m == 2) gm_fold8<8, 4>(acc, r, dep);
+          if (m == 3) gm_fold8<12, 4>(acc, r, dep);
+          if constexpr (G == 2) {
+            if (m == 5) gm_store<G>(acc, r, r2, sig[wave]);
+          } else {
+            if (m == 4) gm_fold4<0, 4>(r, r2, dep);
+            if (m == 5) gm_fold4<4, 4>(r, r2, dep);
+            if constexpr (G == 8) {
+              if (m == 7) gm_fold2(r2);
+              if (m == 9) gm_store<G>(acc, r, r2, sig[wave]);
+            } else {
+              if (m == 7) gm_store<G>(acc, r, r2, sig[wave]);
+            }
+          }
         }
-      };
-      if (uniform(key0 + 63 <= off + wt0 - P.window ? 1 : 0))  // a scalar branch
-        compact(std::true_type{});
-      else
-        compact(std::false_type{});
-    }
+      }
+      // P = exp2(s * scale * log2e - m) for four values per product from
+      // product 6 on (after the group maximum has read the raw scores),
+      // summed in fp32 and packed to bf16 pairs as they complete
+      if (m >= 6 && m < 14) {
+        const int v0 = 4 * (m - 6);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = v0 + e, c = v >> 4, i = v & 15;
+          acc[c][i] = __builtin_amdgcn_exp2f(fmaf(acc[c][i], cexp, -m_use));
+          ps[e & 1] += acc[c][i];
+        }
+        const int c = v0 >> 4, i0 = v0 & 15, s2 = v0 >> 3, w0 = (v0 & 7) >> 1;
+        pb_cur[s2][w0] = pack_bf16x2(acc[c][i0], acc[c][i0 + 1]);
+        pb_cur[s2][w0 + 1] = pack_bf16x2(acc[c][i0 + 2], acc[c][i0 + 3]);
+      }
+    });
+    l_run += ps[0] + ps[1];
   };
 
   // two tiles per trip, so that every LDS address is a constant offset
-  fetch(0, std::integral_constant<int, 0>{});
   int kt = 0;
 #pragma unroll 1
   for (; kt + 1 < ntiles; kt += 2) {
@@ -482,6 +602,22 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     tile(kt + 1, std::integral_constant<int, 1>{});
   }
   if (kt < ntiles) tile(kt, std::integral_constant<int, 0>{});
+
+  // the last tile's O += V^T P^T, row sums and selection
+  auto finish = [&](auto stage_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
+    const u32x4* pb_last = S ? pbB : pbA;
+    const int key0p = (ntiles - 1) * 64;
+    const bool sel_last = SEL != 0 && wave_live && key0p <= p_whi - P.window;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileWait));
+    asm volatile("s_barrier" ::: "memory");
+    pv(S ? kv_st1[1] : kv_st0[1], pb_last, [](int) {});
+    select_part(key0p, sel_last, -1);
+  };
+  if (ntiles & 1)
+    finish(std::integral_constant<int, 0>{});
+  else
+    finish(std::integral_constant<int, 1>{});
 
   mfma_settle4<kSettle32>(oacc);
   const float l_tot = xor32_sum(l_run);
@@ -499,7 +635,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       }
     if (P.lse && h == 0) P.lse[((int64_t)b * P.Hq + head) * P.n_q + tok] = m_run * kLn2 + __logf(l_tot);
   }
-  if (P.select == 1 && lane == 0) {
+  if (SEL == 1 && lane == 0) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
       if (wt0 + u < P.n_q) P.counts[row0 + (int64_t)u * P.Hkv] = cnt[u];
@@ -701,7 +837,12 @@ template <int G>
 hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t s) {
   constexpr int TPB = 4 * (32 / G);
   const int64_t blocks = (int64_t)((p.n_q + TPB - 1) / TPB) * p.B * p.Hkv;
-  prefill_attn_kernel<G><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  switch (p.select) {
+    case 0: prefill_attn_kernel<G, 0><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p); break;
+    case 1: prefill_attn_kernel<G, 1><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p); break;
+    case 2: prefill_attn_kernel<G, 2><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
