@@ -368,6 +368,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 #pragma unroll
   for (int s2 = 0; s2 < 4; ++s2) pbA[s2] = pbB[s2] = u32x4{0u, 0u, 0u, 0u};
 
+  // Schedule variant, chosen by measurement. With selection, P of a tile is
+  // pinned beside the products of its own tile (otherwise the compiler
+  // sinks half of it into the next tile, out of the products' shadow) and
+  // waves keep one priority: raising the priority of waves in step A made
+  // the two blocks sharing a CU drift apart, and at a 1M-token context the
+  // blocks streaming one group's cache then lost L2 locality (97% -> 28%
+  // hits, the clock fell with the extra HBM traffic). Without selection the
+  // unpinned schedule with step A at raised priority measured faster.
+  constexpr bool kPinP = SEL != 0;
+
   // Stores per tile of the compaction; the wait for a tile's loads lets them
   // remain outstanding (vector memory operations complete in order).
   constexpr int kStores = SEL == 1 ? 2 * TPW : 0;
@@ -491,7 +501,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 
     // ---- A: S^T = K Q^T beside the previous tile's selection
     f32x16 acc[2] = {};
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!kPinP) __builtin_amdgcn_s_setprio(1);
     {
       u32x4 kf[3][2];
 #pragma unroll
@@ -510,7 +520,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       }
     }
     mfma_settle<kSettle32>(acc[0], acc[1]);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!kPinP) __builtin_amdgcn_s_setprio(0);
 
     // ---- B: mask, row maximum, rescale; then O += V_{kt-1}^T P_{kt-1}^T
     // beside the group maximum and P of this tile
@@ -589,6 +599,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
         const int c = v0 >> 4, i0 = v0 & 15, s2 = v0 >> 3, w0 = (v0 & 7) >> 1;
         pb_cur[s2][w0] = pack_bf16x2(acc[c][i0], acc[c][i0 + 1]);
         pb_cur[s2][w0 + 1] = pack_bf16x2(acc[c][i0 + 2], acc[c][i0 + 3]);
+        // computed here, beside product m (with selection; see kPinP)
+        if constexpr (kPinP)
+          asm volatile("" : "+v"(pb_cur[s2][w0]), "+v"(pb_cur[s2][w0 + 1]), "+v"(ps[0]), "+v"(ps[1]));
       }
     });
     l_run += ps[0] + ps[1];
