@@ -145,6 +145,36 @@ def test_decode_filter_ragged_tail_keeps_last_keys(tail):
     assert set(planted) <= set(int(j) for j in got), "a planted last candidate was not selected"
 
 
+def test_decode_slicewise_copy_dense_slices():
+    """Rows with more than 16 survivors per thread gather the slices'
+    survivors slice by slice (two per lane per pass, a loop beyond 128).
+    Clusters of keys aimed at the queries put 300 and 100 survivors into two
+    slices; every planted key must be selected and the rest match the oracle."""
+    W, k, Hq, Hkv = 64, 4096, 4, 1
+    ncand = 300000
+    L = ncand + W - 1
+    print(f"[case] decode slice-wise copy ncand={ncand} k={k}", flush=True)
+    kv = torch.zeros((1, Hkv, L + 1, 2, 128), dtype=torch.bfloat16, device=DEV)
+    kv[0, :, :L] = synth.randn_bf16((Hkv, L, 2, 128), 171, DEV)
+    q = synth.randn_bf16((1, Hq, 128), 172, DEV)
+    u = q[0].float().sum(0)
+    u = u / u.norm() * (128 ** 0.5)
+    planted = list(range(100000, 100300)) + list(range(200000, 200100))
+    kv[0, 0, planted, 0] = (2.0 * u).to(torch.bfloat16)
+    kv_new = synth.randn_bf16((1, Hkv, 2, 128), 173, DEV)
+    seq_lens = torch.tensor([L + 1], dtype=torch.int32, device=DEV)
+    o, lse, idx = hs.decode_step(q, kv_new, kv, seq_lens, L + 1, top_k=k, window=W)
+    torch.cuda.synchronize()
+    Ks, Vs = kv[0, :, :, 0].float().cpu().numpy(), kv[0, :, :, 1].float().cpu().numpy()
+    ref = orc.decode_step(f32(q[0]), [], f32(kv_new[0]), Ks, Vs, L + 1, k, W, orc.default_scale(128))
+    got = idx.cpu().numpy()[0, 0]
+    check_idx_row(got, ref["idx"][0], ref["sigma"][0], ref["tau"][0], L, W, k, where="slice-wise copy")
+    assert set(planted) <= set(int(j) for j in got), "a planted key was not selected"
+    stats = OutStats()
+    stats.add(f32(o[0]), ref["o_full"])
+    stats.check("decode full o")
+
+
 def test_decode_streaming_select():
     """k close to the row length defeats the sample filter: streaming select."""
     run_decode([9000], 1, 4, 1, 8000, 16, seed=14, n_sparse=1)

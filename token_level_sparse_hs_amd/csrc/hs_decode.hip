@@ -740,9 +740,18 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams P) 
   for (int w = 0; w < kCombThreads / 64; ++w) l += red[1][w];
   const int grp = tid >> 7, d = tid & 127;
   const int s0 = (ns * grp) / kCombGroups, s1 = (ns * (grp + 1)) / kCombGroups;
+  // 32 loads in flight per thread: with a few hundred splits per head the
+  // sum is a chain of memory round trips, not of arithmetic
   float acc = 0.f;
   const float* pd = base + d;
   int s = s0;
+  for (; s + 32 <= s1; s += 32) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = pd[(s + u) * sstride];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) acc += wsh[s + u] * v[u];
+  }
   for (; s + 8 <= s1; s += 8) {
     float v[8];
 #pragma unroll

@@ -1115,53 +1115,100 @@ __global__ __launch_bounds__(kSelThreads) void select_decode_final_kernel(Select
     topk_stream(sh, dense, r.ncand, k, out);
     return;
   }
-  // Survivors into LDS: thread t copies the contiguous run [t*run, t*run +
-  // run) of the concatenation (the run the register selection below reads
-  // back). One binary search over the slice offsets finds the run's first
-  // slice; a walk then crosses slice boundaries in order, and every read of
-  // a group is issued before the first is used. (A binary search per element
-  // chained about nine dependent LDS reads per survivor: most of this
-  // kernel's time at the 1M context.)
+  // Survivors into LDS, in concatenation order. With more than 16 per
+  // thread (the 1M context): one slice per wave at a time, lanes e and
+  // e + 64 copying the slice's survivors e and e + 64, so each read is one
+  // coalesced run, and a wave has 16 slices' reads in flight before it
+  // writes any (per-thread runs made every read touch a cache line per
+  // lane there). Reads go to clamped in-segment positions; only lanes
+  // inside a slice's count write.
   const int run = uniform((int)((total + kSelThreads - 1) / kSelThreads));
-  const int beg = (int)threadIdx.x * run;
-  int sl = 0;  // the last slice whose offset is <= the run's first position
-  {
-    const uint32_t b0 = (uint32_t)imin(beg, (int)total - 1);
-    int hi = ns;
-    while (hi - sl > 1) {
-      const int mid = (sl + hi) >> 1;
-      if (lds.off[mid] <= b0) sl = mid;
-      else hi = mid;
-    }
-  }
-  uint32_t sbase = lds.off[sl], next = lds.off[sl + 1];  // the slice's first position, the next slice's
-  const int64_t seg0 = (int64_t)row * P.nslices * kDecSlice;
-  constexpr int kCopyGroup = 16;
-  for (int e0 = 0; e0 < run; e0 += kCopyGroup) {
-    uint32_t src[kCopyGroup];
+  if (run > 16) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int kSl = 16;
+    const int64_t seg0 = (int64_t)row * P.nslices * kDecSlice;
+    for (int sb = wave * kSl; sb < ns; sb += (kSelThreads / 64) * kSl) {
+      uint32_t kk[2][kSl], o[kSl], c[kSl];
+      int32_t jj[2][kSl];
 #pragma unroll
-    for (int u = 0; u < kCopyGroup; ++u) {
-      const uint32_t i = (uint32_t)imin(beg + e0 + u, (int)total - 1);  // past the run: re-read the last
-      while (i >= next) {  // into the following slice (empty slices skipped; off[ns] = total ends it)
-        ++sl;
-        sbase = next;
-        next = lds.off[sl + 1];
+      for (int u = 0; u < kSl; ++u) {
+        const int sl = imin(sb + u, ns - 1);
+        o[u] = lds.off[sl];
+        c[u] = sb + u < ns ? lds.off[sl + 1] - o[u] : 0u;
+        const int last = imax((int)c[u] - 1, 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t p = seg0 + (int64_t)sl * kDecSlice + imin(lane + 64 * h, last);
+          kk[h][u] = P.seg_key[p];
+          jj[h][u] = P.seg_idx[p];
+        }
       }
-      src[u] = (uint32_t)sl * kDecSlice + (i - sbase);
-    }
-    uint32_t kk[kCopyGroup];
-    int32_t jj[kCopyGroup];
 #pragma unroll
-    for (int u = 0; u < kCopyGroup; ++u) {
-      kk[u] = P.seg_key[seg0 + src[u]];
-      jj[u] = P.seg_idx[seg0 + src[u]];
-    }
+      for (int u = 0; u < kSl; ++u)
 #pragma unroll
-    for (int u = 0; u < kCopyGroup; ++u) {
-      const int i = beg + e0 + u;
-      if (e0 + u < run && i < (int)total) {
-        lds.key[i] = score_key(__uint_as_float(kk[u]));
-        lds.idx[i] = jj[u];
+        for (int h = 0; h < 2; ++h)
+          if ((uint32_t)(lane + 64 * h) < c[u]) {
+            lds.key[o[u] + lane + 64 * h] = score_key(__uint_as_float(kk[h][u]));
+            lds.idx[o[u] + lane + 64 * h] = jj[h][u];
+          }
+      // slices holding more than 128 survivors
+#pragma unroll 1
+      for (int u = 0; u < kSl; ++u) {
+        const int sl = sb + u;
+        for (uint32_t e = 128u + lane; sl < ns && e < c[u]; e += 64u) {
+          const int64_t p = seg0 + (int64_t)sl * kDecSlice + e;
+          lds.key[o[u] + e] = score_key(__uint_as_float(P.seg_key[p]));
+          lds.idx[o[u] + e] = P.seg_idx[p];
+        }
+      }
+    }
+  } else {
+    // Shorter runs (64 sequences): thread t copies the contiguous run
+    // [t*run, t*run + run) of the concatenation (measured faster there). One
+    // binary search over the slice offsets finds the run's first slice; a
+    // walk then crosses slice boundaries in order, and every read of a group
+    // is issued before the first is used (a binary search per element
+    // chained about nine dependent LDS reads per survivor).
+    const int beg = (int)threadIdx.x * run;
+    int sl = 0;  // the last slice whose offset is <= the run's first position
+    {
+      const uint32_t b0 = (uint32_t)imin(beg, (int)total - 1);
+      int hi = ns;
+      while (hi - sl > 1) {
+        const int mid = (sl + hi) >> 1;
+        if (lds.off[mid] <= b0) sl = mid;
+        else hi = mid;
+      }
+    }
+    uint32_t sbase = lds.off[sl], next = lds.off[sl + 1];  // the slice's first position, the next slice's
+    const int64_t seg0 = (int64_t)row * P.nslices * kDecSlice;
+    constexpr int kCopyGroup = 16;
+    for (int e0 = 0; e0 < run; e0 += kCopyGroup) {
+      uint32_t src[kCopyGroup];
+#pragma unroll
+      for (int u = 0; u < kCopyGroup; ++u) {
+        const uint32_t i = (uint32_t)imin(beg + e0 + u, (int)total - 1);  // past the run: re-read the last
+        while (i >= next) {  // into the following slice (empty slices skipped; off[ns] = total ends it)
+          ++sl;
+          sbase = next;
+          next = lds.off[sl + 1];
+        }
+        src[u] = (uint32_t)sl * kDecSlice + (i - sbase);
+      }
+      uint32_t kk[kCopyGroup];
+      int32_t jj[kCopyGroup];
+#pragma unroll
+      for (int u = 0; u < kCopyGroup; ++u) {
+        kk[u] = P.seg_key[seg0 + src[u]];
+        jj[u] = P.seg_idx[seg0 + src[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyGroup; ++u) {
+        const int i = beg + e0 + u;
+        if (e0 + u < run && i < (int)total) {
+          lds.key[i] = score_key(__uint_as_float(kk[u]));
+          lds.idx[i] = jj[u];
+        }
       }
     }
   }
