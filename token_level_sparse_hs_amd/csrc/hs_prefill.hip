@@ -384,11 +384,11 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   constexpr int kTileWait = kStores < 63 ? kStores : 63;
 
   // O^T += V^T P^T for one tile: MFMA m = 4 s2 + bk, A operand from two
-  // transpose reads (issued two products ahead), B = pb[s2]. FILL(m) places
+  // transpose reads (issued four products ahead), B = pb[s2]. FILL(m) places
   // vector work of the caller after product m; each product and its work
   // form one scheduling chunk.
   auto pv = [&](const uint8_t* Vb, const u32x4* pb, auto&& fill) __attribute__((always_inline)) {
-    u32x2 vf[3][2];
+    u32x2 vf[5][2];
     auto vread = [&](int m, u32x2* dst) __attribute__((always_inline)) {
       const int s2 = m >> 2, bk = m & 3;
       const int kb = 32 * (s2 >> 1) + 16 * (s2 & 1);
@@ -397,11 +397,13 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     };
     vread(0, vf[0]);
     vread(1, vf[1]);
+    vread(2, vf[2]);
+    vread(3, vf[3]);
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-      if (m + 2 < 16) vread(m + 2, vf[(m + 2) % 3]);
+      if (m + 4 < 16) vread(m + 4, vf[(m + 4) % 5]);
       const int s2 = m >> 2, bk = m & 3;
-      const u32x4 w = {vf[m % 3][0][0], vf[m % 3][0][1], vf[m % 3][1][0], vf[m % 3][1][1]};
+      const u32x4 w = {vf[m % 5][0][0], vf[m % 5][0][1], vf[m % 5][1][0], vf[m % 5][1][1]};
       oacc[bk] = mfma32x32x16(as_bf16x8(w), as_bf16x8(pb[s2]), oacc[bk]);
       fill(m);
       __builtin_amdgcn_sched_barrier(0);
