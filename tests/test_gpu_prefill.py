@@ -133,3 +133,17 @@ def test_threshold_wave32_all_rows():
     register slots per lane (n = 1800, k = 64, stride 1: 1792 samples);
     every row is checked."""
     run(1, 1800, 1800, 8, 2, 64, 32, seed=1000)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (8, 2)])
+@pytest.mark.parametrize("n", [1, 5, 63, 64, 65, 129])
+def test_short_contexts(n, Hq, Hkv):
+    """One to three 64-key tiles: the first and the last tile of the full
+    layer's pipeline (V of a tile consumed one tile after its K) meet, with
+    and without tiles between them; k and W small so that rows select."""
+    run(1, n, n, Hq, Hkv, 4, 2, seed=1100 + n + Hkv)
+
+
+def test_short_chunk_over_two_tiles():
+    """Three query rows at the end of a 70-token cache (two tiles, G = 4)."""
+    run(1, 3, 70, 8, 2, 8, 4, seed=1200)
