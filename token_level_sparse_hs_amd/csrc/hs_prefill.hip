@@ -9,9 +9,10 @@
 // sharing" and "Prefill exits early").
 //
 // Design (MI355X):
-//  * One 256-thread block = 4 waves = one KV group g and 4*(32/G) query
-//    tokens. Each wave owns 32 MFMA rows = 32/G tokens x the G query heads of
-//    group g, so the group's heads share every K/V tile staged in LDS and the
+//  * One block = 8 waves (two per SIMD, one block per CU; 4 waves for G = 1)
+//    = one KV group g and 8*(32/G) query tokens. Each wave owns 32 MFMA rows
+//    = 32/G tokens x the G query heads of group g, so the group's heads and
+//    all eight waves share every K/V tile staged in LDS, and the
 //    group maximum over heads (the selection score) is a reduction across
 //    lanes: a token's heads sit 16/G lanes apart inside one 16-lane row, and
 //    masked DPP steps halve the values each lane carries.
@@ -244,6 +245,12 @@ __device__ __forceinline__ void gm_store(const f32x16* acc, const float* r, cons
   }
 }
 
+// Waves per block of the full layer: eight (two per SIMD, one block per CU)
+// share every K/V tile; one query head per group (G = 1) needs more
+// registers than two waves per SIMD allow and keeps four.
+template <int G>
+constexpr int attn_waves() { return G == 1 ? 4 : 8; }
+
 // SEL: 0 no selection, 1 token-level candidates, 2 block-level maxima.
 //
 // Software pipeline over 64-key tiles (one wave's view of tile i):
@@ -259,9 +266,12 @@ __device__ __forceinline__ void gm_store(const f32x16* acc, const float* r, cons
 // everything. Rows whose maximum rises past the deferred-rescale slack finish
 // O += V_{i-1}^T P_{i-1}^T first, rescale, and let B add a zero P.
 template <int G, int SEL>
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
+__global__ __launch_bounds__(64 * attn_waves<G>(), G == 1 ? 2 : 1) void prefill_attn_kernel(PrefillParams P) {
+  constexpr int NW = attn_waves<G>();
   constexpr int TPW = 32 / G;
-  constexpr int TPB = 4 * TPW;
+  constexpr int TPB = NW * TPW;
+  constexpr int RPW = 64 / NW;  // tile rows each wave fetches
+  constexpr int NLD = RPW / 4;  // 16-byte loads per lane and tile, for K and for V
   // K and V tiles of 64 keys, two stages each, unpadded 256-byte rows written
   // by direct global->LDS loads. 16-byte chunks are XOR-permuted within a row
   // so that both operand read patterns hit distinct banks: chunk c of K row r
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   // c ^ 4(r % 4) (the transpose reads take 4 rows x 64 bytes at a time).
   __shared__ __attribute__((aligned(1024))) uint8_t kv_st0[2][kTileB];
   __shared__ __attribute__((aligned(1024))) uint8_t kv_st1[2][kTileB];
-  __shared__ __attribute__((aligned(16))) float sig[4][TPW * 64];
+  __shared__ __attribute__((aligned(16))) float sig[NW][TPW * 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   const int p_bhi = off + imin(t0 + TPB, P.n_q) - 1;
   const int ntiles = p_bhi / 64 + 1;
 
-  // Tile loads: wave w fetches tile rows 16w + 4i + lane/16 (i = 0..3) of K
+  // Tile loads: wave w fetches tile rows RPW w + 4i + lane/16 (i < NLD) of K
   // and of V, 16 bytes per lane, straight into LDS (lane l lands at byte 16l
   // of a 1 KB run of 4 rows, i.e. chunk position l % 16); each lane reads the
   // global chunk that belongs at its position. Rows past the cache's valid
@@ -327,10 +337,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   const uint32_t span = (uint32_t)(P.n_kv - 1) * rowb + 2u * kHeadDim;  // bytes up to the last valid row's end
   const u32x4 krs = rsrc_words(slab, span);
   const u32x4 vrs = rsrc_words(slab + P.kv.voff, span);
-  uint32_t dk[4], dv[4];
+  uint32_t dk[NLD], dv[NLD];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t r = 16u * wave + 4u * i + (lane >> 4);
+  for (int i = 0; i < NLD; ++i) {
+    const uint32_t r = (uint32_t)RPW * wave + 4u * i + (lane >> 4);
     dk[i] = r * rowb + 16u * ((lane & 15) ^ (r & 15));
     dv[i] = r * rowb + 16u * ((lane & 15) ^ (4u * (r & 3)));
   }
@@ -340,16 +350,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   auto fetch_k = [&](int kt, auto stage_c) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
     const uint32_t soff = (uint32_t)uniform(kt * 64) * rowb;
-    const uint32_t base = lds_addr(S ? kv_st1[0] : kv_st0[0]) + (uint32_t)(16 * wave) * kRowB;
+    const uint32_t base = lds_addr(S ? kv_st1[0] : kv_st0[0]) + (uint32_t)(RPW * wave) * kRowB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(base + 4u * i * kRowB, dk[i], krs, soff);
+    for (int i = 0; i < NLD; ++i) lds_dma16(base + 4u * i * kRowB, dk[i], krs, soff);
   };
   auto fetch_v = [&](int kt, auto stage_c) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
     const uint32_t soff = (uint32_t)uniform(kt * 64) * rowb;
-    const uint32_t base = lds_addr(S ? kv_st1[1] : kv_st0[1]) + (uint32_t)(16 * wave) * kRowB;
+    const uint32_t base = lds_addr(S ? kv_st1[1] : kv_st0[1]) + (uint32_t)(RPW * wave) * kRowB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(base + 4u * i * kRowB, dv[i], vrs, soff);
+    for (int i = 0; i < NLD; ++i) lds_dma16(base + 4u * i * kRowB, dv[i], vrs, soff);
   };
   // Operand read offsets within a tile. K (S^T = K Q^T, A operand): lane
   // (n, h) reads dims 16s + 8h .. +8 of key n (+32 for the second MFMA block).
@@ -372,10 +382,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   // pinned beside the products of its own tile (otherwise the compiler
   // sinks half of it into the next tile, out of the products' shadow) and
   // waves keep one priority: raising the priority of waves in step A made
-  // the two blocks sharing a CU drift apart, and at a 1M-token context the
-  // blocks streaming one group's cache then lost L2 locality (97% -> 28%
-  // hits, the clock fell with the extra HBM traffic). Without selection the
-  // unpinned schedule with step A at raised priority measured faster.
+  // blocks drift apart, and at a 1M-token context the blocks streaming one
+  // group's cache then lost L2 locality (97% -> 28% hits, the clock fell
+  // with the extra HBM traffic). Without selection the unpinned schedule
+  // with step A at raised priority measured faster.
   constexpr bool kPinP = SEL != 0;
 
   // Stores per tile of the compaction; the wait for a tile's loads lets them
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   // the first tile's selection step reads the group maxima of a tile that
   // does not exist (with no candidates, but finite scores are assumed)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) st16(&kv_st1[1][(tid + 256 * e) * 16], u32x4{0u, 0u, 0u, 0u});
+  for (int e = 0; e < NLD; ++e) st16(&kv_st1[1][(tid + 64 * NW * e) * 16], u32x4{0u, 0u, 0u, 0u});
   if constexpr (SEL != 0) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) sig[wave][u * 64 + lane] = kNegInf;
@@ -850,12 +860,13 @@ __global__ __launch_bounds__(256, 2) void score_pass_kernel(PrefillParams P) {
 
 template <int G>
 hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t s) {
-  constexpr int TPB = 4 * (32 / G);
+  constexpr int TPB = attn_waves<G>() * (32 / G);
   const int64_t blocks = (int64_t)((p.n_q + TPB - 1) / TPB) * p.B * p.Hkv;
+  const dim3 grid((unsigned)blocks), block(64 * attn_waves<G>());
   switch (p.select) {
-    case 0: prefill_attn_kernel<G, 0><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p); break;
-    case 1: prefill_attn_kernel<G, 1><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p); break;
-    case 2: prefill_attn_kernel<G, 2><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p); break;
+    case 0: prefill_attn_kernel<G, 0><<<grid, block, 0, s>>>(p); break;
+    case 1: prefill_attn_kernel<G, 1><<<grid, block, 0, s>>>(p); break;
+    case 2: prefill_attn_kernel<G, 2><<<grid, block, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
